@@ -1,0 +1,168 @@
+/*
+ * fq.h -- C ABI of the FibQuant random-access KV-cache codec for MI355X (gfx950).
+ *
+ * Sources cited below:
+ *   [FQ]     "FibQuant: Universal Vector Quantization for Random-Access KV-Cache
+ *            Compression", technical summary (gist.science), by section:
+ *            1 problem statement, 2.1 canonical source, 2.2 codebook
+ *            construction, 2.3 encoding and decoding, 5 significance.
+ *   [FQ-abs] the authors' abstract of the same paper.
+ *
+ * Conventions for every call:
+ *   - Pure C: plain pointers and sizes.  Every data pointer is HIP device
+ *     memory owned by the caller, except the artifact bytes given to
+ *     fq_codebook_load / fq_artifact_check, which are host memory.
+ *   - Every call returns an fq_status; no exception crosses the boundary.
+ *     Arguments are checked on the host before any device work is queued;
+ *     an argument error leaves every output untouched.
+ *   - Work is queued asynchronously on `stream` (a hipStream_t passed as
+ *     void*; NULL is the null stream).  A fault inside a kernel surfaces at
+ *     the caller's next synchronisation, not as a return code.
+ *   - Only fq_codebook_load allocates device memory.  fq_encode, fq_decode
+ *     and fq_attend_decode allocate nothing; attention scratch comes from a
+ *     caller-provided workspace.
+ *   - A codebook handle is immutable after load and may be used from several
+ *     host threads and streams at once.
+ *   - Vectors have d = 64 coordinates.
+ */
+#ifndef FQ_H
+#define FQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct fq_codebook fq_codebook; /* opaque */
+
+typedef enum { FQ_F16 = 1, FQ_F32 = 2 } fq_dtype;
+
+typedef enum {
+  FQ_OK = 0,
+  FQ_ERR_INVALID_ARG = 1, /* null / misaligned pointer, bad size or stride */
+  FQ_ERR_BAD_ARTIFACT = 2, /* malformed, truncated or corrupt artifact */
+  FQ_ERR_UNSUPPORTED = 3, /* well-formed but outside what the kernels handle */
+  FQ_ERR_NO_MEMORY = 4,   /* device allocation failed (load only) */
+  FQ_ERR_DEVICE = 5       /* HIP runtime error, or no usable device */
+} fq_status;
+
+typedef struct {
+  int32_t d;            /* vector length (64) */
+  int32_t k;            /* block size */
+  int32_t N;            /* codebook size, a power of two */
+  int32_t nb;           /* blocks per vector, ceil(d / k) */
+  int32_t idx_bits;     /* bits per index, log2 N */
+  int32_t record_words; /* uint32 words per record, ceil(nb * idx_bits / 32) */
+  int32_t last_block;   /* real coordinates in the last block */
+  int32_t reserved;
+  double rate_nominal;  /* log2(N) / k bits per coordinate [FQ 2.3] */
+  double rate_actual;   /* nb * idx_bits / d */
+  double distortion;    /* test distortion per unit vector recorded in the artifact */
+  uint64_t artifact_hash; /* FNV-1a 64 of the artifact body */
+} fq_info;
+
+/* Human-readable name of a status code (static storage). */
+const char* fq_status_string(fq_status s);
+
+/*
+ * Parse and validate an artifact on the host only (no device is touched).
+ *
+ * The artifact holds the shared rotation Pi (float64, d x d, row-major,
+ * z = Pi u) and the shared codebook C (float32, N x k): one offline codebook
+ * for every layer and head [FQ 2.1] and one shared Haar rotation [FQ 1, 2.3].
+ * Checks: magic, version, header size, d = 64, 1 <= k <= 64, N a power of two
+ * with 2 <= N <= 4096, nb / idx_bits / record_words / last_block consistent,
+ * total size, FNV-1a hash, finite values, max |Pi^T Pi - I| <= 1e-9.
+ * Returns FQ_ERR_BAD_ARTIFACT for a malformed or corrupt blob,
+ * FQ_ERR_UNSUPPORTED for a valid blob the kernels cannot run
+ * (k not in {2, 3, 4, 8}).  `out` may be NULL.
+ */
+fq_status fq_artifact_check(const void* artifact, size_t nbytes, fq_info* out);
+
+/*
+ * Validate an artifact (as fq_artifact_check) and upload its tables to
+ * `device`.  The blob is copied; the caller may free it on return.  On
+ * success *out receives a handle to release with fq_codebook_free.
+ */
+fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_codebook** out);
+
+/* Describe a loaded codebook. */
+fq_status fq_codebook_info(const fq_codebook* cb, fq_info* out);
+
+/* Release a codebook.  The caller guarantees no queued work still uses it.  NULL is a no-op. */
+void fq_codebook_free(fq_codebook* cb);
+
+/*
+ * Encode n vectors [FQ 2.3]: nu = |x|_2; z = Pi (x / nu); for each of the nb
+ * blocks of z, the index of the nearest codeword (squared Euclidean distance
+ * over the block's real coordinates, ties to the lowest index); pack the
+ * indices at fixed rate and store the norm [FQ 1].
+ *
+ *   x      [n rows, stride x_ld elements] of x_dtype (FQ_F16 or FQ_F32), row r at
+ *          x + r * x_ld; x_ld >= 64; rows 16-byte aligned when x_ld is a
+ *          multiple of 8 (F16) / 4 (F32), else 4-byte aligned.
+ *   codes  [n, record_words] uint32 out, 4-byte aligned: field j (idx_bits bits)
+ *          at bits [j*idx_bits, (j+1)*idx_bits) of the record, counted from the
+ *          least significant bit of little-endian words; unused bits are 0.
+ *   norms  [n] binary16 out (bit patterns), nu rounded to nearest-even.
+ *   A zero vector gets all-zero indices and norm 0.  n == 0 is a no-op.
+ *   Indices agree with a float64 evaluation of the same distances except
+ *   where two distances lie within a relative 1e-6 of each other.
+ */
+fq_status fq_encode(const fq_codebook* cb, const void* x, fq_dtype x_dtype, int64_t n,
+                    int64_t x_ld, uint32_t* codes, uint16_t* norms, void* stream);
+
+/*
+ * Decode [FQ 2.3]: fetch the codewords of a record, concatenate them (the last
+ * block truncated to its real coordinates), apply Pi^T and scale by the stored
+ * norm.  Random access [FQ 1]: when `rows` is non-NULL, output row i decodes
+ * record rows[i] (0 <= rows[i] < n_records, checked on the device: an
+ * out-of-range address decodes to a zero row); when NULL, row i decodes
+ * record i and n_records is ignored.
+ *
+ *   codes [n_records, record_words] uint32, norms [n_records] binary16 (layout of fq_encode)
+ *   rows  [n] int64 or NULL, 8-byte aligned
+ *   y     [n rows, stride y_ld elements] of y_dtype out (F16 rounded to
+ *         nearest-even, or F32); y_ld >= 64
+ */
+fq_status fq_decode(const fq_codebook* cb, const uint32_t* codes, const uint16_t* norms,
+                    const int64_t* rows, int64_t n_records, int64_t n, void* y,
+                    fq_dtype y_dtype, int64_t y_ld, void* stream);
+
+/*
+ * Bytes of device workspace fq_attend_decode needs for this shape.
+ */
+fq_status fq_attend_workspace_size(const fq_codebook* cb_k, int B, int Hq, int Hkv, int64_t T,
+                                   size_t* bytes);
+
+/*
+ * Fused decode-step attention over a compressed cache, the kernel fusion the
+ * fixed-address records allow [FQ 5]; the cache is read at every decoding
+ * step [FQ-abs].  For batch b and query head h (KV head g = h / (Hq / Hkv)):
+ *   s_t = scale * <q[b,h], k_hat[b,g,t]>,  p = softmax_t(s),  out[b,h] = sum_t p_t v_hat[b,g,t]
+ * where k_hat / v_hat are the fq_decode reconstructions.  Computed without
+ * materialising them: scores nu_t <Pi q, z_hat_t> and values accumulated as
+ * sum p_t nu_t z_hat_t in the rotated domain, rotated back once.
+ *
+ *   q        [B, Hq, 64] binary16
+ *   k_codes  [B, Hkv, T, Wk] uint32,  k_norms [B, Hkv, T] binary16  (cb_k layout)
+ *   v_codes  [B, Hkv, T, Wv] uint32,  v_norms [B, Hkv, T] binary16  (cb_v layout)
+ *   out      [B, Hq, 64] binary16
+ *   Hq % Hkv == 0, Hq / Hkv <= 16, T >= 1; workspace of at least
+ *   fq_attend_workspace_size bytes, 256-byte aligned, contents need not be
+ *   initialised.  cb_k and cb_v may be the same handle; both must be on the
+ *   same device.
+ */
+fq_status fq_attend_decode(const fq_codebook* cb_k, const fq_codebook* cb_v, const uint16_t* q,
+                           const uint32_t* k_codes, const uint16_t* k_norms,
+                           const uint32_t* v_codes, const uint16_t* v_norms, int B, int Hq,
+                           int Hkv, int64_t T, float scale, void* workspace,
+                           size_t workspace_bytes, uint16_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FQ_H */

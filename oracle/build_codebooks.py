@@ -1,0 +1,62 @@
+"""Offline build of the shared codebook artifacts (calls only ``oracle``).
+
+Writes one ``.fqcb`` file per (k, N) variant into
+``kv_cache_compression_fq_amd/codebooks/``.  Every artifact carries the same
+rotation Pi (seed 0): one shared rotation for keys, values, layers and heads
+([FQ 1, 2.3]) and one codebook per rate ([FQ 2.1]).
+
+Usage:  python -m oracle.build_codebooks [k:N ...] [--samples S] [--restarts R]
+"""
+import argparse
+import os
+import sys
+import time
+
+from . import artifact, codebook, rotation
+
+VARIANTS = [(2, 16), (2, 64), (2, 256), (3, 512), (4, 256), (8, 256), (8, 16), (4, 4),
+            (3, 4096)]
+D = 64
+OUT_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                       "kv_cache_compression_fq_amd", "codebooks")
+
+
+def artifact_name(k, N):
+    return f"fq_d{D}_k{k}_N{N}.fqcb"
+
+
+def build_one(k, N, samples, restarts, out_dir, log):
+    Pi = rotation.make_rotation(D, rotation.SEED_ROT)
+    t0 = time.time()
+    book = codebook.build_codebook(D, k, N, restarts=restarts, samples=samples,
+                                   test_samples=samples, log=log)
+    book["seed_rot"] = rotation.SEED_ROT
+    book["law_a"], book["law_b"] = codebook.radius_law(D, k)
+    blob = artifact.write_artifact(Pi, book)
+    path = os.path.join(out_dir, artifact_name(k, N))
+    with open(path, "wb") as f:
+        f.write(blob)
+    log(f"wrote {path}: D_test={book['D_test']:.6f} restart={book['best_restart']} "
+        f"iters={book['iterations']} ({time.time() - t0:.0f} s)")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("variants", nargs="*", help="k:N pairs (default: all)")
+    ap.add_argument("--samples", type=int, default=1 << 20)
+    ap.add_argument("--restarts", type=int, default=8)
+    ap.add_argument("--out", default=OUT_DIR)
+    a = ap.parse_args(argv)
+    todo = VARIANTS if not a.variants else [tuple(map(int, v.split(":"))) for v in a.variants]
+    os.makedirs(a.out, exist_ok=True)
+
+    def log(msg):
+        print(msg, flush=True)
+
+    for k, N in todo:
+        build_one(k, N, a.samples, a.restarts, a.out, log)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
