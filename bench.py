@@ -1,0 +1,297 @@
+#!/usr/bin/env python3
+"""Throughput of the FibQuant hot path on one MI355X.
+
+One step is one pass of the whole path over the GPT-2-small-shaped KV cache
+(12 layers x {K, V} x batch 4 x 12 heads x 1024 tokens, d = 64, binary16,
+seeded synthetic values with per-channel log-uniform scales and 1% x20
+outlier channels):
+
+  for each rate variant k2N16, k2N64, k2N256, k3N512:
+      encode every vector (norm, rotation, block search, packing)
+      decode every record (gather, inverse rotation, rescale) to binary16
+  random-access decode of 2^20 uniformly drawn records (k2N16 codes)
+  decode-step attention over the compressed cache, all 12 layers (k2N16)
+
+``value`` is vectors encoded and decoded per second over the whole step.  The
+same run also times fused attention at the TinyLlama-shaped decode step
+(batch 16, 32 query / 4 KV heads, 32768 tokens, 22 layers, k4N256) and
+reports its HBM bandwidth, and times the CPU oracle on a bounded sample.
+
+Each (variant, op) works on its own buffers (four input replicas of 151 MB)
+so that reads are served from HBM rather than the 256 MB Infinity Cache.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KV vectors/s encode+decode (d=64) and attend HBM GB/s, % of MI355X peak"
+HBM_PEAK_GBS = 8000.0
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12     # non-packed lane-ops/s: 39.3 T
+VARIANTS = [(2, 16), (2, 64), (2, 256), (3, 512)]
+L, B, H, T = 12, 4, 12, 1024
+N_RAND = 1 << 20
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def enc_ops_per_vector(k, N):
+    """Op-count model of encode: 4096 rotation MACs + nb*N*(k+2) search lane-ops."""
+    nb = -(-64 // k)
+    return 4096 + nb * N * (k + 2)
+
+
+def record_bytes(k, N):
+    nb = -(-64 // k)
+    bits = N.bit_length() - 1
+    return 4 * (-(-(nb * bits) // 32))
+
+
+class Timer:
+    """Per-op HIP event pairs on the launch stream (torch's current stream)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pending = []
+        self.ms = {}
+
+    def run(self, name, fn):
+        ev0 = self.torch.cuda.Event(enable_timing=True)
+        ev1 = self.torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        fn()
+        ev1.record()
+        self.pending.append((name, ev0, ev1))
+
+    def collect(self):
+        self.torch.cuda.synchronize()
+        for name, a, b in self.pending:
+            self.ms.setdefault(name, []).append(a.elapsed_time(b))
+        self.pending = []
+
+    def reset(self):
+        self.collect()
+        self.ms = {}
+
+
+def cpu_baseline(n_sample):
+    """Time the oracle on a bounded sample of the same workload (BLAS held to 1 thread)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from kv_cache_compression_fq_amd import fq, synth
+    from oracle import artifact, codec
+    x = synth.kv_slab(2, 0, 0, 1, 1, n_sample).reshape(-1, 64)
+    total = 0.0
+    with threadpool_limits(limits=1):
+        for k, N in VARIANTS:
+            art = artifact.read_artifact(fq.read_codebook_bytes(k, N))
+            t0 = time.perf_counter()
+            idx, nb = codec.encode(x, art["Pi"], art["C"])
+            codec.decode(idx, nb, art["Pi"], art["C"])
+            total += time.perf_counter() - t0
+    return {"value": len(VARIANTS) * n_sample / total, "unit": "vectors/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n_sample} vectors of layer 0 / K / head 0 of the same cache, encode + "
+                      f"decode at each of the 4 variants ({total:.1f} s, numpy float64, "
+                      f"BLAS limited to 1 thread)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=8192)
+    ap.add_argument("--attend-layers", type=int, default=22)
+    ap.add_argument("--attend-steps", type=int, default=10)
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the codec shards by (layer, head) or token range "
+              "with no exchange, so no multi-GPU figure is produced; run with --gpus 1",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from kv_cache_compression_fq_amd import fq, synth
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"device {torch.cuda.get_device_name(0)}")
+
+    # ---------------------------------------------------------------- inputs
+    n = L * 2 * B * H * T
+    t0 = time.time()
+    x_host = synth.kv_cache(2, L, B, H, T).reshape(n, 64)
+    x0 = torch.from_numpy(x_host).to(dev)
+    xs = [x0] + [x0.clone() for _ in VARIANTS[1:]]
+    del x_host
+    cbs = [fq.load_codebook(k, N) for k, N in VARIANTS]
+    codes = [torch.empty((n, cb.W), dtype=torch.int32, device=dev) for cb in cbs]
+    norms = [torch.empty((n,), dtype=torch.int16, device=dev) for _ in cbs]
+    ys = [torch.empty((n, 64), dtype=torch.float16, device=dev) for _ in cbs]
+    rows = torch.from_numpy(synth.random_rows(n, N_RAND, seed=33)).to(dev)
+    y_rand = torch.empty((N_RAND, 64), dtype=torch.float16, device=dev)
+    q = torch.from_numpy(synth.query(B, H, seed=5)).to(dev)
+    per_slab = B * H * T
+    ws_bytes = fq.fq_attend_workspace_size(cbs[0], B, H, H, T)
+    ws = torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device=dev)
+    att_out = torch.empty((B, H, 64), dtype=torch.float16, device=dev)
+    log(f"inputs ready: {n} vectors ({time.time() - t0:.1f} s)")
+
+    timer = Timer(torch)
+
+    def step():
+        for v, cb in enumerate(cbs):
+            timer.run(f"encode_k{cb.k}N{cb.N}",
+                      lambda v=v, cb=cb: fq.fq_encode(cb, xs[v], codes[v], norms[v]))
+            timer.run(f"decode_k{cb.k}N{cb.N}",
+                      lambda v=v, cb=cb: fq.fq_decode(cb, codes[v], norms[v], y=ys[v]))
+        timer.run("random_decode_k2N16",
+                  lambda: fq.fq_decode(cbs[0], codes[0], norms[0], rows=rows, y=y_rand))
+        W = cbs[0].W
+        for layer in range(L):
+            kc = codes[0][(2 * layer) * per_slab:(2 * layer + 1) * per_slab].view(B, H, T, W)
+            vc = codes[0][(2 * layer + 1) * per_slab:(2 * layer + 2) * per_slab].view(B, H, T, W)
+            kn = norms[0][(2 * layer) * per_slab:(2 * layer + 1) * per_slab].view(B, H, T)
+            vn = norms[0][(2 * layer + 1) * per_slab:(2 * layer + 2) * per_slab].view(B, H, T)
+            timer.run("attend_gpt2_k2N16",
+                      lambda kc=kc, vc=vc, kn=kn, vn=vn: fq.fq_attend_decode(
+                          cbs[0], cbs[0], q, kc, kn, vc, vn, 0.125, workspace=ws, out=att_out))
+
+    for _ in range(a.warmup):
+        step()
+    timer.reset()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(a.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    timer.collect()
+    ms_per_step = 1e3 * elapsed / a.steps
+    vectors = 2 * n * len(VARIANTS)               # each vector encoded and decoded
+    value = vectors / (elapsed / a.steps)
+
+    ops = {}
+    for name, lst in timer.ms.items():
+        ops[name] = {"ms_avg": float(np.mean(lst)), "launches": len(lst)}
+    for k, N in VARIANTS:
+        e = ops[f"encode_k{k}N{N}"]
+        e["vectors_per_s"] = n / (e["ms_avg"] * 1e-3)
+        e["ops_per_vector"] = enc_ops_per_vector(k, N)
+        e["alu_tops"] = e["vectors_per_s"] * e["ops_per_vector"] / 1e12
+        e["alu_frac"] = e["alu_tops"] / VALU_PEAK_TOPS
+        d = ops[f"decode_k{k}N{N}"]
+        d["vectors_per_s"] = n / (d["ms_avg"] * 1e-3)
+        d["bytes_per_vector"] = record_bytes(k, N) + 2 + 128
+        d["gbs"] = d["vectors_per_s"] * d["bytes_per_vector"] / 1e9
+        d["hbm_frac"] = d["gbs"] / HBM_PEAK_GBS
+    r = ops["random_decode_k2N16"]
+    r["vectors_per_s"] = N_RAND / (r["ms_avg"] * 1e-3)
+    r["bytes_per_vector"] = 8 + record_bytes(2, 16) + 2 + 128
+    r["gbs"] = r["vectors_per_s"] * r["bytes_per_vector"] / 1e9
+    at = ops["attend_gpt2_k2N16"]
+    at["bytes_per_call"] = per_slab * 2 * (record_bytes(2, 16) + 2) + 2 * B * H * 64 * 2
+    at["gbs"] = at["bytes_per_call"] / (at["ms_avg"] * 1e-3) / 1e9
+
+    # dominant kernel of the step
+    totals = {k: v["ms_avg"] * v["launches"] for k, v in ops.items()}
+    dom = max(totals, key=totals.get)
+    if dom.startswith("encode"):
+        ach = ops[dom]["alu_tops"]
+        roof = {"kernel": dom, "bound": "alu", "achieved": ach, "peak": VALU_PEAK_TOPS,
+                "unit": "Tops/s", "frac": ach / VALU_PEAK_TOPS, "traffic": None}
+    else:
+        ach = ops[dom].get("gbs", 0.0)
+        roof = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None}
+
+    # ---------------------------------------------- TinyLlama-shaped attention
+    attend = None
+    if a.attend_layers > 0:
+        for t in (xs, codes, norms, ys):
+            t.clear()
+        torch.cuda.empty_cache()
+        attend = bench_attend(torch, fq, synth, dev, a.attend_layers, a.attend_steps, a.warmup)
+
+    cpu = None if a.no_cpu_baseline else cpu_baseline(a.cpu_sample)
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "vectors/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "gpt2-small-kv-cache: 12 layers x {K,V} x batch 4 x 12 heads x "
+                               "seq 1024, d=64, fp16; FibQuant k2N16, k2N64, k2N256, k3N512; "
+                               "+ 2^20 random-access decodes + 12-layer decode-step attention",
+                   "vectors": n, "variants": [f"k{k}N{N}" for k, N in VARIANTS],
+                   "parallelism": "single-gpu"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "ops": ops,
+        "attend_tinyllama": attend,
+    }
+    print(json.dumps(out))
+    return 0
+
+
+def bench_attend(torch, fq, synth, dev, layers, steps, warmup):
+    """Fused attention at batch 16, 32 query / 4 KV heads, 32768 tokens, k4N256, per layer."""
+    Bq, Hq, Hkv, Tq = 16, 32, 4, 32768
+    cb = fq.load_codebook(4, 256)
+    per = Bq * Hkv * Tq
+    kc = [torch.empty((Bq, Hkv, Tq, cb.W), dtype=torch.int32, device=dev) for _ in range(layers)]
+    vc = [torch.empty((Bq, Hkv, Tq, cb.W), dtype=torch.int32, device=dev) for _ in range(layers)]
+    kn = [torch.empty((Bq, Hkv, Tq), dtype=torch.int16, device=dev) for _ in range(layers)]
+    vn = [torch.empty((Bq, Hkv, Tq), dtype=torch.int16, device=dev) for _ in range(layers)]
+    t0 = time.time()
+    for layer in range(layers):
+        for kv, (c, nn) in enumerate(((kc, kn), (vc, vn))):
+            x = synth.kv_slab_device(3, layer, kv, Bq, Hkv, Tq, dev).reshape(per, 64)
+            fq.fq_encode(cb, x, c[layer].view(per, cb.W), nn[layer].view(per))
+            del x
+    torch.cuda.synchronize()
+    log(f"attention cache ready: {layers} layers ({time.time() - t0:.1f} s)")
+    q = torch.from_numpy(synth.query(Bq, Hq, seed=5)).to(dev)
+    ws = torch.empty((fq.fq_attend_workspace_size(cb, Bq, Hq, Hkv, Tq),), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((Bq, Hq, 64), dtype=torch.float16, device=dev)
+    timer = Timer(torch)
+
+    def one():
+        for layer in range(layers):
+            timer.run("attend", lambda layer=layer: fq.fq_attend_decode(
+                cb, cb, q, kc[layer], kn[layer], vc[layer], vn[layer], 0.125, workspace=ws,
+                out=out))
+
+    for _ in range(warmup):
+        one()
+    timer.reset()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(steps):
+        one()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t1
+    timer.collect()
+    import numpy as np
+    ms = float(np.mean(timer.ms["attend"]))
+    bytes_layer = per * 2 * (cb.W * 4 + 2) + 2 * Bq * Hq * 64 * 2
+    return {"workload": "tinyllama decode step: batch 16, 32 q / 4 kv heads, seq 32768, d=64, "
+                        f"k4N256 K and V, {layers} layers",
+            "ms_per_layer_event": ms, "ms_per_layer_wall": 1e3 * el / (steps * layers),
+            "bytes_per_layer": bytes_layer, "gbs": bytes_layer / (ms * 1e-3) / 1e9,
+            "hbm_frac": bytes_layer / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

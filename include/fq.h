@@ -76,8 +76,9 @@ const char* fq_status_string(fq_status s);
  * with 2 <= N <= 4096, nb / idx_bits / record_words / last_block consistent,
  * total size, FNV-1a hash, finite values, max |Pi^T Pi - I| <= 1e-9.
  * Returns FQ_ERR_BAD_ARTIFACT for a malformed or corrupt blob,
- * FQ_ERR_UNSUPPORTED for a valid blob the kernels cannot run
- * (k not in {2, 3, 4, 8}).  `out` may be NULL.
+ * FQ_ERR_UNSUPPORTED for a valid blob the kernels are not built for.  Built
+ * (k, N): k = 2 with N in {16, 32, 64, 128, 256}; k = 3 with N in {512, 4096};
+ * k = 4 with N in {4, 256}; k = 8 with N in {16, 256}.  `out` may be NULL.
  */
 fq_status fq_artifact_check(const void* artifact, size_t nbytes, fq_info* out);
 
@@ -123,7 +124,8 @@ fq_status fq_encode(const fq_codebook* cb, const void* x, fq_dtype x_dtype, int6
  * record i and n_records is ignored.
  *
  *   codes [n_records, record_words] uint32, norms [n_records] binary16 (layout of fq_encode)
- *   rows  [n] int64 or NULL, 8-byte aligned
+ *   rows  [n] int64 or NULL, 8-byte aligned; with rows, the record array may span at
+ *         most 2^31 - 1 bytes (n_records * record_words * 4), else FQ_ERR_UNSUPPORTED
  *   y     [n rows, stride y_ld elements] of y_dtype out (F16 rounded to
  *         nearest-even, or F32); y_ld >= 64
  */

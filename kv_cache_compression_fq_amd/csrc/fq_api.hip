@@ -1,0 +1,393 @@
+// C ABI of the FibQuant codec: artifact parsing, device tables, argument checks.
+//
+// The artifact holds the shared rotation and the shared codebook (FibQuant
+// technical summary, sections 2.1-2.3).  Everything here runs on the host;
+// kernels live in fq_encode.hip, fq_decode.hip and fq_attend.hip.
+#include <math.h>
+#include <string.h>
+
+#include <new>
+
+#include "fq_internal.h"
+
+namespace {
+
+constexpr uint32_t HEADER_BYTES = 256;
+constexpr uint32_t VERSION = 1;
+
+struct Header {
+  char magic[4];
+  uint32_t version, header_bytes, d, k, N, nb, bits, W, last, restarts, max_iter, iters, best;
+  uint64_t seed_rot, samples;
+  double tol, d_train, d_test, rate_nom, rate_act, law_a, law_b;
+};
+static_assert(sizeof(Header) == 128, "header layout");
+
+uint64_t fnv1a64(const unsigned char* p, size_t n) {
+  uint64_t h = 0xCBF29CE484222325ull;
+  for (size_t i = 0; i < n; ++i) {
+    h ^= p[i];
+    h *= 0x100000001B3ull;
+  }
+  return h;
+}
+
+bool is_pow2(uint32_t v) { return v && !(v & (v - 1)); }
+
+// Parse + validate.  On success fills hdr and returns pointers into the blob.
+fq_status parse(const void* blob, size_t nbytes, Header* hdr, const double** pi,
+                const float** cw) {
+  if (!blob) return FQ_ERR_INVALID_ARG;
+  if (nbytes < HEADER_BYTES + 8) return FQ_ERR_BAD_ARTIFACT;
+  const unsigned char* b = static_cast<const unsigned char*>(blob);
+  memcpy(hdr, b, sizeof(Header));
+  if (memcmp(hdr->magic, "FQCB", 4) != 0 || hdr->version != VERSION ||
+      hdr->header_bytes != HEADER_BYTES)
+    return FQ_ERR_BAD_ARTIFACT;
+  for (size_t i = sizeof(Header); i < HEADER_BYTES; ++i)
+    if (b[i] != 0) return FQ_ERR_BAD_ARTIFACT;
+  const uint32_t d = hdr->d, k = hdr->k, N = hdr->N;
+  if (d < 1 || d > 4096 || k < 1 || k > d || !is_pow2(N) || N < 2 || N > (1u << 20))
+    return FQ_ERR_BAD_ARTIFACT;
+  const uint64_t want = HEADER_BYTES + 8ull * d * d + 4ull * N * k + 8;
+  if (nbytes != want) return FQ_ERR_BAD_ARTIFACT;
+  uint32_t bits = 0;
+  while ((1u << bits) < N) ++bits;
+  const uint32_t nb = (d + k - 1) / k;
+  if (hdr->nb != nb || hdr->bits != bits || hdr->W != (nb * bits + 31) / 32 ||
+      hdr->last != d - (nb - 1) * k)
+    return FQ_ERR_BAD_ARTIFACT;
+  uint64_t h;
+  memcpy(&h, b + want - 8, 8);
+  if (h != fnv1a64(b, want - 8)) return FQ_ERR_BAD_ARTIFACT;
+  *pi = reinterpret_cast<const double*>(b + HEADER_BYTES);
+  *cw = reinterpret_cast<const float*>(b + HEADER_BYTES + 8ull * d * d);
+  // payload is not guaranteed aligned inside the caller's blob: check through memcpy
+  for (uint64_t i = 0; i < (uint64_t)d * d; ++i) {
+    double v;
+    memcpy(&v, b + HEADER_BYTES + 8 * i, 8);
+    if (!isfinite(v)) return FQ_ERR_BAD_ARTIFACT;
+  }
+  for (uint64_t i = 0; i < (uint64_t)N * k; ++i) {
+    float v;
+    memcpy(&v, b + HEADER_BYTES + 8ull * d * d + 4 * i, 4);
+    if (!isfinite(v)) return FQ_ERR_BAD_ARTIFACT;
+  }
+  // orthogonality of Pi
+  std::vector<double> P((size_t)d * d);
+  memcpy(P.data(), b + HEADER_BYTES, 8ull * d * d);
+  double worst = 0;
+  for (uint32_t i = 0; i < d; ++i)
+    for (uint32_t j = i; j < d; ++j) {
+      double s = 0;
+      for (uint32_t r = 0; r < d; ++r) s += P[(size_t)r * d + i] * P[(size_t)r * d + j];
+      worst = fmax(worst, fabs(s - (i == j ? 1.0 : 0.0)));
+    }
+  if (worst > 1e-9) return FQ_ERR_BAD_ARTIFACT;
+  if (d != (uint32_t)fq::D || N > (uint32_t)fq::MAX_N || !fq::variant_supported(k, bits))
+    return FQ_ERR_UNSUPPORTED;
+  return FQ_OK;
+}
+
+void fill_info(const Header& h, fq_info* o) {
+  o->d = h.d;
+  o->k = h.k;
+  o->N = h.N;
+  o->nb = h.nb;
+  o->idx_bits = h.bits;
+  o->record_words = h.W;
+  o->last_block = h.last;
+  o->reserved = 0;
+  o->rate_nominal = (double)h.bits / h.k;
+  o->rate_actual = (double)h.nb * h.bits / h.d;
+  o->distortion = h.d_test;
+  o->artifact_hash = 0;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct DeviceGuard {
+  int prev = -1;
+  hipError_t err = hipSuccess;
+  explicit DeviceGuard(int dev) {
+    err = hipGetDevice(&prev);
+    if (err == hipSuccess && prev != dev) err = hipSetDevice(dev);
+  }
+  ~DeviceGuard() {
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fq_status_string(fq_status s) {
+  switch (s) {
+    case FQ_OK: return "ok";
+    case FQ_ERR_INVALID_ARG: return "invalid argument";
+    case FQ_ERR_BAD_ARTIFACT: return "bad codebook artifact";
+    case FQ_ERR_UNSUPPORTED: return "unsupported codebook or shape";
+    case FQ_ERR_NO_MEMORY: return "device allocation failed";
+    case FQ_ERR_DEVICE: return "HIP device error";
+  }
+  return "unknown status";
+}
+
+fq_status fq_artifact_check(const void* artifact, size_t nbytes, fq_info* out) {
+  Header h;
+  const double* pi;
+  const float* cw;
+  fq_status st = parse(artifact, nbytes, &h, &pi, &cw);
+  if ((st == FQ_OK || st == FQ_ERR_UNSUPPORTED) && out) {
+    fill_info(h, out);
+    uint64_t hh;
+    memcpy(&hh, static_cast<const unsigned char*>(artifact) + nbytes - 8, 8);
+    out->artifact_hash = hh;
+  }
+  return st;
+}
+
+fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_codebook** out) {
+  if (!out) return FQ_ERR_INVALID_ARG;
+  *out = nullptr;
+  Header h;
+  const double* pi_p;
+  const float* cw_p;
+  fq_status st = parse(artifact, nbytes, &h, &pi_p, &cw_p);
+  if (st != FQ_OK) return st;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) return FQ_ERR_DEVICE;
+  if (device < 0 || device >= ndev) return FQ_ERR_INVALID_ARG;
+
+  fq_codebook* cb = new (std::nothrow) fq_codebook();
+  if (!cb) return FQ_ERR_NO_MEMORY;
+  cb->device = device;
+  cb->d = h.d;
+  cb->k = h.k;
+  cb->N = h.N;
+  cb->nb = h.nb;
+  cb->bits = h.bits;
+  cb->W = h.W;
+  cb->last = h.last;
+  cb->enc_stride = ((h.k + 1) + 3) / 4 * 4;
+  cb->rate_nominal = (double)h.bits / h.k;
+  cb->rate_actual = (double)h.nb * h.bits / h.d;
+  cb->distortion = h.d_test;
+  memcpy(&cb->hash, static_cast<const unsigned char*>(artifact) + nbytes - 8, 8);
+  const int d = cb->d, k = cb->k, N = cb->N, S = cb->enc_stride;
+  cb->pi.resize((size_t)d * d);
+  cb->c.resize((size_t)N * k);
+  memcpy(cb->pi.data(), pi_p, 8ull * d * d);
+  memcpy(cb->c.data(), cw_p, 4ull * N * k);
+
+  // host-side tables
+  std::vector<float> pi32((size_t)d * d), enc((size_t)N * S, 0.f), cb32(cb->c);
+  std::vector<double> cb64((size_t)N * k);
+  std::vector<_Float16> pih((size_t)d * d), pil((size_t)d * d), cbh((size_t)N * k),
+      cbl((size_t)N * k);
+  for (size_t i = 0; i < pi32.size(); ++i) {
+    pi32[i] = (float)cb->pi[i];
+    pih[i] = (_Float16)cb->pi[i];
+    pil[i] = (_Float16)((cb->pi[i] - (double)pih[i]) * 2048.0);
+  }
+  float cmax = 0, cmax_last = 0;
+  for (int n = 0; n < N; ++n) {
+    double cc = 0, cl = 0;
+    for (int t = 0; t < k; ++t) {
+      const double v = cb->c[(size_t)n * k + t];
+      cb64[(size_t)n * k + t] = v;
+      enc[(size_t)n * S + t] = (float)(-2.0 * v);
+      cc += v * v;
+      if (t < cb->last) cl += v * v;
+      cbh[(size_t)n * k + t] = (_Float16)v;
+      cbl[(size_t)n * k + t] = (_Float16)((v - (double)cbh[(size_t)n * k + t]) * 2048.0);
+    }
+    enc[(size_t)n * S + k] = (float)cc;
+    cmax = fmaxf(cmax, (float)sqrt(cc));
+    cmax_last = fmaxf(cmax_last, (float)sqrt(cl));
+  }
+  cb->cmax = cmax;
+  cb->cmax_last = cmax_last;
+  // Pi as B fragments of v_mfma_f32_16x16x32_f16 for Y = Z Pi: fragment
+  // [part][s][nt][lane][e] = part(Pi)[32 s + 8 (lane / 16) + e][16 nt + lane % 16],
+  // part 0 = hi, part 1 = lo; one 16-byte load per lane per (part, s, nt).
+  std::vector<_Float16> frag(2 * 2 * 4 * 64 * 8);
+  for (int part = 0; part < 2; ++part)
+    for (int s2 = 0; s2 < 2; ++s2)
+      for (int nt = 0; nt < 4; ++nt)
+        for (int lane = 0; lane < 64; ++lane)
+          for (int e = 0; e < 8; ++e) {
+            const size_t src = (size_t)(32 * s2 + 8 * (lane / 16) + e) * d + 16 * nt + lane % 16;
+            frag[(((size_t)(part * 2 + s2) * 4 + nt) * 64 + lane) * 8 + e] =
+                part == 0 ? pih[src] : pil[src];
+          }
+
+  // one device allocation, 256-byte aligned sub-buffers
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  const size_t o_pi64 = take(8ull * d * d), o_pi32 = take(4ull * d * d),
+               o_cb64 = take(8ull * N * k), o_enc = take(4ull * N * S),
+               o_cb32 = take(4ull * N * k), o_pih = take(2ull * d * d),
+               o_pil = take(2ull * d * d), o_cbh = take(2ull * N * k),
+               o_cbl = take(2ull * N * k), o_frag = take(2ull * frag.size());
+  cb->dev_bytes = off;
+  {
+    DeviceGuard g(device);
+    if (g.err != hipSuccess) {
+      delete cb;
+      return FQ_ERR_DEVICE;
+    }
+    if (hipMalloc(&cb->dev_block, off) != hipSuccess) {
+      (void)hipGetLastError();
+      delete cb;
+      return FQ_ERR_NO_MEMORY;
+    }
+    char* base = static_cast<char*>(cb->dev_block);
+    cb->t.pi64 = reinterpret_cast<double*>(base + o_pi64);
+    cb->t.pi32 = reinterpret_cast<float*>(base + o_pi32);
+    cb->t.cb64 = reinterpret_cast<double*>(base + o_cb64);
+    cb->t.enc = reinterpret_cast<float*>(base + o_enc);
+    cb->t.cb32 = reinterpret_cast<float*>(base + o_cb32);
+    cb->t.pi16hi = reinterpret_cast<_Float16*>(base + o_pih);
+    cb->t.pi16lo = reinterpret_cast<_Float16*>(base + o_pil);
+    cb->t.cb16hi = reinterpret_cast<_Float16*>(base + o_cbh);
+    cb->t.cb16lo = reinterpret_cast<_Float16*>(base + o_cbl);
+    cb->t.pifrag = reinterpret_cast<_Float16*>(base + o_frag);
+    std::vector<char> staging(off, 0);
+    memcpy(staging.data() + o_pi64, cb->pi.data(), 8ull * d * d);
+    memcpy(staging.data() + o_pi32, pi32.data(), 4ull * d * d);
+    memcpy(staging.data() + o_cb64, cb64.data(), 8ull * N * k);
+    memcpy(staging.data() + o_enc, enc.data(), 4ull * N * S);
+    memcpy(staging.data() + o_cb32, cb32.data(), 4ull * N * k);
+    memcpy(staging.data() + o_pih, pih.data(), 2ull * d * d);
+    memcpy(staging.data() + o_pil, pil.data(), 2ull * d * d);
+    memcpy(staging.data() + o_cbh, cbh.data(), 2ull * N * k);
+    memcpy(staging.data() + o_cbl, cbl.data(), 2ull * N * k);
+    memcpy(staging.data() + o_frag, frag.data(), 2ull * frag.size());
+    if (hipMemcpy(cb->dev_block, staging.data(), off, hipMemcpyHostToDevice) != hipSuccess) {
+      (void)hipGetLastError();
+      (void)hipFree(cb->dev_block);
+      delete cb;
+      return FQ_ERR_DEVICE;
+    }
+  }
+  *out = cb;
+  return FQ_OK;
+}
+
+fq_status fq_codebook_info(const fq_codebook* cb, fq_info* out) {
+  if (!cb || !out) return FQ_ERR_INVALID_ARG;
+  out->d = cb->d;
+  out->k = cb->k;
+  out->N = cb->N;
+  out->nb = cb->nb;
+  out->idx_bits = cb->bits;
+  out->record_words = cb->W;
+  out->last_block = cb->last;
+  out->reserved = 0;
+  out->rate_nominal = cb->rate_nominal;
+  out->rate_actual = cb->rate_actual;
+  out->distortion = cb->distortion;
+  out->artifact_hash = cb->hash;
+  return FQ_OK;
+}
+
+void fq_codebook_free(fq_codebook* cb) {
+  if (!cb) return;
+  {
+    DeviceGuard g(cb->device);
+    if (cb->dev_block) (void)hipFree(cb->dev_block);
+  }
+  delete cb;
+}
+
+fq_status fq_encode(const fq_codebook* cb, const void* x, fq_dtype x_dtype, int64_t n,
+                    int64_t x_ld, uint32_t* codes, uint16_t* norms, void* stream) {
+  if (!cb || n < 0) return FQ_ERR_INVALID_ARG;
+  if (x_dtype != FQ_F16 && x_dtype != FQ_F32) return FQ_ERR_INVALID_ARG;
+  if (n == 0) return FQ_OK;
+  const int esz = x_dtype == FQ_F16 ? 2 : 4;
+  if (!x || !codes || !norms || x_ld < fq::D || (x_ld * esz) % 16 != 0 || !aligned(x, 16) ||
+      !aligned(codes, 4) || !aligned(norms, 2))
+    return FQ_ERR_INVALID_ARG;
+  if (n > (int64_t(1) << 40)) return FQ_ERR_INVALID_ARG;
+  DeviceGuard g(cb->device);
+  if (g.err != hipSuccess) return FQ_ERR_DEVICE;
+  (void)hipGetLastError();
+  hipError_t e = fq::launch_encode(cb, x, x_dtype, n, x_ld, codes, norms,
+                                   static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FQ_OK : FQ_ERR_DEVICE;
+}
+
+fq_status fq_decode(const fq_codebook* cb, const uint32_t* codes, const uint16_t* norms,
+                    const int64_t* rows, int64_t n_records, int64_t n, void* y, fq_dtype y_dtype,
+                    int64_t y_ld, void* stream) {
+  if (!cb || n < 0) return FQ_ERR_INVALID_ARG;
+  if (y_dtype != FQ_F16 && y_dtype != FQ_F32) return FQ_ERR_INVALID_ARG;
+  if (n == 0) return FQ_OK;
+  const int esz = y_dtype == FQ_F16 ? 2 : 4;
+  if (!codes || !norms || !y || y_ld < fq::D || (y_ld * esz) % 16 != 0 || !aligned(y, 16) ||
+      !aligned(codes, 4) || !aligned(norms, 2))
+    return FQ_ERR_INVALID_ARG;
+  if (rows && (!aligned(rows, 8) || n_records < 0)) return FQ_ERR_INVALID_ARG;
+  if (y_ld > (int64_t(1) << 22)) return FQ_ERR_UNSUPPORTED;  // 32-bit offsets per 16-row tile
+  // gathered records are addressed with 32-bit buffer offsets
+  if (rows && n_records * cb->W * 4 > (int64_t(1) << 31) - 1) return FQ_ERR_UNSUPPORTED;
+  if (n > (int64_t(1) << 40)) return FQ_ERR_INVALID_ARG;
+  DeviceGuard g(cb->device);
+  if (g.err != hipSuccess) return FQ_ERR_DEVICE;
+  (void)hipGetLastError();
+  hipError_t e = fq::launch_decode(cb, codes, norms, rows, rows ? n_records : n, n, y, y_dtype,
+                                   y_ld, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FQ_OK : FQ_ERR_DEVICE;
+}
+
+static fq_status check_attend_shape(const fq_codebook* ck, int B, int Hq, int Hkv, int64_t T) {
+  if (!ck || B < 1 || Hq < 1 || Hkv < 1 || T < 1) return FQ_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return FQ_ERR_INVALID_ARG;
+  if (Hq / Hkv > 16) return FQ_ERR_UNSUPPORTED;
+  if (T > (int64_t(1) << 31) || (int64_t)B * Hkv > (1 << 20)) return FQ_ERR_UNSUPPORTED;
+  return FQ_OK;
+}
+
+fq_status fq_attend_workspace_size(const fq_codebook* cb_k, int B, int Hq, int Hkv, int64_t T,
+                                   size_t* bytes) {
+  if (!bytes) return FQ_ERR_INVALID_ARG;
+  fq_status st = check_attend_shape(cb_k, B, Hq, Hkv, T);
+  if (st != FQ_OK) return st;
+  *bytes = fq::attend_workspace_bytes(cb_k, B, Hq, Hkv, T);
+  return FQ_OK;
+}
+
+fq_status fq_attend_decode(const fq_codebook* cb_k, const fq_codebook* cb_v, const uint16_t* q,
+                           const uint32_t* k_codes, const uint16_t* k_norms,
+                           const uint32_t* v_codes, const uint16_t* v_norms, int B, int Hq,
+                           int Hkv, int64_t T, float scale, void* workspace,
+                           size_t workspace_bytes, uint16_t* out, void* stream) {
+  fq_status st = check_attend_shape(cb_k, B, Hq, Hkv, T);
+  if (st != FQ_OK) return st;
+  if (!cb_v || cb_v->device != cb_k->device) return FQ_ERR_INVALID_ARG;
+  if (!q || !k_codes || !k_norms || !v_codes || !v_norms || !workspace || !out)
+    return FQ_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) ||
+      !aligned(k_norms, 16) || !aligned(v_norms, 16) || !aligned(workspace, 256))
+    return FQ_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return FQ_ERR_INVALID_ARG;
+  if (workspace_bytes < fq::attend_workspace_bytes(cb_k, B, Hq, Hkv, T))
+    return FQ_ERR_INVALID_ARG;
+  DeviceGuard g(cb_k->device);
+  if (g.err != hipSuccess) return FQ_ERR_DEVICE;
+  (void)hipGetLastError();
+  hipError_t e = fq::launch_attend(cb_k, cb_v, q, k_codes, k_norms, v_codes, v_norms, B, Hq, Hkv,
+                                   T, scale, workspace, out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FQ_OK : FQ_ERR_DEVICE;
+}
+
+}  // extern "C"

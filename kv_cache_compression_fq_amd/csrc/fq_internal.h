@@ -1,0 +1,96 @@
+// Internal declarations shared by the library's own translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "fq.h"
+
+namespace fq {
+
+constexpr int D = 64;             // vector length handled by the kernels
+constexpr int MAX_N = 4096;       // largest codebook
+constexpr int MAX_WORDS = 12;     // record words for k >= 2, N <= 4096: ceil(32*12/32)
+
+// (k, index bits) pairs the kernels are built for: the configurations' rates
+// (k=2: N 16 / 64 / 256, k=3: N 512 / 4096, k=4: N 4 / 256, k=8: N 16 / 256)
+// plus the fractional k=2 rates 2.5 and 3.5 (N 32 / 128).  X(k, bits).
+#define FQ_VARIANTS(X) \
+  X(2, 4) X(2, 5) X(2, 6) X(2, 7) X(2, 8) X(3, 9) X(3, 12) X(4, 2) X(4, 8) X(8, 4) X(8, 8)
+
+inline bool variant_supported(int k, int bits) {
+#define FQ_IS(KK, BB) if (k == KK && bits == BB) return true;
+  FQ_VARIANTS(FQ_IS)
+#undef FQ_IS
+  return false;
+}
+
+// Per-codebook device tables, all inside one allocation.
+struct DeviceTables {
+  double* pi64;     // [64][64] Pi, row-major (z = Pi u)
+  float* pi32;      // [64][64] Pi rounded to float32
+  double* cb64;     // [N][k]  codewords (exact float32 values) as float64
+  float* enc;       // [N][S]  search table: -2 c_0 .. -2 c_{k-1}, |c|^2, zero pad; S = enc_stride
+  float* cb32;      // [N][k]  codewords
+  _Float16* pi16hi; // [64][64] Pi rounded to binary16
+  _Float16* pi16lo; // [64][64] (Pi - hi) * 2^11 rounded to binary16
+  _Float16* cb16hi; // [N][k]   codewords rounded to binary16
+  _Float16* cb16lo; // [N][k]   (c - hi) * 2^11 rounded to binary16
+  _Float16* pifrag; // Pi as v_mfma_f32_16x16x32_f16 B fragments, see fq_api.hip
+};
+
+}  // namespace fq
+
+struct fq_codebook {
+  int device;
+  int d, k, N, nb, bits, W, last;
+  int enc_stride;
+  double rate_nominal, rate_actual, distortion;
+  uint64_t hash;
+  float cmax;       // max codeword norm (float32 table)
+  float cmax_last;  // max norm of the first `last` coordinates of a codeword
+  std::vector<double> pi;  // host copy of Pi
+  std::vector<float> c;    // host copy of C
+  void* dev_block;         // the single device allocation
+  size_t dev_bytes;
+  fq::DeviceTables t;
+};
+
+namespace fq {
+
+// Launchers (return hipSuccess or the launch error).  Shapes are validated by
+// the caller; pointers are device pointers.
+hipError_t launch_encode(const fq_codebook* cb, const void* x, fq_dtype xt, int64_t n,
+                         int64_t ld, uint32_t* codes, uint16_t* norms, hipStream_t s);
+hipError_t launch_decode(const fq_codebook* cb, const uint32_t* codes, const uint16_t* norms,
+                         const int64_t* rows, int64_t n_records, int64_t n, void* y,
+                         fq_dtype yt, int64_t ld, hipStream_t s);
+size_t attend_workspace_bytes(const fq_codebook* cb_k, int B, int Hq, int Hkv, int64_t T);
+hipError_t launch_attend(const fq_codebook* ck, const fq_codebook* cv, const uint16_t* q,
+                         const uint32_t* kc, const uint16_t* kn, const uint32_t* vc,
+                         const uint16_t* vn, int B, int Hq, int Hkv, int64_t T, float scale,
+                         void* ws, uint16_t* out, hipStream_t s);
+
+// Workgroups of `kern` that fit on the current device at once (CUs x blocks per CU),
+// or 0 if the runtime cannot say.
+inline int64_t resident_blocks(const void* kern, int threads, size_t shm) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, shm) != hipSuccess)
+    return 0;
+  return (int64_t)cus * (per_cu < 1 ? 1 : per_cu);
+}
+
+// Binary16 helpers usable on host and device.
+__host__ __device__ inline uint16_t f32_to_f16_bits(float f) {
+  _Float16 h = (_Float16)f;
+  uint16_t b;
+  __builtin_memcpy(&b, &h, 2);
+  return b;
+}
+
+}  // namespace fq

@@ -93,3 +93,22 @@ def random_norms(shape, seed, lo=0.5, hi=2.5):
     """binary16 norms 10^U(lo, hi) as uint16 bit patterns."""
     rng = np.random.default_rng(seed)
     return (10.0 ** rng.uniform(lo, hi, size=shape)).astype(np.float16).view(np.uint16)
+
+
+def kv_slab_device(cfg_seed, layer, kv, B, H, T, device, outliers=True, d=D):
+    """Device-side slab [B, H, T, d] binary16 with the same recipe (bench inputs only).
+
+    The per-channel scales come from the same numpy stream as ``kv_slab``; the
+    Gaussian draws come from a torch generator seeded from that stream, so the
+    values are seeded and reproducible but not bit-identical to ``kv_slab``.
+    """
+    import torch
+    out = torch.empty((B, H, T, d), dtype=torch.float16, device=device)
+    for h in range(H):
+        rng = np.random.default_rng([cfg_seed, layer, kv, h])
+        s = torch.from_numpy(stream_scales(rng, d, outliers)).float().to(device)
+        gen = torch.Generator(device=device)
+        gen.manual_seed(int(rng.integers(0, 2 ** 62)))
+        g = torch.randn((B, T, d), generator=gen, device=device, dtype=torch.float32)
+        out[:, h] = (g * s).half()
+    return out

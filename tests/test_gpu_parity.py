@@ -1,0 +1,201 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Contract:
+* indices equal the oracle's, or fall in the near-tie window
+  D(i) - D_min <= 1e-6 D(i) (float64 distances); out-of-window count must be 0;
+* norms bit-exact, except +-1 binary16 ulp where the exact norm lies within
+  1e-6 (relative) of a rounding midpoint; unused record bits are 0;
+* decode of the oracle's codes: max |y - x_hat| <= 1e-3 * nu16 per vector;
+* attention on identical inputs: per (b, h) relative L2 error <= 2e-3.
+Inputs are the seeded synthetic generators of ``kv_cache_compression_fq_amd.synth``.
+"""
+import numpy as np
+import pytest
+
+from kv_cache_compression_fq_amd import fq, synth
+from oracle import artifact, attend, codec
+
+from conftest import VARIANTS, artifact_path
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    print("device:", torch.cuda.get_device_name(0), flush=True)
+    return torch.device("cuda:0")
+
+
+_BOOKS = {}
+
+
+def book(k, N):
+    """(oracle artifact dict, GPU codebook) for a variant, loaded once."""
+    if (k, N) not in _BOOKS:
+        blob = open(artifact_path(k, N), "rb").read()
+        _BOOKS[(k, N)] = (artifact.read_artifact(blob), fq.fq_codebook_load(blob, 0))
+    return _BOOKS[(k, N)]
+
+
+def to_dev(a, dev, view=None):
+    a = np.ascontiguousarray(a)
+    if view is not None:
+        a = a.view(view)
+    return torch.from_numpy(a).to(dev)
+
+
+def gpu_encode(cb, x, dev):
+    codes, norms = fq.fq_encode(cb, to_dev(x, dev))
+    torch.cuda.synchronize()
+    return codes.cpu().numpy().view(np.uint32), norms.cpu().numpy().view(np.uint16)
+
+
+def check_norms(x, norms):
+    nu = np.sqrt(np.sum(np.asarray(x, dtype=np.float64) ** 2, axis=1))
+    want = codec.f16_round(nu)
+    diff = np.nonzero(norms != want)[0]
+    for r in diff:
+        lo = codec.f16_value(np.array([min(norms[r], want[r])]))[0]
+        hi = codec.f16_value(np.array([max(norms[r], want[r])]))[0]
+        mid = 0.5 * (lo + hi)
+        assert abs(int(norms[r]) - int(want[r])) == 1, (r, norms[r], want[r])
+        assert abs(nu[r] - mid) <= 1e-6 * nu[r], (r, nu[r], mid)
+    return len(diff)
+
+
+def check_encode(art, x, codes, norms):
+    nb, bits, W = art["nb"], art["bits"], art["W"]
+    assert codes.shape == (len(x), W)
+    used = nb * bits - 32 * (W - 1)
+    if used < 32:
+        assert np.all((codes[:, -1] >> np.uint32(used)) == 0), "pad bits not zero"
+    idx = codec.unpack(codes, nb, bits)
+    ex, win, bad = codec.accept_indices(x, art["Pi"], art["C"], idx)
+    assert bad == 0, f"{bad} indices outside the near-tie window ({ex} exact, {win} in window)"
+    check_norms(x, norms)
+    return ex, win
+
+
+# ------------------------------------------------------------------ encode
+def test_encode_tiny_fp32(dev):
+    art, cb = book(2, 16)
+    x = np.concatenate([synth.tiny_vectors(4096), synth.tiny_vectors(37, seed=2),
+                        synth.special_vectors(dtype=np.float32)])
+    codes, norms = gpu_encode(cb, x, dev)
+    ex, win = check_encode(art, x, codes, norms)
+    print(f"tiny fp32: {ex} exact, {win} in window")
+
+
+@pytest.mark.parametrize("k,N", VARIANTS)
+def test_encode_variants_fp16(dev, k, N):
+    art, cb = book(k, N)
+    x = np.concatenate([synth.kv_slab(2, 0, 0, 2, 3, 411).reshape(-1, 64),
+                        synth.special_vectors()])
+    codes, norms = gpu_encode(cb, x, dev)
+    ex, win = check_encode(art, x, codes, norms)
+    print(f"k{k}N{N}: {ex} exact, {win} in window")
+
+
+def test_encode_strided_rows_and_empty(dev):
+    art, cb = book(3, 512)
+    x = synth.kv_slab(2, 1, 1, 1, 2, 300).reshape(-1, 64)
+    wide = np.zeros((len(x), 72), dtype=np.float16)
+    wide[:, :64] = x
+    wide[:, 64:] = 1000.0                      # must be ignored
+    xt = to_dev(wide, dev)
+    codes, norms = fq.fq_encode(cb, xt[:, :64])
+    torch.cuda.synchronize()
+    c2, n2 = gpu_encode(cb, x, dev)
+    assert np.array_equal(codes.cpu().numpy().view(np.uint32), c2)
+    assert np.array_equal(norms.cpu().numpy().view(np.uint16), n2)
+    e = torch.empty((0, 64), dtype=torch.float16, device=dev)
+    fq.fq_encode(cb, e)                        # n == 0: no-op
+
+
+def test_encode_rejects_misaligned(dev):
+    art, cb = book(2, 16)
+    x = torch.zeros((10, 72), dtype=torch.float16, device=dev)
+    with pytest.raises(fq.FQError) as e:
+        fq.fq_encode(cb, x[:, 1:65])
+    assert e.value.status == fq.FQ_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------------ decode
+@pytest.mark.parametrize("k,N", VARIANTS)
+@pytest.mark.parametrize("ydt", ["f16", "f32"])
+def test_decode_variants(dev, k, N, ydt):
+    art, cb = book(k, N)
+    x = np.concatenate([synth.kv_slab(3, 0, 1, 2, 2, 333).reshape(-1, 64),
+                        synth.special_vectors()])
+    idx, nbits = codec.encode(x, art["Pi"], art["C"])
+    words = codec.pack(idx, art["bits"])
+    y = fq.fq_decode(cb, to_dev(words, dev, np.int32), to_dev(nbits, dev, np.int16),
+                     y_dtype=torch.float16 if ydt == "f16" else torch.float32)
+    torch.cuda.synchronize()
+    want = codec.decode(idx, nbits, art["Pi"], art["C"])
+    got = y.float().cpu().numpy().astype(np.float64)
+    nu16 = codec.f16_value(nbits)
+    err = np.max(np.abs(got - want), axis=1)
+    assert np.all(err <= 1e-3 * nu16 + 1e-30), float(np.max(err / np.maximum(nu16, 1e-30)))
+    print(f"k{k}N{N} {ydt}: max err/nu {np.max(err / np.maximum(nu16, 1e-30)):.2e}")
+
+
+def test_random_access_decode(dev):
+    art, cb = book(4, 256)
+    x = synth.kv_slab(3, 0, 0, 4, 1, 500).reshape(-1, 64)
+    idx, nbits = codec.encode(x, art["Pi"], art["C"])
+    words = codec.pack(idx, art["bits"])
+    rows = synth.random_rows(len(x), 3001, seed=34)
+    rows[:5] = [0, len(x) - 1, 7, 7, 0]
+    rows[5], rows[6] = -1, len(x)               # out of range: zero rows
+    y = fq.fq_decode(cb, to_dev(words, dev, np.int32), to_dev(nbits, dev, np.int16),
+                     rows=to_dev(rows, dev), y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().astype(np.float64)
+    full = codec.decode(idx, nbits, art["Pi"], art["C"])
+    ok = (rows >= 0) & (rows < len(x))
+    want = np.zeros_like(got)
+    want[ok] = full[rows[ok]]
+    nu16 = np.zeros(len(rows))
+    nu16[ok] = codec.f16_value(nbits)[rows[ok]]
+    err = np.max(np.abs(got - want), axis=1)
+    assert np.all(err <= 1e-3 * nu16)
+    assert np.all(got[~ok] == 0)
+
+
+# ---------------------------------------------------------------- attention
+ATT_CASES = [
+    # (B, Hq, Hkv, T, K codebook, V codebook)
+    (1, 4, 1, 1, (4, 256), (4, 256)),
+    (2, 8, 1, 300, (4, 256), (4, 256)),
+    (2, 32, 4, 1000, (4, 256), (2, 16)),
+    (1, 16, 1, 777, (3, 512), (8, 256)),
+    (2, 12, 12, 1024, (2, 64), (2, 64)),
+    (1, 8, 8, 4099, (8, 16), (4, 4)),
+]
+
+
+@pytest.mark.parametrize("case", ATT_CASES, ids=lambda c: f"B{c[0]}Hq{c[1]}Hkv{c[2]}T{c[3]}")
+def test_attention(dev, case):
+    B, Hq, Hkv, T, kb, vb = case
+    ak, ck = book(*kb)
+    av, cv = book(*vb)
+    seed = B * 1000 + T
+    kw = synth.random_records((B, Hkv, T), ck.W, ck.nb * ck.info["idx_bits"], seed)
+    vw = synth.random_records((B, Hkv, T), cv.W, cv.nb * cv.info["idx_bits"], seed + 1)
+    kn = synth.random_norms((B, Hkv, T), seed + 2)
+    vn = synth.random_norms((B, Hkv, T), seed + 3)
+    q = synth.query(B, Hq, seed=seed + 4)
+    o = fq.fq_attend_decode(ck, cv, to_dev(q, dev), to_dev(kw, dev, np.int32),
+                            to_dev(kn, dev, np.int16), to_dev(vw, dev, np.int32),
+                            to_dev(vn, dev, np.int16), 0.125)
+    torch.cuda.synchronize()
+    ref = attend.attend(q, kw, kn, vw, vn, ak["Pi"], ak["C"], av["C"], 0.125)
+    got = o.float().cpu().numpy().astype(np.float64)
+    rel = np.linalg.norm(got - ref, axis=-1) / np.linalg.norm(ref, axis=-1)
+    print(f"{case}: max rel {np.max(rel):.2e}")
+    assert np.max(rel) <= 2e-3
