@@ -152,10 +152,12 @@ fq_status fq_attend_workspace_size(const fq_codebook* cb_k, int B, int Hq, int H
  *   k_codes  [B, Hkv, T, Wk] uint32,  k_norms [B, Hkv, T] binary16  (cb_k layout)
  *   v_codes  [B, Hkv, T, Wv] uint32,  v_norms [B, Hkv, T] binary16  (cb_v layout)
  *   out      [B, Hq, 64] binary16
- *   Hq % Hkv == 0, Hq / Hkv <= 16, T >= 1; workspace of at least
+ *   Hq % Hkv == 0, Hq / Hkv <= 8, T >= 1; workspace of at least
  *   fq_attend_workspace_size bytes, 256-byte aligned, contents need not be
- *   initialised.  cb_k and cb_v may be the same handle; both must be on the
- *   same device.
+ *   initialised.  cb_k and cb_v may be the same handle; they must be on the
+ *   same device and hold the same (k, N) variant (one shared codebook serves
+ *   keys and values [FQ 2.1]); the k = 3, N = 4096 tables exceed the kernel's
+ *   LDS budget (FQ_ERR_UNSUPPORTED).  All pointers 16-byte aligned.
  */
 fq_status fq_attend_decode(const fq_codebook* cb_k, const fq_codebook* cb_v, const uint16_t* q,
                            const uint32_t* k_codes, const uint16_t* k_norms,

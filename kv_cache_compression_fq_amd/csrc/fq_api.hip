@@ -352,7 +352,8 @@ fq_status fq_decode(const fq_codebook* cb, const uint32_t* codes, const uint16_t
 static fq_status check_attend_shape(const fq_codebook* ck, int B, int Hq, int Hkv, int64_t T) {
   if (!ck || B < 1 || Hq < 1 || Hkv < 1 || T < 1) return FQ_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return FQ_ERR_INVALID_ARG;
-  if (Hq / Hkv > 16) return FQ_ERR_UNSUPPORTED;
+  if (Hq / Hkv > 8) return FQ_ERR_UNSUPPORTED;
+  if (!fq::attend_supported(ck)) return FQ_ERR_UNSUPPORTED;
   if (T > (int64_t(1) << 31) || (int64_t)B * Hkv > (1 << 20)) return FQ_ERR_UNSUPPORTED;
   return FQ_OK;
 }
@@ -374,6 +375,7 @@ fq_status fq_attend_decode(const fq_codebook* cb_k, const fq_codebook* cb_v, con
   fq_status st = check_attend_shape(cb_k, B, Hq, Hkv, T);
   if (st != FQ_OK) return st;
   if (!cb_v || cb_v->device != cb_k->device) return FQ_ERR_INVALID_ARG;
+  if (cb_v->k != cb_k->k || cb_v->N != cb_k->N) return FQ_ERR_UNSUPPORTED;
   if (!q || !k_codes || !k_norms || !v_codes || !v_norms || !workspace || !out)
     return FQ_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) ||

@@ -4,231 +4,507 @@
 //   <q, nu Pi^T z_hat> = nu <Pi q, z_hat>,   sum_t p_t nu_t Pi^T z_hat_t = Pi^T sum_t p_t nu_t z_hat_t
 // so only the query is rotated on the way in and the output once on the way out.
 //
-// Split-K over the context: kernel A computes, for each (batch, KV head, split),
-// the running max m, the sum l and the unnormalised rotated output of every
-// query head of the group; kernel B merges the splits (log-sum-exp), applies
-// Pi^T and writes binary16.
+// Kernel A, one wave per (batch, KV head, split of the context), G = Hq / Hkv <= 8
+// query heads per wave, tiles of 64 tokens:
+//  * lane t loads the K and V records and norms of token t (unconditional
+//    buffer loads, next two tiles in flight) and unpacks them into 16-bit index
+//    tables in LDS;
+//  * scores S^T = Z_k [Q_hi | Q_lo]^T on v_mfma_f32_16x16x32_f16: A = the
+//    tile's key codewords gathered from the LDS codebook (binary16 hi and
+//    lo = (c - hi) 2^11), B = the rotated, scaled queries of the group in
+//    columns 0..G-1 (binary16 hi) and 8..8+G-1 (lo = (q - hi) 2^11); one DPP
+//    rotation folds the lo columns in.  The scores carry ~22 bits, which the
+//    outlier-heavy caches need (rounding only the key codebook to binary16
+//    moves attention outputs by up to 1e-2 relative);
+//  * online softmax in registers: lane (h, g) owns head h and tokens
+//    4g..4g+3 of every 16-token sub-tile;
+//  * values O^T = Z_v^T P'^T (P' = p * nu_v in binary16): the A operand is
+//    fetched with ds_read_tr16_b64 transpose reads pointed straight at the
+//    value codewords in LDS (k = 4 or 8), or at value rows expanded into LDS
+//    (k = 2 or 3), in binary16 (relative rounding 2^-12 per coordinate: at
+//    most ~1e-3 relative on the same caches, inside the 2e-3 bound);
+//  * scores are kept in the log2 domain (the query carries scale * log2 e), so
+//    every softmax weight is one exp2;
+//  * the wave writes its (m, l, o) partial per query head.
+// Kernel B merges the splits (log-sum-exp), applies Pi^T and writes binary16.
 #include "fq_common.h"
 #include "fq_internal.h"
 
 namespace fq {
 namespace {
 
-constexpr int ATT_THREADS = 256;
-constexpr int ATT_TILE = 64;      // tokens per tile
-constexpr int MAX_G = 16;         // query heads per KV head
-constexpr int PART = D + 2;       // floats per partial: m, l, o[64]
+constexpr int ATT_WAVES = 4;
+constexpr int ATT_THREADS = 64 * ATT_WAVES;
+constexpr int TILE = 64;           // tokens per wave iteration (one lane per token)
+constexpr int MAX_G = 8;           // query heads per KV head
+constexpr int PART = D + 2;        // floats per partial: m, l, o[64]
+constexpr int Q_PITCH = D + 8;     // binary16 row pitch of the query table
+constexpr int Z_PITCH = D + 4;     // binary16 row pitch of expanded value rows
+constexpr float NEG_BIG = -3.0e38f;
 
 struct SplitPlan {
-  int S;
-  int64_t chunk;
+  int S;          // workgroup splits per (batch, KV head)
+  int64_t chunk;  // tokens per workgroup split, a multiple of ATT_WAVES * TILE
 };
 
+// About 1024 workgroups (4096 waves) over the device; each wave gets at least
+// one tile.  The four waves of a workgroup take interleaved tiles of its split.
 SplitPlan plan_splits(int B, int Hkv, int64_t T) {
+  constexpr int64_t STEP = (int64_t)ATT_WAVES * TILE;
   const int64_t pairs = (int64_t)B * Hkv;
   int64_t S = (1024 + pairs - 1) / pairs;
-  const int64_t max_s = (T + 255) / 256;
+  const int64_t max_s = (T + STEP - 1) / STEP;
   if (S > max_s) S = max_s;
   if (S < 1) S = 1;
   int64_t chunk = (T + S - 1) / S;
-  chunk = (chunk + ATT_TILE - 1) / ATT_TILE * ATT_TILE;
+  chunk = (chunk + STEP - 1) / STEP * STEP;
   S = (T + chunk - 1) / chunk;
   return {(int)S, chunk};
 }
 
-template <int KK, int KV>
-__global__ __launch_bounds__(ATT_THREADS) void attend_split_ref_kernel(
+template <int K, int BITS>
+struct AttShape {
+  using Sh = Shape<K, BITS>;
+  static constexpr bool EXPAND = !(K == 4 || K == 8);   // value rows expanded into LDS
+  __host__ __device__ static constexpr size_t wave_lds() {
+    return (size_t)2 * TILE * Sh::IDX_PITCH * 2 + 2 * TILE * 4 +
+           (EXPAND ? (size_t)TILE * Z_PITCH * 2 : 0);
+  }
+};
+
+template <int W>
+struct TileRegs {
+  uint32_t kw[W], vw[W];
+  uint32_t kn, vn;   // raw binary16 norms
+};
+
+// Key codebook layout in LDS.  k = 2, 4, 8: one interleaved row per codeword,
+// hi part then lo part (2k binary16), so one read fetches both; k = 3: two
+// separate [N][3] tables (gathered a coordinate at a time).
+template <int K>
+struct KeyTable {
+  static constexpr bool INTERLEAVED = (K == 2 || K == 4 || K == 8);
+};
+
+// Coordinates [c0, c0 + 8) of one key row, hi and lo parts (c0 multiple of 8).
+template <int K>
+__device__ inline void gather8_hl(const uint16_t* idx, const _Float16* tab, const _Float16* tab_lo,
+                                  int c0, half8& hi, half8& lo) {
+  if constexpr (K == 8) {
+    const uint32_t i0 = idx[c0 >> 3];
+    hi = *reinterpret_cast<const half8*>(tab + i0 * 16);
+    lo = *reinterpret_cast<const half8*>(tab + i0 * 16 + 8);
+  } else if constexpr (K == 4) {
+    const uint32_t pair = *reinterpret_cast<const uint32_t*>(idx + (c0 >> 2));
+    const u32x4 a = *reinterpret_cast<const u32x4*>(tab + (pair & 0xFFFFu) * 8);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(tab + (pair >> 16) * 8);
+    const u32x4 hv = {a.x, a.y, b.x, b.y}, lv = {a.z, a.w, b.z, b.w};
+    hi = __builtin_bit_cast(half8, hv);
+    lo = __builtin_bit_cast(half8, lv);
+  } else if constexpr (K == 2) {
+    const uint2 q = *reinterpret_cast<const uint2*>(idx + (c0 >> 1));
+    const uint2* t = reinterpret_cast<const uint2*>(tab);
+    const uint2 a = t[q.x & 0xFFFFu], b = t[q.x >> 16], c = t[q.y & 0xFFFFu], d = t[q.y >> 16];
+    const u32x4 hv = {a.x, b.x, c.x, d.x}, lv = {a.y, b.y, c.y, d.y};
+    hi = __builtin_bit_cast(half8, hv);
+    lo = __builtin_bit_cast(half8, lv);
+  } else {  // K = 3: one coordinate at a time; the last block may be partial
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int c = c0 + e;
+      const int j = c / K, t = c - j * K;
+      const uint32_t i0 = idx[j];
+      hi[e] = tab[i0 * K + t];
+      lo[e] = tab_lo[i0 * K + t];
+    }
+  }
+}
+
+// ds_read_tr16_b64: within each 16-lane group, output lane i element m is
+// element i % 4 of the 64-bit row addressed by lane 4 m + i / 4 of the group.
+__device__ inline half4 read_tr(const _Float16* p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s lds_v4s;
+  const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p));  // address-space cast
+  return __builtin_bit_cast(half4, v);
+}
+
+__device__ inline float rot8(float x) {   // value of lane (l +- 8) within its 16-lane row
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
+}
+
+constexpr int MERGE_PITCH = PART + 2;   // floats per wave partial in the LDS merge area
+
+template <int K, int BITS>
+struct AttLds {
+  using Sh = Shape<K, BITS>;
+  __host__ __device__ static size_t key_bytes(int N) {   // key table(s)
+    return ((size_t)N * 2 * K * 2 + 15) / 16 * 16;
+  }
+  __host__ __device__ static size_t val_bytes(int N) {   // value table (binary16)
+    return ((size_t)N * K * 2 + 15) / 16 * 16;
+  }
+  __host__ __device__ static size_t total(int N) {
+    return key_bytes(N) + val_bytes(N) + 16 * Q_PITCH * 2 + MAX_G * D * 4 +
+           ATT_WAVES * AttShape<K, BITS>::wave_lds() + ATT_WAVES * MAX_G * MERGE_PITCH * 4;
+  }
+};
+
+template <int K, int BITS>
+__global__ __launch_bounds__(ATT_THREADS) void attend_split_kernel(
     const uint16_t* __restrict__ q, const uint32_t* __restrict__ kc,
     const uint16_t* __restrict__ kn, const uint32_t* __restrict__ vc,
-    const uint16_t* __restrict__ vn, int Hq, int Hkv, int64_t T, int64_t chunk, float scale,
-    const float* __restrict__ pi32, const float* __restrict__ cbk, int Nk, int bitsk, int Wk,
-    const float* __restrict__ cbv, int Nv, int bitsv, int Wv, float* __restrict__ ws, int S) {
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const uint16_t* __restrict__ vn, int Hq, int Hkv, int64_t T, int64_t chunk, int S,
+    float scale, const float* __restrict__ pi32, const _Float16* __restrict__ kh_g,
+    const _Float16* __restrict__ kl_g, const _Float16* __restrict__ vh_g, int N,
+    float* __restrict__ ws) {
+  using Sh = Shape<K, BITS>;
+  using AS = AttShape<K, BITS>;
+  using L = AttLds<K, BITS>;
+  constexpr int W = Sh::W, IP = Sh::IDX_PITCH;
   const int G = Hq / Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t t0 = (int64_t)split * chunk;
-  const int64_t t1 = t0 + chunk < T ? t0 + chunk : T;
+  const int sw = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int col = lane & 15, grp = lane >> 4;
 
   extern __shared__ __align__(16) unsigned char smem[];
-  float* sQ = reinterpret_cast<float*>(smem);             // [G][64] rotated, scaled queries
-  float* sPart = sQ + MAX_G * D;                           // [4][G][TILE] partial scores
-  float* sP = sPart + 4 * MAX_G * ATT_TILE;                // [G][TILE] p * nu_v
-  float* sAlpha = sP + MAX_G * ATT_TILE;                   // [G]
-  float* sCbK = sAlpha + MAX_G;                            // [Nk][KK]
-  float* sCbV = sCbK + Nk * KK;                            // [Nv][KV]
+  _Float16* sK = reinterpret_cast<_Float16*>(smem);                      // key table(s)
+  _Float16* sKlo = sK + (size_t)N * K;                                   // k = 3 lo table
+  _Float16* sVh = reinterpret_cast<_Float16*>(smem + L::key_bytes(N));
+  _Float16* sQ = reinterpret_cast<_Float16*>(smem + L::key_bytes(N) + L::val_bytes(N));
+  float* sQf = reinterpret_cast<float*>(sQ + 16 * Q_PITCH);             // [MAX_G][D] raw q
+  unsigned char* wbase = reinterpret_cast<unsigned char*>(sQf + MAX_G * D) +
+                         (size_t)wave * AS::wave_lds();
+  float* sMerge = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(sQf + MAX_G * D) +
+                                           ATT_WAVES * AS::wave_lds());   // [wave][h][MERGE_PITCH]
+  uint16_t* sKi = reinterpret_cast<uint16_t*>(wbase);            // [TILE][IP]
+  uint16_t* sVi = sKi + TILE * IP;                               // [TILE][IP]
+  float* sNk = reinterpret_cast<float*>(sVi + TILE * IP);        // [TILE]
+  float* sNv = sNk + TILE;                                       // [TILE]
+  _Float16* sZh = reinterpret_cast<_Float16*>(sNv + TILE);       // [TILE][Z_PITCH] (expand)
 
-  for (int e = tid; e < Nk * KK; e += ATT_THREADS) sCbK[e] = cbk[e];
-  for (int e = tid; e < Nv * KV; e += ATT_THREADS) sCbV[e] = cbv[e];
-  // q_rot[h][c] = scale * sum_i Pi[c][i] q[b, g*G + h][i]
-  for (int e = tid; e < G * D; e += ATT_THREADS) {
+  for (int e = threadIdx.x; e < N * K; e += ATT_THREADS) {
+    const int n = e / K, t = e - n * K;
+    if constexpr (KeyTable<K>::INTERLEAVED) {
+      sK[n * 2 * K + t] = kh_g[e];
+      sK[n * 2 * K + K + t] = kl_g[e];
+    } else {
+      sK[e] = kh_g[e];
+      sKlo[e] = kl_g[e];
+    }
+    sVh[e] = vh_g[e];
+  }
+  for (int e = threadIdx.x; e < MAX_G * D; e += ATT_THREADS) {
+    const int h = e / D;
+    sQf[e] = h < G ? f16_bits_to_f32(q[((int64_t)b * Hq + (int64_t)g * G + h) * D + (e % D)]) : 0.f;
+  }
+  __syncthreads();
+  // rotated, scaled queries: row h < G = hi part of head h, row 8 + h = lo part;
+  // thread (c, hq) forms coordinate c of heads hq and hq + 4
+  {
+    const int c = threadIdx.x & 63, hq = threadIdx.x >> 6;
+    const float4* prow = reinterpret_cast<const float4*>(pi32 + c * D);
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll 4
+    for (int i4 = 0; i4 < D / 4; ++i4) {
+      const float4 p = prow[i4];
+      const float4 x0 = *reinterpret_cast<const float4*>(sQf + hq * D + 4 * i4);
+      const float4 x1 = *reinterpret_cast<const float4*>(sQf + (hq + 4) * D + 4 * i4);
+      a0 = fmaf(p.x, x0.x, fmaf(p.y, x0.y, fmaf(p.z, x0.z, fmaf(p.w, x0.w, a0))));
+      a1 = fmaf(p.x, x1.x, fmaf(p.y, x1.y, fmaf(p.z, x1.z, fmaf(p.w, x1.w, a1))));
+    }
+    a0 *= scale * 1.4426950408889634f;   // scores in log2 units
+    a1 *= scale * 1.4426950408889634f;
+    const _Float16 h0 = (_Float16)a0, h1 = (_Float16)a1;
+    sQ[hq * Q_PITCH + c] = h0;
+    sQ[(hq + 4) * Q_PITCH + c] = h1;
+    sQ[(8 + hq) * Q_PITCH + c] = (_Float16)((a0 - (float)h0) * 2048.f);
+    sQ[(12 + hq) * Q_PITCH + c] = (_Float16)((a1 - (float)h1) * 2048.f);
+  }
+  __syncthreads();
+
+  const int64_t t0 = (int64_t)sw * chunk;
+  const int64_t t1 = t0 + chunk < T ? t0 + chunk : T;
+  const int64_t stream = (int64_t)b * Hkv + g;
+  constexpr int64_t WSTEP = (int64_t)ATT_WAVES * TILE;
+
+  // B operands of the score product: Qcat[col][32 s + 8 grp + e]
+  half8 qf[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+    qf[s] = *reinterpret_cast<const half8*>(sQ + col * Q_PITCH + 32 * s + 8 * grp);
+
+  float m_run = NEG_BIG, l_run = 0.f;
+  floatx4 oh[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) oh[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  auto load = [&](TileRegs<W>& t, int64_t tb) {
+    const int64_t left = t1 - tb;
+    const int cnt = left <= 0 ? 0 : (left < TILE ? (int)left : TILE);
+    const int64_t rec0 = stream * T + (left <= 0 ? 0 : tb);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint32_t*>(kc + rec0 * W), (short)0, cnt * W * 4, BUF_DWORD3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint32_t*>(vc + rec0 * W), (short)0, cnt * W * 4, BUF_DWORD3);
+    const __amdgpu_buffer_rsrc_t rkn = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(kn + rec0), (short)0, cnt * 2, BUF_DWORD3);
+    const __amdgpu_buffer_rsrc_t rvn = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(vn + rec0), (short)0, cnt * 2, BUF_DWORD3);
+    load_record<W>(t.kw, rk, (uint32_t)(lane * W * 4));
+    load_record<W>(t.vw, rv, (uint32_t)(lane * W * 4));
+    t.kn = __builtin_amdgcn_raw_buffer_load_b16(rkn, lane * 2, 0, 0);
+    t.vn = __builtin_amdgcn_raw_buffer_load_b16(rvn, lane * 2, 0, 0);
+  };
+  auto stage = [&](const TileRegs<W>& t) {
+    unpack_record<K, BITS, W>(t.kw, sKi + lane * IP);
+    unpack_record<K, BITS, W>(t.vw, sVi + lane * IP);
+    sNk[lane] = f16_bits_to_f32((uint16_t)t.kn);
+    sNv[lane] = f16_bits_to_f32((uint16_t)t.vn);
+    if constexpr (AS::EXPAND) {
+      // the lane writes its own value row (hi and lo) for the transpose reads
+      const uint16_t* vi = sVi + lane * IP;
+#pragma unroll
+      for (int c0 = 0; c0 < D; c0 += 8) {
+        half8 hh;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int c = c0 + e, j = c / K;
+          hh[e] = sVh[vi[j] * K + (c - j * K)];
+        }
+        *reinterpret_cast<half4*>(sZh + lane * Z_PITCH + c0) = half4{hh[0], hh[1], hh[2], hh[3]};
+        *reinterpret_cast<half4*>(sZh + lane * Z_PITCH + c0 + 4) = half4{hh[4], hh[5], hh[6], hh[7]};
+      }
+    }
+  };
+
+  auto process = [&](int64_t tb) {
+    const int64_t left = t1 - tb;
+    const bool partial = left < TILE;                 // uniform
+    const int valid = partial ? (int)left : TILE;
+    // ---- scores for the 4 sub-tiles of 16 tokens (lanes of columns >= G hold
+    //      unused but finite values)
+    float sc[4][4];
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) {
+      const uint16_t* ki = sKi + (16 * sub + col) * IP;
+      floatx4 ah = {0.f, 0.f, 0.f, 0.f}, al = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        half8 zh, zl;
+        gather8_hl<K>(ki, sK, sKlo, 32 * s + 8 * grp, zh, zl);
+        ah = __builtin_amdgcn_mfma_f32_16x16x32_f16(zh, qf[s], ah, 0, 0, 0);
+        al = __builtin_amdgcn_mfma_f32_16x16x32_f16(zl, qf[s], al, 0, 0, 0);
+      }
+      const float4 nk4 = *reinterpret_cast<const float4*>(sNk + 16 * sub + 4 * grp);
+      const float nk[4] = {nk4.x, nk4.y, nk4.z, nk4.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float x = fmaf(al[r], 0x1p-11f, ah[r]);
+        sc[sub][r] = fmaf(rot8(x), 0x1p-11f, x) * nk[r];
+      }
+    }
+    if (partial) {
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (16 * sub + 4 * grp + r >= valid) sc[sub][r] = NEG_BIG;
+    }
+    // ---- online softmax (lane owns head col; its group lanes share the head)
+    float mx = NEG_BIG;
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[sub][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    // rescale the accumulators only when some head's running max moved
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) oh[mt] *= alpha;
+    }
+    m_run = m_new;
+    float ps = 0.f;
+    half8 pb[2];
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) {
+      const float4 nv4 = *reinterpret_cast<const float4*>(sNv + 16 * sub + 4 * grp);
+      const float nv[4] = {nv4.x, nv4.y, nv4.z, nv4.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = __builtin_amdgcn_exp2f(sc[sub][r] - m_new);
+        ps += p;
+        pb[sub >> 1][4 * (sub & 1) + r] = (_Float16)(p * nv[r]);
+      }
+    }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    l_run += ps;
+    // ---- values: K slot (grp, e) holds token 32 ks + 4 grp + (e & 3) + 16 (e >> 2)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int tok_a = 32 * ks + 4 * grp + (col >> 2);
+      const int tok_b = tok_a + 16;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int c = 16 * mt + 4 * (col & 3);
+        const _Float16 *pa, *pbp;
+        if constexpr (AS::EXPAND) {
+          pa = sZh + tok_a * Z_PITCH + c;
+          pbp = sZh + tok_b * Z_PITCH + c;
+        } else {
+          const uint32_t ia = sVi[tok_a * IP + c / K], ib = sVi[tok_b * IP + c / K];
+          pa = sVh + ia * K + (c % K);
+          pbp = sVh + ib * K + (c % K);
+        }
+        const half4 ha = read_tr(pa), hb = read_tr(pbp);
+        const half8 zh = {ha[0], ha[1], ha[2], ha[3], hb[0], hb[1], hb[2], hb[3]};
+        oh[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(zh, pb[ks], oh[mt], 0, 0, 0);
+      }
+    }
+  };
+
+  // wave w takes tiles t0 + (w + 4 i) TILE of the workgroup's split
+  int64_t tb = t0 + (int64_t)wave * TILE;
+  if (tb < t1) {
+    TileRegs<W> ra, rb;
+    load(ra, tb);
+    load(rb, tb + WSTEP);
+    for (;;) {
+      stage(ra);
+      wave_lds_sync();
+      load(ra, tb + 2 * WSTEP);
+      process(tb);
+      wave_lds_sync();
+      tb += WSTEP;
+      if (tb >= t1) break;
+      stage(rb);
+      wave_lds_sync();
+      load(rb, tb + 2 * WSTEP);
+      process(tb);
+      wave_lds_sync();
+      tb += WSTEP;
+      if (tb >= t1) break;
+    }
+  }
+
+  // ---- merge the four waves' partials of each head in LDS, write one partial
+  if (col < G) {
+    float* mine = sMerge + (wave * MAX_G + col) * MERGE_PITCH;
+    if (grp == 0) {
+      mine[0] = m_run;
+      mine[1] = l_run;
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        mine[2 + 16 * mt + 4 * grp + r] = oh[mt][r];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < G * D; e += ATT_THREADS) {
     const int h = e / D, c = e % D;
-    const uint16_t* qr = q + ((int64_t)b * Hq + (int64_t)g * G + h) * D;
-    float a = 0.f;
-    for (int i = 0; i < D; ++i) a = fmaf(pi32[c * D + i], f16_bits_to_f32(qr[i]), a);
-    sQ[h * D + c] = a * scale;
-  }
-  __syncthreads();
-
-  const int64_t base = ((int64_t)b * Hkv + g) * T;
-  // per-head running state: wave w owns heads w, w+4, ...
-  float m_run[MAX_G / 4], l_run[MAX_G / 4];
+    float M = NEG_BIG;
 #pragma unroll
-  for (int u = 0; u < MAX_G / 4; ++u) {
-    m_run[u] = -INFINITY;
-    l_run[u] = 0.f;
-  }
-  // value accumulators: thread owns coordinate c = lane for heads wave, wave+4, ...
-  float o_acc[MAX_G / 4];
+    for (int w = 0; w < ATT_WAVES; ++w) M = fmaxf(M, sMerge[(w * MAX_G + h) * MERGE_PITCH]);
+    float Ls = 0.f, o = 0.f;
 #pragma unroll
-  for (int u = 0; u < MAX_G / 4; ++u) o_acc[u] = 0.f;
-
-  for (int64_t tt = t0; tt < t1; tt += ATT_TILE) {
-    const int64_t t = tt + lane;
-    const bool valid = t < t1;
-    // ---- scores: part `wave` covers coordinates [16 wave, 16 wave + 16)
-    {
-      float zk[16];
-      float nuk = 0.f;
-      if (valid) {
-        const uint32_t* rec = kc + (base + t) * Wk;
-        nuk = f16_bits_to_f32(kn[base + t]);
-#pragma unroll
-        for (int cc = 0; cc < 16; ++cc) {
-          const int c = wave * 16 + cc;
-          const int j = c / KK, tq = c % KK;
-          zk[cc] = sCbK[record_field(rec, j, bitsk) * KK + tq];
-        }
-      } else {
-#pragma unroll
-        for (int cc = 0; cc < 16; ++cc) zk[cc] = 0.f;
-      }
-      for (int h = 0; h < G; ++h) {
-        float a = 0.f;
-#pragma unroll
-        for (int cc = 0; cc < 16; ++cc) a = fmaf(sQ[h * D + wave * 16 + cc], zk[cc], a);
-        sPart[(wave * MAX_G + h) * ATT_TILE + lane] = a * nuk;
-      }
+    for (int w = 0; w < ATT_WAVES; ++w) {
+      const float* pw = sMerge + (w * MAX_G + h) * MERGE_PITCH;
+      const float wt = pw[1] > 0.f ? __builtin_amdgcn_exp2f(pw[0] - M) : 0.f;
+      Ls = fmaf(wt, pw[1], Ls);
+      o = fmaf(wt, pw[2 + c], o);
     }
-    __syncthreads();
-    // ---- online softmax: wave w handles heads w, w+4, ...; lane = token
-    {
-      const float nuv = valid ? f16_bits_to_f32(vn[base + t]) : 0.f;
-#pragma unroll
-      for (int u = 0; u < MAX_G / 4; ++u) {
-        const int h = wave + 4 * u;
-        if (h < G) {
-          float s = sPart[(0 * MAX_G + h) * ATT_TILE + lane] + sPart[(1 * MAX_G + h) * ATT_TILE + lane] +
-                    sPart[(2 * MAX_G + h) * ATT_TILE + lane] + sPart[(3 * MAX_G + h) * ATT_TILE + lane];
-          if (!valid) s = -INFINITY;
-          const float mt = wave_max(s);
-          const float mn = fmaxf(m_run[u], mt);
-          const float p = valid ? __expf(s - mn) : 0.f;
-          const float ps = wave_sum(p);
-          const float alpha = __expf(m_run[u] - mn);
-          l_run[u] = l_run[u] * alpha + ps;
-          m_run[u] = mn;
-          sP[h * ATT_TILE + lane] = p * nuv;
-          if (lane == 0) sAlpha[h] = alpha;
-        }
-      }
+    float* dst = ws + (((int64_t)b * Hq + (int64_t)g * G + h) * S + sw) * PART;
+    if (c == 0) {
+      dst[0] = M;
+      dst[1] = Ls;
     }
-    __syncthreads();
-    // ---- values: thread owns coordinate c = lane, heads wave, wave+4, ...
-    {
-      const int c = lane;
-      const int j = c / KV, tq = c % KV;
-#pragma unroll
-      for (int u = 0; u < MAX_G / 4; ++u) {
-        const int h = wave + 4 * u;
-        if (h < G) o_acc[u] *= sAlpha[h];
-      }
-      const int64_t nt = (t1 - tt) < ATT_TILE ? (t1 - tt) : ATT_TILE;
-      for (int e = 0; e < nt; ++e) {
-        const uint32_t* rec = vc + (base + tt + e) * Wv;
-        const float zv = sCbV[record_field(rec, j, bitsv) * KV + tq];
-#pragma unroll
-        for (int u = 0; u < MAX_G / 4; ++u) {
-          const int h = wave + 4 * u;
-          if (h < G) o_acc[u] = fmaf(sP[h * ATT_TILE + e], zv, o_acc[u]);
-        }
-      }
-    }
-    __syncthreads();
-  }
-  // ---- write partials
-#pragma unroll
-  for (int u = 0; u < MAX_G / 4; ++u) {
-    const int h = wave + 4 * u;
-    if (h < G) {
-      float* dst = ws + (((int64_t)b * Hq + (int64_t)g * G + h) * S + split) * PART;
-      if (lane == 0) {
-        dst[0] = m_run[u];
-        dst[1] = l_run[u];
-      }
-      dst[2 + lane] = o_acc[u];
-    }
+    dst[2 + c] = o;
   }
 }
 
-__global__ __launch_bounds__(64) void attend_merge_kernel(const float* __restrict__ ws, int S,
-                                                          int Hq, const float* __restrict__ pi32,
-                                                          uint16_t* __restrict__ out) {
-  const int h = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
+// One workgroup per (batch, query head): log-sum-exp merge of the S split
+// partials, then out = Pi^T o_rot in binary16.
+__global__ __launch_bounds__(256) void attend_merge_kernel(const float* __restrict__ ws, int S,
+                                                           int Hq, const float* __restrict__ pi32,
+                                                           uint16_t* __restrict__ out) {
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const float* src = ws + ((int64_t)b * Hq + h) * S * PART;
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, src[s * PART]);
-  float L = 0.f, o = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float w = __expf(src[s * PART] - M);
-    L = fmaf(w, src[s * PART + 1], L);
-    o = fmaf(w, src[s * PART + 2 + c], o);
-  }
-  __shared__ float sO[D];
-  sO[c] = o / L;
+  __shared__ float sRed[256];
+  __shared__ float sO[4][D];
+  __shared__ float sL[4];
+  float M = NEG_BIG;
+  for (int s = tid; s < S; s += 256) M = fmaxf(M, src[(int64_t)s * PART]);
+  sRed[tid] = M;
   __syncthreads();
-  // out = Pi^T o_rot: out[c] = sum_j Pi[j][c] o_rot[j]
-  float a = 0.f;
-  for (int j = 0; j < D; ++j) a = fmaf(pi32[j * D + c], sO[j], a);
-  out[((int64_t)b * Hq + h) * D + c] = f32_to_f16_rne(a);
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) sRed[tid] = fmaxf(sRed[tid], sRed[tid + w]);
+    __syncthreads();
+  }
+  M = sRed[0];
+  const int c = tid & 63, part = tid >> 6;
+  float o = 0.f, Ls = 0.f;
+  for (int s = part; s < S; s += 4) {
+    const float* p = src + (int64_t)s * PART;
+    const float wt = __builtin_amdgcn_exp2f(p[0] - M);   // partials are in log2 units
+    Ls = fmaf(wt, p[1], Ls);
+    o = fmaf(wt, p[2 + c], o);
+  }
+  sO[part][c] = o;
+  if (c == 0) sL[part] = Ls;
+  __syncthreads();
+  if (tid < D) {
+    const float Lt = sL[0] + sL[1] + sL[2] + sL[3];
+    sRed[tid] = (sO[0][tid] + sO[1][tid] + sO[2][tid] + sO[3][tid]) / Lt;
+  }
+  __syncthreads();
+  if (tid < D) {
+    float a = 0.f;
+    for (int j = 0; j < D; ++j) a = fmaf(pi32[j * D + tid], sRed[j], a);
+    out[((int64_t)b * Hq + h) * D + tid] = f32_to_f16_rne(a);
+  }
 }
 
-template <int KK, int KV>
-hipError_t launch_ref(const fq_codebook* ck, const fq_codebook* cv, const uint16_t* q,
-                      const uint32_t* kc, const uint16_t* kn, const uint32_t* vc,
-                      const uint16_t* vn, int B, int Hq, int Hkv, int64_t T, float scale,
-                      float* ws, uint16_t* out, hipStream_t s) {
+template <int K, int BITS>
+size_t attend_lds_bytes(int N) {
+  return AttLds<K, BITS>::total(N);
+}
+
+template <int K, int BITS>
+hipError_t launch_v(const fq_codebook* ck, const fq_codebook* cv, const uint16_t* q,
+                    const uint32_t* kc, const uint16_t* kn, const uint32_t* vc,
+                    const uint16_t* vn, int B, int Hq, int Hkv, int64_t T, float scale,
+                    float* ws, uint16_t* out, hipStream_t s) {
   const SplitPlan p = plan_splits(B, Hkv, T);
-  const size_t shm = sizeof(float) * (MAX_G * D + 4 * MAX_G * ATT_TILE + MAX_G * ATT_TILE +
-                                      MAX_G + ck->N * KK + cv->N * KV);
-  auto kern = attend_split_ref_kernel<KK, KV>;
+  const size_t shm = attend_lds_bytes<K, BITS>(ck->N);
+  auto kern = attend_split_kernel<K, BITS>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(p.S, Hkv, B), dim3(ATT_THREADS), shm, s, q, kc, kn, vc, vn, Hq,
-                     Hkv, T, p.chunk, scale, ck->t.pi32, ck->t.cb32, ck->N, ck->bits, ck->W,
-                     cv->t.cb32, cv->N, cv->bits, cv->W, ws, p.S);
+  hipLaunchKernelGGL(kern, dim3((unsigned)p.S, Hkv, B), dim3(ATT_THREADS), shm, s, q, kc, kn, vc, vn, Hq,
+                     Hkv, T, p.chunk, p.S, scale, ck->t.pi32, ck->t.cb16hi, ck->t.cb16lo,
+                     cv->t.cb16hi, ck->N, ws);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attend_merge_kernel, dim3(Hq, B), dim3(64), 0, s, ws, p.S, Hq, ck->t.pi32,
+  hipLaunchKernelGGL(attend_merge_kernel, dim3(Hq, B), dim3(256), 0, s, ws, p.S, Hq, ck->t.pi32,
                      out);
   return hipGetLastError();
 }
 
-template <int KK>
-hipError_t dispatch_v(const fq_codebook* ck, const fq_codebook* cv, const uint16_t* q,
-                      const uint32_t* kc, const uint16_t* kn, const uint32_t* vc,
-                      const uint16_t* vn, int B, int Hq, int Hkv, int64_t T, float scale,
-                      float* ws, uint16_t* out, hipStream_t s) {
-  switch (cv->k) {
-    case 2: return launch_ref<KK, 2>(ck, cv, q, kc, kn, vc, vn, B, Hq, Hkv, T, scale, ws, out, s);
-    case 3: return launch_ref<KK, 3>(ck, cv, q, kc, kn, vc, vn, B, Hq, Hkv, T, scale, ws, out, s);
-    case 4: return launch_ref<KK, 4>(ck, cv, q, kc, kn, vc, vn, B, Hq, Hkv, T, scale, ws, out, s);
-    case 8: return launch_ref<KK, 8>(ck, cv, q, kc, kn, vc, vn, B, Hq, Hkv, T, scale, ws, out, s);
-  }
-  return hipErrorInvalidValue;
-}
-
 }  // namespace
+
+bool attend_supported(const fq_codebook* cb) {
+#define FQ_ATS(KK, BB) \
+  if (cb->k == KK && cb->bits == BB) return attend_lds_bytes<KK, BB>(cb->N) <= 160 * 1024;
+  FQ_VARIANTS(FQ_ATS)
+#undef FQ_ATS
+  return false;
+}
 
 size_t attend_workspace_bytes(const fq_codebook* /*cb_k*/, int B, int Hq, int Hkv, int64_t T) {
   const SplitPlan p = plan_splits(B, Hkv, T);
@@ -240,12 +516,11 @@ hipError_t launch_attend(const fq_codebook* ck, const fq_codebook* cv, const uin
                          const uint16_t* vn, int B, int Hq, int Hkv, int64_t T, float scale,
                          void* ws, uint16_t* out, hipStream_t s) {
   float* w = static_cast<float*>(ws);
-  switch (ck->k) {
-    case 2: return dispatch_v<2>(ck, cv, q, kc, kn, vc, vn, B, Hq, Hkv, T, scale, w, out, s);
-    case 3: return dispatch_v<3>(ck, cv, q, kc, kn, vc, vn, B, Hq, Hkv, T, scale, w, out, s);
-    case 4: return dispatch_v<4>(ck, cv, q, kc, kn, vc, vn, B, Hq, Hkv, T, scale, w, out, s);
-    case 8: return dispatch_v<8>(ck, cv, q, kc, kn, vc, vn, B, Hq, Hkv, T, scale, w, out, s);
-  }
+#define FQ_ATT(KK, BB)                                                                           \
+  if (ck->k == KK && ck->bits == BB)                                                             \
+    return launch_v<KK, BB>(ck, cv, q, kc, kn, vc, vn, B, Hq, Hkv, T, scale, w, out, s);
+  FQ_VARIANTS(FQ_ATT)
+#undef FQ_ATT
   return hipErrorInvalidValue;
 }
 

@@ -6,6 +6,73 @@
 
 namespace fq {
 
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BUF_DWORD3 = 0x00020000;   // raw buffer descriptor word 3 (gfx9 family)
+
+// Compile-time record shape of a (k, index bits) variant for d = 64.
+template <int K, int BITS>
+struct Shape {
+  static constexpr int NB = (64 + K - 1) / K;                 // blocks per vector
+  static constexpr int W = (NB * BITS + 31) / 32;             // record words
+  static constexpr int IDX_PITCH = (NB + 7) / 8 * 8 + 4;      // u16 per staged index row
+};
+
+// W words at byte offset `off` of a buffer, with the widest loads the record
+// alignment allows (records of 1, 2, 4 or 8 words sit on their own size).
+template <int W>
+__device__ inline void load_record(uint32_t (&w)[W], __amdgpu_buffer_rsrc_t rc, uint32_t off) {
+  if constexpr (W == 4 || W == 8) {
+#pragma unroll
+    for (int q = 0; q < W / 4; ++q) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, off + 16 * q, 0, 0);
+      w[4 * q] = v.x;
+      w[4 * q + 1] = v.y;
+      w[4 * q + 2] = v.z;
+      w[4 * q + 3] = v.w;
+    }
+  } else if constexpr (W == 2) {
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rc, off, 0, 0);
+    w[0] = v.x;
+    w[1] = v.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < W; ++i) w[i] = __builtin_amdgcn_raw_buffer_load_b32(rc, off + 4 * i, 0, 0);
+  }
+}
+
+// Unpack one record into 16-bit indices at dst[0 .. NB) (static shifts).
+template <int K, int BITS, int W>
+__device__ inline void unpack_record(const uint32_t (&w)[W], uint16_t* dst) {
+  constexpr int NB = Shape<K, BITS>::NB;
+  constexpr uint32_t MASK = (1u << BITS) - 1u;
+  uint32_t f[NB + 1];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int pos = j * BITS, wi = pos >> 5, o = pos & 31;
+    uint32_t v = w[wi] >> o;
+    if (o + BITS > 32) v |= w[wi + 1] << (32 - o);
+    f[j] = v & MASK;
+  }
+  f[NB] = 0u;
+  uint32_t* d32 = reinterpret_cast<uint32_t*>(dst);
+  if constexpr (BITS == 8 && NB % 4 == 0) {
+    // byte fields: one byte permute per pair of indices
+#pragma unroll
+    for (int i = 0; i < NB / 4; ++i) {
+      d32[2 * i] = __builtin_amdgcn_perm(0u, w[i], 0x0c010c00u);
+      d32[2 * i + 1] = __builtin_amdgcn_perm(0u, w[i], 0x0c030c02u);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NB; j += 2) d32[j >> 1] = f[j] | (f[j + 1] << 16);
+  }
+}
+
 // binary16 bit pattern -> float
 __device__ inline float f16_bits_to_f32(uint16_t b) {
   _Float16 h;

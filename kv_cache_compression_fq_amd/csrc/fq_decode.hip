@@ -28,23 +28,11 @@
 namespace fq {
 namespace {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 constexpr int DEC_WAVES = 4;
 constexpr int DEC_THREADS = 64 * DEC_WAVES;
 constexpr int TILE = 16;           // vectors per MFMA tile
 constexpr int CHUNK = 64;          // vectors per wave iteration (one lane per record)
 constexpr int OUT_PITCH = D + 8;   // LDS row (elements) of the transpose buffer
-constexpr int BUF_DWORD3 = 0x00020000;   // raw buffer descriptor word 3 (gfx9 family)
-
-template <int K, int BITS>
-struct Shape {
-  static constexpr int NB = (D + K - 1) / K;                  // blocks per vector
-  static constexpr int W = (NB * BITS + 31) / 32;             // record words
-  static constexpr int IDX_PITCH = (NB + 7) / 8 * 8 + 4;      // u16 per staged vector
-};
 
 template <int K, int BITS, typename TY>
 constexpr size_t wave_lds() {
@@ -56,30 +44,6 @@ struct ChunkRegs {
   uint32_t w[W];
   uint32_t nu_bits;  // raw binary16 norm, converted only when staged
 };
-
-// The W words of one record at byte offset `off`, with the widest loads its
-// alignment allows (records of 1, 2, 4 or 8 words sit on their own size).
-template <int W>
-__device__ inline void load_words(ChunkRegs<W>& t, __amdgpu_buffer_rsrc_t rc, uint32_t off) {
-  if constexpr (W == 4 || W == 8) {
-#pragma unroll
-    for (int q = 0; q < W / 4; ++q) {
-      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, off + 16 * q, 0, 0);
-      t.w[4 * q] = v.x;
-      t.w[4 * q + 1] = v.y;
-      t.w[4 * q + 2] = v.z;
-      t.w[4 * q + 3] = v.w;
-    }
-  } else if constexpr (W == 2) {
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rc, off, 0, 0);
-    t.w[0] = v.x;
-    t.w[1] = v.y;
-  } else {
-#pragma unroll
-    for (int w = 0; w < W; ++w) t.w[w] = __builtin_amdgcn_raw_buffer_load_b32(rc, off + 4 * w, 0, 0);
-  }
-}
 
 // Record v of a chunk into lane v's registers.  Non-gathered: a descriptor over
 // the chunk's own records, so lanes past the end read 0 (hardware range check).
@@ -93,7 +57,7 @@ __device__ inline void load_chunk(ChunkRegs<W>& t, int64_t chunk, int lane, cons
       const_cast<uint32_t*>(codes + base * W), (short)0, cnt * W * 4, BUF_DWORD3);
   const __amdgpu_buffer_rsrc_t rn = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(norms + base), (short)0, cnt * 2, BUF_DWORD3);
-  load_words<W>(t, rc, (uint32_t)(lane * W * 4));
+  load_record<W>(t.w, rc, (uint32_t)(lane * W * 4));
   t.nu_bits = __builtin_amdgcn_raw_buffer_load_b16(rn, lane * 2, 0, 0);
 }
 
@@ -113,27 +77,8 @@ __device__ inline void load_chunk_gather(ChunkRegs<W>& t, int64_t chunk, int lan
       const_cast<uint16_t*>(norms), (short)0, (int)(n_records * 2), BUF_DWORD3);
   const uint32_t off = ok ? (uint32_t)(rec * W) * 4u : 0x80000000u;
   const uint32_t offn = ok ? (uint32_t)rec * 2u : 0x80000000u;
-  load_words<W>(t, rc, off);
+  load_record<W>(t.w, rc, off);
   t.nu_bits = __builtin_amdgcn_raw_buffer_load_b16(rn, offn, 0, 0);
-}
-
-// Unpack the lane's record into 16-bit indices at sIdx[0 .. NB) (static shifts).
-template <int K, int BITS, int W>
-__device__ inline void unpack_to_lds(const ChunkRegs<W>& t, uint16_t* sIdx) {
-  constexpr int NB = Shape<K, BITS>::NB;
-  constexpr uint32_t MASK = (1u << BITS) - 1u;
-  uint32_t f[NB + 1];
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const int pos = j * BITS, w = pos >> 5, o = pos & 31;
-    uint32_t v = t.w[w] >> o;
-    if (o + BITS > 32) v |= t.w[w + 1] << (32 - o);
-    f[j] = v & MASK;
-  }
-  f[NB] = 0u;
-  uint32_t* dst = reinterpret_cast<uint32_t*>(sIdx);
-#pragma unroll
-  for (int j = 0; j < NB; j += 2) dst[j >> 1] = f[j] | (f[j + 1] << 16);
 }
 
 // Coordinates [c0, c0 + 8) of z_hat (binary16) for one staged vector.
@@ -219,7 +164,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
       load_chunk<W>(t, c, lane, codes, norms, n);
   };
   auto stage = [&](const ChunkRegs<W>& t) {
-    unpack_to_lds<K, BITS, W>(t, sIdx + lane * Sh::IDX_PITCH);
+    unpack_record<K, BITS, W>(t.w, sIdx + lane * Sh::IDX_PITCH);
     sNu[lane] = f16_bits_to_f32((uint16_t)t.nu_bits);
   };
   auto decode_chunk = [&](int64_t base) {

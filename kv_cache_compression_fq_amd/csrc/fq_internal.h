@@ -67,6 +67,7 @@ hipError_t launch_encode(const fq_codebook* cb, const void* x, fq_dtype xt, int6
 hipError_t launch_decode(const fq_codebook* cb, const uint32_t* codes, const uint16_t* norms,
                          const int64_t* rows, int64_t n_records, int64_t n, void* y,
                          fq_dtype yt, int64_t ld, hipStream_t s);
+bool attend_supported(const fq_codebook* cb);  // the codebooks fit the kernel's LDS
 size_t attend_workspace_bytes(const fq_codebook* cb_k, int B, int Hq, int Hkv, int64_t T);
 hipError_t launch_attend(const fq_codebook* ck, const fq_codebook* cv, const uint16_t* q,
                          const uint32_t* kc, const uint16_t* kn, const uint32_t* vc,

@@ -169,33 +169,86 @@ def test_random_access_decode(dev):
 
 # ---------------------------------------------------------------- attention
 ATT_CASES = [
-    # (B, Hq, Hkv, T, K codebook, V codebook)
-    (1, 4, 1, 1, (4, 256), (4, 256)),
-    (2, 8, 1, 300, (4, 256), (4, 256)),
-    (2, 32, 4, 1000, (4, 256), (2, 16)),
-    (1, 16, 1, 777, (3, 512), (8, 256)),
-    (2, 12, 12, 1024, (2, 64), (2, 64)),
-    (1, 8, 8, 4099, (8, 16), (4, 4)),
+    # (B, Hq, Hkv, T, codebook shared by K and V)
+    (1, 4, 1, 1, (4, 256)),
+    (2, 8, 1, 300, (4, 256)),
+    (2, 32, 4, 1000, (2, 16)),
+    (1, 8, 1, 777, (3, 512)),
+    (2, 12, 12, 1024, (2, 64)),
+    (1, 8, 8, 4099, (8, 16)),
+    (1, 16, 2, 2049, (8, 256)),
+    (2, 6, 3, 100, (4, 4)),
+    (1, 8, 1, 64, (2, 256)),
 ]
 
 
-@pytest.mark.parametrize("case", ATT_CASES, ids=lambda c: f"B{c[0]}Hq{c[1]}Hkv{c[2]}T{c[3]}")
+def run_attention(dev, q, kw, kn, vw, vn, ck, cv, scale=0.125):
+    o = fq.fq_attend_decode(ck, cv, to_dev(q, dev), to_dev(kw, dev, np.int32),
+                            to_dev(kn, dev, np.int16), to_dev(vw, dev, np.int32),
+                            to_dev(vn, dev, np.int16), scale)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("case", ATT_CASES, ids=lambda c: f"B{c[0]}Hq{c[1]}Hkv{c[2]}T{c[3]}k{c[4][0]}N{c[4][1]}")
 def test_attention(dev, case):
-    B, Hq, Hkv, T, kb, vb = case
-    ak, ck = book(*kb)
-    av, cv = book(*vb)
+    B, Hq, Hkv, T, kb = case
+    art, cb = book(*kb)
     seed = B * 1000 + T
-    kw = synth.random_records((B, Hkv, T), ck.W, ck.nb * ck.info["idx_bits"], seed)
-    vw = synth.random_records((B, Hkv, T), cv.W, cv.nb * cv.info["idx_bits"], seed + 1)
+    bits = cb.nb * cb.info["idx_bits"]
+    kw = synth.random_records((B, Hkv, T), cb.W, bits, seed)
+    vw = synth.random_records((B, Hkv, T), cb.W, bits, seed + 1)
     kn = synth.random_norms((B, Hkv, T), seed + 2)
     vn = synth.random_norms((B, Hkv, T), seed + 3)
     q = synth.query(B, Hq, seed=seed + 4)
-    o = fq.fq_attend_decode(ck, cv, to_dev(q, dev), to_dev(kw, dev, np.int32),
-                            to_dev(kn, dev, np.int16), to_dev(vw, dev, np.int32),
-                            to_dev(vn, dev, np.int16), 0.125)
-    torch.cuda.synchronize()
-    ref = attend.attend(q, kw, kn, vw, vn, ak["Pi"], ak["C"], av["C"], 0.125)
-    got = o.float().cpu().numpy().astype(np.float64)
+    got = run_attention(dev, q, kw, kn, vw, vn, cb, cb)
+    ref = attend.attend(q, kw, kn, vw, vn, art["Pi"], art["C"], art["C"], 0.125)
     rel = np.linalg.norm(got - ref, axis=-1) / np.linalg.norm(ref, axis=-1)
     print(f"{case}: max rel {np.max(rel):.2e}")
     assert np.max(rel) <= 2e-3
+
+
+def test_attention_rejects_unsupported(dev):
+    _, c4 = book(4, 256)
+    _, c2 = book(2, 16)
+    q = torch.zeros((1, 16, 64), dtype=torch.float16, device=dev)
+    kw = torch.zeros((1, 1, 8, c4.W), dtype=torch.int32, device=dev)
+    nn = torch.zeros((1, 1, 8), dtype=torch.int16, device=dev)
+    with pytest.raises(fq.FQError) as e:            # 16 query heads per KV head
+        fq.fq_attend_decode(c4, c4, q, kw, nn, kw, nn, 0.125)
+    assert e.value.status == fq.FQ_ERR_UNSUPPORTED
+    with pytest.raises((fq.FQError, ValueError)):   # K and V codebooks of different variants
+        fq.fq_attend_decode(c4, c2, q[:, :8], kw, nn, kw, nn, 0.125)
+
+
+def test_attention_tinyllama_sampled(dev):
+    """Decode step at batch 16, 32 query / 4 KV heads, 32768 tokens, k4N256.
+
+    Sampled (batch, KV head) streams carry oracle-encoded synthetic keys and
+    values (per-channel log-uniform scales, 1% x20 outlier channels); the rest
+    carry uniform random records.  Checked row by row on the sampled streams.
+    """
+    B, Hq, Hkv, T = 16, 32, 4, 32768
+    art, cb = book(4, 256)
+    bits = cb.nb * cb.info["idx_bits"]
+    kw = synth.random_records((B, Hkv, T), cb.W, bits, 51)
+    vw = synth.random_records((B, Hkv, T), cb.W, bits, 52)
+    kn = synth.random_norms((B, Hkv, T), 53)
+    vn = synth.random_norms((B, Hkv, T), 54)
+    sampled = [(0, 0), (7, 2), (15, 3)]
+    for (b, g) in sampled:
+        for kv, (w_, n_) in enumerate(((kw, kn), (vw, vn))):
+            x = synth.kv_stream(3, b, kv, g, (T,))
+            idx, nb = codec.encode(x, art["Pi"], art["C"])
+            w_[b, g] = codec.pack(idx, art["bits"])
+            n_[b, g] = nb
+    q = synth.query(B, Hq, seed=5)
+    got = run_attention(dev, q, kw, kn, vw, vn, cb, cb)
+    rows = [(b, h) for (b, g) in sampled for h in range(8 * g, 8 * g + 8)]
+    ref = attend.attend(q, kw, kn, vw, vn, art["Pi"], art["C"], art["C"], 0.125, rows=rows)
+    worst = 0.0
+    for (b, h), o in ref.items():
+        rel = np.linalg.norm(got[b, h] - o) / np.linalg.norm(o)
+        worst = max(worst, rel)
+    print(f"tinyllama sampled rows: max rel {worst:.2e}")
+    assert worst <= 2e-3
