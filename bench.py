@@ -35,6 +35,7 @@ VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12     # non-packed lane-ops/s: 39.3 T
 VARIANTS = [(2, 16), (2, 64), (2, 256), (3, 512)]
 L, B, H, T = 12, 4, 12, 1024
 N_RAND = 1 << 20
+COPY_BYTES = 1 << 28
 
 
 def log(msg):
@@ -109,7 +110,10 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=8192)
+    ap.add_argument("--cpu-sample", type=int, default=16384)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 256 MiB device copy three times, so that a "
+                         "counter run can scale FETCH_SIZE / WRITE_SIZE by a known size")
     ap.add_argument("--attend-layers", type=int, default=22)
     ap.add_argument("--attend-steps", type=int, default=10)
     a = ap.parse_args()
@@ -146,6 +150,15 @@ def main():
     ws = torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device=dev)
     att_out = torch.empty((B, H, 64), dtype=torch.float16, device=dev)
     log(f"inputs ready: {n} vectors ({time.time() - t0:.1f} s)")
+
+    if a.copy_calibration:
+        src = torch.empty((COPY_BYTES,), dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"copy calibration: 3 copies of {COPY_BYTES} bytes")
 
     timer = Timer(torch)
 
