@@ -184,33 +184,36 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
   memcpy(cb->c.data(), cw_p, 4ull * N * k);
 
   // host-side tables
-  std::vector<float> pi32((size_t)d * d), enc((size_t)N * S, 0.f), cb32(cb->c);
-  std::vector<double> cb64((size_t)N * k);
+  std::vector<float> pi32((size_t)d * d), enc((size_t)N * S, 0.f);
   std::vector<_Float16> pih((size_t)d * d), pil((size_t)d * d), cbh((size_t)N * k),
       cbl((size_t)N * k);
+  double rho_pi = 0.0;   // largest |Pi - hi - 2^-11 lo|
   for (size_t i = 0; i < pi32.size(); ++i) {
     pi32[i] = (float)cb->pi[i];
     pih[i] = (_Float16)cb->pi[i];
     pil[i] = (_Float16)((cb->pi[i] - (double)pih[i]) * 2048.0);
+    rho_pi = fmax(rho_pi, fabs(cb->pi[i] - (double)pih[i] - (double)pil[i] / 2048.0));
   }
-  float cmax = 0, cmax_last = 0;
   for (int n = 0; n < N; ++n) {
-    double cc = 0, cl = 0;
+    double cc = 0;
     for (int t = 0; t < k; ++t) {
       const double v = cb->c[(size_t)n * k + t];
-      cb64[(size_t)n * k + t] = v;
       enc[(size_t)n * S + t] = (float)(-2.0 * v);
       cc += v * v;
-      if (t < cb->last) cl += v * v;
       cbh[(size_t)n * k + t] = (_Float16)v;
       cbl[(size_t)n * k + t] = (_Float16)((v - (double)cbh[(size_t)n * k + t]) * 2048.0);
     }
     enc[(size_t)n * S + k] = (float)cc;
-    cmax = fmaxf(cmax, (float)sqrt(cc));
-    cmax_last = fmaxf(cmax_last, (float)sqrt(cl));
   }
-  cb->cmax = cmax;
-  cb->cmax_last = cmax_last;
+  // Encode rotation error bound per coordinate of a unit vector: 130 accumulated
+  // float32 terms at 2^-23 each, relative to sum_j |Pi_ij x_j| <= |x|; the
+  // binary16 split of Pi (|x|_1 <= 8 |x|); three float32 roundings of the
+  // scaling; for float32 input the split of x adds 2^-23.
+  {
+    const double acc = 130.0 * 0x1p-23 * (1.0 + 0x1p-10);
+    cb->enc_ez16 = (float)((acc + 8.0 * rho_pi + 0x1p-22) * 1.01);
+    cb->enc_ez32 = (float)((acc + 8.0 * rho_pi + 0x1p-22 + 0x1p-23) * 1.01);
+  }
   // Pi as B fragments of v_mfma_f32_16x16x32_f16 for Y = Z Pi: fragment
   // [part][s][nt][lane][e] = part(Pi)[32 s + 8 (lane / 16) + e][16 nt + lane % 16],
   // part 0 = hi, part 1 = lo; one 16-byte load per lane per (part, s, nt).
@@ -224,6 +227,18 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
             frag[(((size_t)(part * 2 + s2) * 4 + nt) * 64 + lane) * 8 + e] =
                 part == 0 ? pih[src] : pil[src];
           }
+  // Pi as A fragments of v_mfma_f32_16x16x32_f16 for z = Pi x (encode):
+  // [part][ot][ks][lane][e] = part(Pi)[16 ot + lane % 16][32 ks + 8 (lane / 16) + e].
+  std::vector<_Float16> efrag(2 * 4 * 2 * 64 * 8);
+  for (int part = 0; part < 2; ++part)
+    for (int ot = 0; ot < 4; ++ot)
+      for (int ks = 0; ks < 2; ++ks)
+        for (int lane = 0; lane < 64; ++lane)
+          for (int e = 0; e < 8; ++e) {
+            const size_t src = (size_t)(16 * ot + lane % 16) * d + 32 * ks + 8 * (lane / 16) + e;
+            efrag[(((size_t)(part * 4 + ot) * 2 + ks) * 64 + lane) * 8 + e] =
+                part == 0 ? pih[src] : pil[src];
+          }
 
   // one device allocation, 256-byte aligned sub-buffers
   size_t off = 0;
@@ -233,10 +248,9 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
     return o;
   };
   const size_t o_pi64 = take(8ull * d * d), o_pi32 = take(4ull * d * d),
-               o_cb64 = take(8ull * N * k), o_enc = take(4ull * N * S),
-               o_cb32 = take(4ull * N * k), o_pih = take(2ull * d * d),
-               o_pil = take(2ull * d * d), o_cbh = take(2ull * N * k),
-               o_cbl = take(2ull * N * k), o_frag = take(2ull * frag.size());
+               o_enc = take(4ull * N * S), o_cbh = take(2ull * N * k),
+               o_cbl = take(2ull * N * k), o_frag = take(2ull * frag.size()),
+               o_efrag = take(2ull * efrag.size());
   cb->dev_bytes = off;
   {
     DeviceGuard g(device);
@@ -252,25 +266,19 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
     char* base = static_cast<char*>(cb->dev_block);
     cb->t.pi64 = reinterpret_cast<double*>(base + o_pi64);
     cb->t.pi32 = reinterpret_cast<float*>(base + o_pi32);
-    cb->t.cb64 = reinterpret_cast<double*>(base + o_cb64);
     cb->t.enc = reinterpret_cast<float*>(base + o_enc);
-    cb->t.cb32 = reinterpret_cast<float*>(base + o_cb32);
-    cb->t.pi16hi = reinterpret_cast<_Float16*>(base + o_pih);
-    cb->t.pi16lo = reinterpret_cast<_Float16*>(base + o_pil);
     cb->t.cb16hi = reinterpret_cast<_Float16*>(base + o_cbh);
     cb->t.cb16lo = reinterpret_cast<_Float16*>(base + o_cbl);
     cb->t.pifrag = reinterpret_cast<_Float16*>(base + o_frag);
+    cb->t.encfrag = reinterpret_cast<_Float16*>(base + o_efrag);
     std::vector<char> staging(off, 0);
     memcpy(staging.data() + o_pi64, cb->pi.data(), 8ull * d * d);
     memcpy(staging.data() + o_pi32, pi32.data(), 4ull * d * d);
-    memcpy(staging.data() + o_cb64, cb64.data(), 8ull * N * k);
     memcpy(staging.data() + o_enc, enc.data(), 4ull * N * S);
-    memcpy(staging.data() + o_cb32, cb32.data(), 4ull * N * k);
-    memcpy(staging.data() + o_pih, pih.data(), 2ull * d * d);
-    memcpy(staging.data() + o_pil, pil.data(), 2ull * d * d);
     memcpy(staging.data() + o_cbh, cbh.data(), 2ull * N * k);
     memcpy(staging.data() + o_cbl, cbl.data(), 2ull * N * k);
     memcpy(staging.data() + o_frag, frag.data(), 2ull * frag.size());
+    memcpy(staging.data() + o_efrag, efrag.data(), 2ull * efrag.size());
     if (hipMemcpy(cb->dev_block, staging.data(), off, hipMemcpyHostToDevice) != hipSuccess) {
       (void)hipGetLastError();
       (void)hipFree(cb->dev_block);

@@ -29,16 +29,13 @@ inline bool variant_supported(int k, int bits) {
 
 // Per-codebook device tables, all inside one allocation.
 struct DeviceTables {
-  double* pi64;     // [64][64] Pi, row-major (z = Pi u)
-  float* pi32;      // [64][64] Pi rounded to float32
-  double* cb64;     // [N][k]  codewords (exact float32 values) as float64
-  float* enc;       // [N][S]  search table: -2 c_0 .. -2 c_{k-1}, |c|^2, zero pad; S = enc_stride
-  float* cb32;      // [N][k]  codewords
-  _Float16* pi16hi; // [64][64] Pi rounded to binary16
-  _Float16* pi16lo; // [64][64] (Pi - hi) * 2^11 rounded to binary16
-  _Float16* cb16hi; // [N][k]   codewords rounded to binary16
-  _Float16* cb16lo; // [N][k]   (c - hi) * 2^11 rounded to binary16
-  _Float16* pifrag; // Pi as v_mfma_f32_16x16x32_f16 B fragments, see fq_api.hip
+  double* pi64;      // [64][64] Pi, row-major (z = Pi u)
+  float* pi32;       // [64][64] Pi rounded to float32
+  float* enc;        // [N][S]  search table: -2 c_0 .. -2 c_{k-1}, |c|^2, zero pad; S = enc_stride
+  _Float16* cb16hi;  // [N][k]   codewords rounded to binary16
+  _Float16* cb16lo;  // [N][k]   (c - hi) * 2^11 rounded to binary16
+  _Float16* pifrag;  // Pi as v_mfma_f32_16x16x32_f16 B fragments (decode), see fq_api.hip
+  _Float16* encfrag; // Pi hi / lo as v_mfma_f32_16x16x32_f16 A fragments (encode)
 };
 
 }  // namespace fq
@@ -49,8 +46,8 @@ struct fq_codebook {
   int enc_stride;
   double rate_nominal, rate_actual, distortion;
   uint64_t hash;
-  float cmax;       // max codeword norm (float32 table)
-  float cmax_last;  // max norm of the first `last` coordinates of a codeword
+  float enc_ez16;   // encode: bound on |z~ - z| per coordinate, binary16 input
+  float enc_ez32;   // the same for float32 input
   std::vector<double> pi;  // host copy of Pi
   std::vector<float> c;    // host copy of C
   void* dev_block;         // the single device allocation
