@@ -205,12 +205,15 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
     }
     enc[(size_t)n * S + k] = (float)cc;
   }
-  // Encode rotation error bound per coordinate of a unit vector: 130 accumulated
-  // float32 terms at 2^-23 each, relative to sum_j |Pi_ij x_j| <= |x|; the
-  // binary16 split of Pi (|x|_1 <= 8 |x|); three float32 roundings of the
-  // scaling; for float32 input the split of x adds 2^-23.
+  // Encode rotation error bound per coordinate of a unit vector.  Each output
+  // is a float32 sum of four 16-product groups (each accumulated from zero,
+  // at most 15 roundings) for the hi part and four for the lo part (scaled by
+  // 2^-11), then one fused multiply-add and one product: at most 20 roundings
+  // of 2^-23 relative to sum_j |Pi_ij x_j| <= |x|, plus the binary16 split of
+  // Pi (|x|_1 <= 8 |x|) and the float32 reciprocal of the norm; for float32
+  // input the split of x adds 2^-23.
   {
-    const double acc = 130.0 * 0x1p-23 * (1.0 + 0x1p-10);
+    const double acc = 20.0 * 0x1p-23 * (1.0 + 0x1p-10) * (1.0 + 0x1p-11);
     cb->enc_ez16 = (float)((acc + 8.0 * rho_pi + 0x1p-22) * 1.01);
     cb->enc_ez32 = (float)((acc + 8.0 * rho_pi + 0x1p-22 + 0x1p-23) * 1.01);
   }
@@ -227,18 +230,32 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
             frag[(((size_t)(part * 2 + s2) * 4 + nt) * 64 + lane) * 8 + e] =
                 part == 0 ? pih[src] : pil[src];
           }
-  // Pi as A fragments of v_mfma_f32_16x16x32_f16 for z = Pi x (encode):
-  // [part][ot][ks][lane][e] = part(Pi)[16 ot + lane % 16][32 ks + 8 (lane / 16) + e].
-  std::vector<_Float16> efrag(2 * 4 * 2 * 64 * 8);
+  // Pi as A fragments of v_mfma_f32_16x16x16_f16 for z = Pi x (encode):
+  // [part][ot][kq][lane][e] = part(Pi)[16 ot + lane % 16][16 kq + 4 (lane / 16) + e].
+  std::vector<_Float16> efrag(2 * 4 * 4 * 64 * 4);
   for (int part = 0; part < 2; ++part)
     for (int ot = 0; ot < 4; ++ot)
-      for (int ks = 0; ks < 2; ++ks)
+      for (int kq = 0; kq < 4; ++kq)
         for (int lane = 0; lane < 64; ++lane)
-          for (int e = 0; e < 8; ++e) {
-            const size_t src = (size_t)(16 * ot + lane % 16) * d + 32 * ks + 8 * (lane / 16) + e;
-            efrag[(((size_t)(part * 4 + ot) * 2 + ks) * 64 + lane) * 8 + e] =
+          for (int e = 0; e < 4; ++e) {
+            const size_t src = (size_t)(16 * ot + lane % 16) * d + 16 * kq + 4 * (lane / 16) + e;
+            efrag[(((size_t)(part * 4 + ot) * 4 + kq) * 64 + lane) * 4 + e] =
                 part == 0 ? pih[src] : pil[src];
           }
+
+  // candidate grids for the block search (k = 2, 3)
+  fq::GridTable grid, grid1;
+  cb->grid_G = 0;
+  cb->grid1_G = 0;
+  if (k == 2 || k == 3) {
+    const int G = (k == 2) ? (N <= 64 ? 32 : 64) : (N <= 512 ? 32 : 64);
+    fq::build_grid(cb->c.data(), N, k, k, G, fq::GRID_R, fq::grid_record_entries(k), &grid);
+    cb->grid_G = G;
+    if (cb->last < k) {
+      fq::build_grid(cb->c.data(), N, k, 1, 4 * N, fq::GRID_R, fq::grid_record_entries(k), &grid1);
+      cb->grid1_G = 4 * N;
+    }
+  }
 
   // one device allocation, 256-byte aligned sub-buffers
   size_t off = 0;
@@ -250,7 +267,8 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
   const size_t o_pi64 = take(8ull * d * d), o_pi32 = take(4ull * d * d),
                o_enc = take(4ull * N * S), o_cbh = take(2ull * N * k),
                o_cbl = take(2ull * N * k), o_frag = take(2ull * frag.size()),
-               o_efrag = take(2ull * efrag.size());
+               o_efrag = take(2ull * efrag.size()),
+               o_grid = take(2ull * grid.rec.size() + 64), o_grid1 = take(2ull * grid1.rec.size() + 64);
   cb->dev_bytes = off;
   {
     DeviceGuard g(device);
@@ -271,6 +289,8 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
     cb->t.cb16lo = reinterpret_cast<_Float16*>(base + o_cbl);
     cb->t.pifrag = reinterpret_cast<_Float16*>(base + o_frag);
     cb->t.encfrag = reinterpret_cast<_Float16*>(base + o_efrag);
+    cb->t.grid = grid.rec.empty() ? nullptr : reinterpret_cast<uint16_t*>(base + o_grid);
+    cb->t.grid1 = grid1.rec.empty() ? nullptr : reinterpret_cast<uint16_t*>(base + o_grid1);
     std::vector<char> staging(off, 0);
     memcpy(staging.data() + o_pi64, cb->pi.data(), 8ull * d * d);
     memcpy(staging.data() + o_pi32, pi32.data(), 4ull * d * d);
@@ -279,6 +299,9 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
     memcpy(staging.data() + o_cbl, cbl.data(), 2ull * N * k);
     memcpy(staging.data() + o_frag, frag.data(), 2ull * frag.size());
     memcpy(staging.data() + o_efrag, efrag.data(), 2ull * efrag.size());
+    if (!grid.rec.empty()) memcpy(staging.data() + o_grid, grid.rec.data(), 2ull * grid.rec.size());
+    if (!grid1.rec.empty())
+      memcpy(staging.data() + o_grid1, grid1.rec.data(), 2ull * grid1.rec.size());
     if (hipMemcpy(cb->dev_block, staging.data(), off, hipMemcpyHostToDevice) != hipSuccess) {
       (void)hipGetLastError();
       (void)hipFree(cb->dev_block);

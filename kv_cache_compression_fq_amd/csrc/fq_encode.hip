@@ -6,7 +6,7 @@
 //  1. norm: nu = |x|_2 in float64 from the exact input values; the stored
 //     norm is nu rounded once to binary16.
 //  2. rotation on the matrix cores: Pi = Pi_hi + 2^-11 Pi_lo (both binary16),
-//     y = Pi_hi x + 2^-11 Pi_lo x with v_mfma_f32_16x16x32_f16 (binary16 input
+//     y = Pi_hi x + 2^-11 Pi_lo x with v_mfma_f32_16x16x16_f16 (binary16 input
 //     is exact; float32 input is scaled by a power of two and split the same
 //     way), z~ = y / nu in float32, staged in LDS.
 //  3. block search: every (vector, block) column looks for
@@ -20,16 +20,20 @@
 //     than the gap as D_n grows, so when the second-best gap exceeds their sum
 //     for the runner-up, the float32 winner is the exact argmin for the exact
 //     z and the result is final.
-//  5. otherwise (near ties, non-finite data) the block is redone exactly by
-//     the whole wave: z's block in float64 from x and the float64 Pi, then all
-//     N codewords with sum_t (z_t - c_t)^2 in float64, ties to the lowest index.
+//  5. otherwise (near ties, non-finite data, blocks outside the candidate
+//     grid) the block is redone exactly by 16 lanes: z's block in float64 from
+//     x and the float64 Pi, then all N codewords with sum_t (z_t - c_t)^2 in
+//     float64, ties to the lowest index.
 //  6. the chunk's indices are packed LSB-first into fixed-size records and
 //     written with coalesced word stores, norms beside them.
 //
-// ez covers the binary16 split of Pi (and of x), the float32 accumulation on
-// the matrix cores (taken as at most one rounding of 2^-23 relative per
-// accumulated term, 130 terms) and the final scaling; it is computed on the
-// host from the actual split residuals.
+// ez covers the binary16 split of Pi (and of x), the float32 accumulation
+// (each 16-product group summed from zero on the matrix cores, taken as at
+// most one rounding of 2^-23 relative per accumulated term, then the groups
+// added in float32) and the final scaling; it is computed on the host from the
+// actual split residuals.
+#include <type_traits>
+
 #include "fq_common.h"
 #include "fq_internal.h"
 
@@ -37,9 +41,11 @@ namespace fq {
 namespace {
 
 constexpr int EV = 16;          // vectors per wave chunk
-constexpr int ENC_WAVES = 8;    // waves per workgroup
+// waves per workgroup: 4, or 8 when the codebook table fills most of LDS
+template <int BITS>
+constexpr int enc_waves() { return BITS >= 10 ? 8 : 4; }
 constexpr int ZP = 68;          // floats per staged z row
-constexpr int ROT_BYTES = 2 * 4 * 2 * 64 * 8 * 2;   // Pi fragments, [part][ot][ks][lane][8]
+constexpr int ROT_BYTES = 2 * 4 * 4 * 64 * 4 * 2;   // Pi fragments, [part][ot][kq][lane][4]
 constexpr float SLACK = 1e-5f;  // covers |D~ - D| inside the square roots of the bound
 
 template <int K, int BITS>
@@ -66,6 +72,10 @@ struct EncArgs {
   int N;
   float ez;   // bound on |z~ - z| per coordinate of a unit vector
   float gv;   // relative rounding bound of the float32 search value
+  const uint16_t* grid;    // candidate records of the block grid (k = 2, 3)
+  const uint16_t* grid1;   // candidate records of the one-coordinate last block
+  int G, G1;               // cells per dimension
+  float gscale, g1scale;   // cells per unit length
 };
 
 __host__ __device__ inline size_t enc_table_bytes(int N, int S) {
@@ -79,30 +89,48 @@ __device__ inline double shfl_xor_f64(double v, int m) {
   return __builtin_bit_cast(double, p);
 }
 
-// x fragments of one vector (lane's vector j = lane % 16, coordinates
-// 32 ks + 8 (lane / 16) .. + 7) as binary16 hi parts (and lo parts, scaled by
-// 2^11, for float32 input), the float64 sum of squares, and for float32 input
-// the power of two the fragments were scaled by.
+// x fragments of one vector for v_mfma_f32_16x16x16_f16 (lane's vector
+// j = lane % 16, coordinates 16 kq + 4 (lane / 16) .. + 3) as binary16 hi parts
+// (and lo parts, scaled by 2^11, for float32 input), the float64 sum of
+// squares, and for float32 input the power of two the fragments were scaled by.
 template <typename TX>
 struct XFrag {
-  half8 hi[2], lo[2];
+  half4 hi[4], lo[4];
   double ss;
   float escale;   // the fragments hold x * 2^-e; escale = 2^e
 };
 
+// Raw loads of one lane's x elements (issued one chunk ahead).
 template <typename TX>
-__device__ inline void load_x(const TX* xr, int g, XFrag<TX>& f);
+struct XRaw;
+template <>
+struct XRaw<_Float16> {
+  u32x2 q[4];
+};
+template <>
+struct XRaw<float> {
+  floatx4 q[4];
+};
+
+template <typename TX>
+__device__ inline void load_raw(const TX* xr, int g, XRaw<TX>& r) {
+#pragma unroll
+  for (int kq = 0; kq < 4; ++kq)
+    r.q[kq] = *reinterpret_cast<const std::remove_reference_t<decltype(r.q[0])>*>(xr + 16 * kq + 4 * g);
+}
+
+template <typename TX>
+__device__ inline void finish_x(const XRaw<TX>& r, XFrag<TX>& f);
 
 template <>
-__device__ inline void load_x<_Float16>(const _Float16* xr, int g, XFrag<_Float16>& f) {
+__device__ inline void finish_x<_Float16>(const XRaw<_Float16>& r, XFrag<_Float16>& f) {
   double ss = 0.0;
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(xr + 32 * ks + 8 * g);
-    f.hi[ks] = __builtin_bit_cast(half8, v);
+  for (int kq = 0; kq < 4; ++kq) {
+    f.hi[kq] = __builtin_bit_cast(half4, r.q[kq]);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const double t = (double)(float)f.hi[ks][e];
+    for (int e = 0; e < 4; ++e) {
+      const double t = (double)(float)f.hi[kq][e];
       ss = fma(t, t, ss);
     }
   }
@@ -113,25 +141,16 @@ __device__ inline void load_x<_Float16>(const _Float16* xr, int g, XFrag<_Float1
 }
 
 template <>
-__device__ inline void load_x<float>(const float* xr, int g, XFrag<float>& f) {
-  float v[2][8];
+__device__ inline void finish_x<float>(const XRaw<float>& r, XFrag<float>& f) {
   double ss = 0.0;
   float mx = 0.f;
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const floatx4 a = *reinterpret_cast<const floatx4*>(xr + 32 * ks + 8 * g);
-    const floatx4 b = *reinterpret_cast<const floatx4*>(xr + 32 * ks + 8 * g + 4);
+  for (int kq = 0; kq < 4; ++kq)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      v[ks][e] = a[e];
-      v[ks][4 + e] = b[e];
+      ss = fma((double)r.q[kq][e], (double)r.q[kq][e], ss);
+      mx = fmaxf(mx, fabsf(r.q[kq][e]));
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      ss = fma((double)v[ks][e], (double)v[ks][e], ss);
-      mx = fmaxf(mx, fabsf(v[ks][e]));
-    }
-  }
   ss += shfl_xor_f64(ss, 16);
   ss += shfl_xor_f64(ss, 32);
   mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
@@ -141,13 +160,13 @@ __device__ inline void load_x<float>(const float* xr, int g, XFrag<float>& f) {
   if (mx > 0.f && mx <= 3.0e38f) (void)frexpf(mx, &e);
   const float down = ldexpf(1.f, -e);
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
+  for (int kq = 0; kq < 4; ++kq)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float s = v[ks][i] * down;
-      const _Float16 h = (_Float16)s;
-      f.hi[ks][i] = h;
-      f.lo[ks][i] = (_Float16)((s - (float)h) * 2048.f);
+    for (int i = 0; i < 4; ++i) {
+      const float sv = r.q[kq][i] * down;
+      const _Float16 h = (_Float16)sv;
+      f.hi[kq][i] = h;
+      f.lo[kq][i] = (_Float16)((sv - (float)h) * 2048.f);
     }
   f.ss = ss;
   f.escale = ldexpf(1.f, e);
@@ -168,10 +187,110 @@ __device__ inline uint32_t pack_word(const uint16_t* idx, int nb, int w) {
   return v;
 }
 
-template <int K, int BITS, typename TX>
-__global__ __launch_bounds__(ENC_WAVES * 64) void encode_kernel(EncArgs a) {
+// A column (one block of one vector) ready for the search: its coordinates,
+// squared norm, and for the grid whether it lies inside plus its cell record.
+template <int K, int RW>
+struct ColPrep {
+  float z[K];
+  float zz;
+  bool inside;
+  uint32_t rec[RW];
+};
+
+template <int K, int RW, bool GRID, bool LASTB>
+__device__ inline void prepare_column(ColPrep<K, RW>& cp, const float* zrow, bool live,
+                                      const uint16_t* grid, int G, float gscale) {
+  constexpr int KR = LASTB ? 1 : K;   // real coordinates
+  float zz = 0.f;
+#pragma unroll
+  for (int t = 0; t < K; ++t) {
+    cp.z[t] = (live && t < KR) ? zrow[t] : 0.f;
+    zz = fmaf(cp.z[t], cp.z[t], zz);
+  }
+  cp.zz = zz;
+  cp.inside = live;
+  if constexpr (GRID) {
+    int cell = 0, mul = 1;
+#pragma unroll
+    for (int t = 0; t < KR; ++t) {
+      cp.inside = cp.inside && cp.z[t] >= -(float)GRID_R && cp.z[t] < (float)GRID_R;
+      int u = (int)((cp.z[t] + (float)GRID_R) * gscale);
+      u = u < 0 ? 0 : (u >= G ? G - 1 : u);
+      cell += u * mul;
+      mul *= G;
+    }
+    const uint32_t* rp = reinterpret_cast<const uint32_t*>(grid + (size_t)cell * (2 * RW));
+#pragma unroll
+    for (int h = 0; h < RW / 4; ++h) {
+      const u32x4 r0 = *reinterpret_cast<const u32x4*>(rp + 4 * h);
+      cp.rec[4 * h] = r0.x;
+      cp.rec[4 * h + 1] = r0.y;
+      cp.rec[4 * h + 2] = r0.z;
+      cp.rec[4 * h + 3] = r0.w;
+    }
+  }
+}
+
+// Best and second-best t(n) = |c_n|^2 - 2 <z, c_n> over the cell's list (grid)
+// or the whole codebook (scan), and the gap test.  For the last block only the
+// first coordinate counts: t(n) = c_n0^2 - 2 z_0 c_n0.
+template <int K, int S, int RW, bool GRID, bool LASTB>
+__device__ inline void search_column(const ColPrep<K, RW>& cp, const float* sEnc, int N, float gv,
+                                     float ez, int& i1out, bool& certain) {
+  float m1 = INFINITY, m2 = INFINITY;
+  int i1 = 0;
+  bool listed = true;   // the search covered every possible nearest codeword
+  auto visit = [&](const float* er, int i, bool use) {
+    float t;
+    if constexpr (LASTB) {
+      t = fmaf(er[0], cp.z[0], 0.25f * er[0] * er[0]);
+    } else {
+      t = er[K];
+#pragma unroll
+      for (int tt = 0; tt < K; ++tt) t = fmaf(er[tt], cp.z[tt], t);
+    }
+    t = use ? t : INFINITY;
+    const bool p = t < m1;
+    m2 = __builtin_amdgcn_fmed3f(m1, m2, t);
+    m1 = p ? t : m1;
+    i1 = p ? i : i1;
+  };
+  if constexpr (GRID) {
+    // the cell's exact candidate list (count first, then increasing indices)
+    const uint32_t c0 = cp.rec[0] & 0xFFFFu;
+    const int cnt = (cp.inside && c0 != GRID_OVERFLOW) ? (int)c0 : 0;
+    listed = cnt > 0;
+#pragma unroll
+    for (int e = 1; e < 2 * RW; ++e) {
+      if (__builtin_amdgcn_ballot_w64(e <= cnt) == 0) break;
+      const uint32_t i = (e & 1) ? (cp.rec[e >> 1] >> 16) : (cp.rec[e >> 1] & 0xFFFFu);
+      visit(sEnc + i * S, (int)i, e <= cnt);
+    }
+  } else {
+#pragma unroll 4
+    for (int i = 0; i < N; ++i) visit(sEnc + i * S, i, true);
+  }
+  // gap test of the header, with the runner-up's terms doubled for both
+  // (m1 <= m2) and (r + 3|z|)^2 <= 2 r^2 + 18 |z|^2
+  constexpr float KSQ = LASTB ? 1.f : (K == 2 ? 1.41421356f : (K == 3 ? 1.73205081f : (K == 4 ? 2.f : 2.82842712f)));
+  const float d2 = fmaxf(m2 + cp.zz, 0.f) + SLACK;
+  // hardware square root (within 1 ulp), nudged up to stay an upper bound
+  const float rt = __builtin_amdgcn_sqrtf(d2) * 1.0001f;
+  const float thr = 2.f * gv * (2.f * d2 + 18.f * cp.zz) + 4.f * ez * KSQ * rt + 1e-12f;
+  // a single listed candidate is the nearest codeword everywhere in the cell
+  certain = listed && m1 < INFINITY && (m2 == INFINITY || (m2 - m1) > thr);
+  i1out = i1;
+}
+
+template <int K, int BITS, typename TX, bool GRID>
+__global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves_per_eu(4))) void encode_kernel(EncArgs a) {
   using Sh = EncShape<K, BITS>;
   constexpr int NB = Sh::NB, S = Sh::S, IP = Sh::IP;
+  constexpr int NBF = (Sh::LAST == K) ? NB : NB - 1;   // full blocks per vector
+  constexpr int NCF = EV * NBF;                         // full-block columns per chunk
+  constexpr int CPLF = (NCF + 63) / 64;
+  constexpr int QB = (CPLF + 1) / 2;
+  constexpr int RW = grid_record_entries(K) / 2;        // record words
   extern __shared__ __align__(16) unsigned char smem[];
   const int N = a.N;
   _Float16* sRot = reinterpret_cast<_Float16*>(smem);
@@ -191,80 +310,73 @@ __global__ __launch_bounds__(ENC_WAVES * 64) void encode_kernel(EncArgs a) {
 
   const TX* __restrict__ x = static_cast<const TX*>(a.x);
   const int64_t nchunks = (a.n + EV - 1) / EV;
-  const int64_t tw = (int64_t)gridDim.x * ENC_WAVES;
+  constexpr int WAVES = enc_waves<BITS>();
+  const int64_t tw = (int64_t)gridDim.x * WAVES;
   const int j = lane & 15, g = lane >> 4;
-  const float ez2 = 2.f * a.ez;
 
-  for (int64_t ch = (int64_t)blockIdx.x * ENC_WAVES + wave; ch < nchunks; ch += tw) {
+  // the lane's row of a chunk (rows past the end repeat the last one)
+  auto row_of = [&](int64_t chunk) {
+    const int64_t base = chunk * EV;
+    const int64_t last = a.n - 1 - base;
+    return x + (base + (j < last ? j : last)) * a.ld;
+  };
+  int64_t ch = (int64_t)blockIdx.x * WAVES + wave;
+  XRaw<TX> xraw;
+  if (ch < nchunks) load_raw<TX>(row_of(ch), g, xraw);
+  for (; ch < nchunks; ch += tw) {
     const int64_t base = ch * EV;
     const int nv = (int)((a.n - base) < EV ? (a.n - base) : EV);
-    const int jr = j < nv ? j : nv - 1;
 
-    // ---- 1. load + norm
+    // ---- 1. norm (float64) and the binary16 fragments; next chunk's x in flight
     XFrag<TX> xf;
-    load_x<TX>(x + (base + jr) * a.ld, g, xf);
+    finish_x<TX>(xraw, xf);
+    if (ch + tw < nchunks) load_raw<TX>(row_of(ch + tw), g, xraw);
     const double nu = sqrt(xf.ss);
     const uint16_t nbits = f64_to_f16_bits(nu);
-    const float inv = nu > 0.0 ? (float)((double)xf.escale / nu) : 0.f;
+    // a zero vector gets NaN coordinates: its blocks go to the exact path,
+    // which returns index 0 for them
+    const float inv = nu > 0.0 ? (float)((double)xf.escale / nu) : __builtin_nanf("");
     if (g == 0) sNu[j] = nu;
 
-    // ---- 2. rotation: lane holds z~[vector j][16 ot + 4 g + r]
+    // ---- 2. rotation: lane holds z~[vector j][16 ot + 4 g + r]; every
+    //      16-product group is accumulated from zero and the groups are summed
+    //      in float32, which keeps the rounding bound small
 #pragma unroll
     for (int ot = 0; ot < 4; ++ot) {
-      floatx4 ah = {0.f, 0.f, 0.f, 0.f}, al = {0.f, 0.f, 0.f, 0.f};
+      const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+      constexpr int NP = sizeof(TX) == 4 ? 3 : 2;
+      floatx4 pp[4][NP];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const half8 ph = *reinterpret_cast<const half8*>(sRot + (((0 * 4 + ot) * 2 + ks) * 64 + lane) * 8);
-        const half8 pl = *reinterpret_cast<const half8*>(sRot + (((1 * 4 + ot) * 2 + ks) * 64 + lane) * 8);
-        ah = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, xf.hi[ks], ah, 0, 0, 0);
-        al = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, xf.hi[ks], al, 0, 0, 0);
-        if constexpr (sizeof(TX) == 4)
-          al = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, xf.lo[ks], al, 0, 0, 0);
+      for (int kq = 0; kq < 4; ++kq) {
+        const half4 ph = *reinterpret_cast<const half4*>(sRot + (((0 * 4 + ot) * 4 + kq) * 64 + lane) * 4);
+        const half4 pl = *reinterpret_cast<const half4*>(sRot + (((1 * 4 + ot) * 4 + kq) * 64 + lane) * 4);
+        pp[kq][0] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, xf.hi[kq], zero, 0, 0, 0);
+        pp[kq][1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, xf.hi[kq], zero, 0, 0, 0);
+        if constexpr (NP == 3)
+          pp[kq][2] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, xf.lo[kq], zero, 0, 0, 0);
       }
       floatx4 zv;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) zv[r] = fmaf(al[r], 0x1p-11f, ah[r]) * inv;
+      for (int r = 0; r < 4; ++r) {
+        const float zh = (pp[0][0][r] + pp[1][0][r]) + (pp[2][0][r] + pp[3][0][r]);
+        float zl = (pp[0][1][r] + pp[1][1][r]) + (pp[2][1][r] + pp[3][1][r]);
+        if constexpr (NP == 3)
+          zl += (pp[0][2][r] + pp[1][2][r]) + (pp[2][2][r] + pp[3][2][r]);
+        zv[r] = fmaf(zl, 0x1p-11f, zh) * inv;
+      }
       *reinterpret_cast<floatx4*>(sZ + j * ZP + 16 * ot + 4 * g) = zv;
     }
     wave_lds_sync();
 
-    // ---- 3-4. search + certification, one column per lane at a time
+    // ---- 3-4. search + certification.  Full blocks first, in batches of QB
+    //      columns per lane: gather the blocks and issue their candidate
+    //      record loads, then search; the one-coordinate last block (k = 3)
+    //      gets a pass of its own.  Column ids: full c < NCF is (c / NBF,
+    //      c % NBF); c = NCF + v is vector v's last block.
     int nfb = 0;
-    for (int q = 0; q < Sh::CPL; ++q) {
-      const int c = lane + 64 * q;
-      const int v = c / NB, b = c - v * NB;
-      const bool live = c < Sh::NCOL && v < nv;
-      const bool partial = (K * (b + 1) > D);
-      float z[K];
-      float zz = 0.f;
-#pragma unroll
-      for (int t = 0; t < K; ++t) {
-        const bool real = live && (!partial || t < Sh::LAST);
-        z[t] = real ? sZ[v * ZP + K * b + t] : 0.f;
-        zz = fmaf(z[t], z[t], zz);
-      }
-      float m1 = INFINITY, m2 = INFINITY;
-      int i1 = 0;
-#pragma unroll 4
-      for (int i = 0; i < N; ++i) {
-        const float* e = sEnc + i * S;
-        float t = partial ? 0.25f * e[0] * e[0] : e[K];
-#pragma unroll
-        for (int tt = 0; tt < K; ++tt) t = fmaf(e[tt], z[tt], t);
-        const bool p = t < m1;
-        m2 = __builtin_amdgcn_fmed3f(m1, m2, t);
-        m1 = p ? t : m1;
-        i1 = p ? i : i1;
-      }
-      const float zn = sqrtf(zz);
-      const float r1 = sqrtf(fmaxf(m1 + zz, 0.f) + SLACK), r2 = sqrtf(fmaxf(m2 + zz, 0.f) + SLACK);
-      const float keff = partial ? 1.f : (float)K;
-      const float A1 = r1 + 3.f * zn, A2 = r2 + 3.f * zn;
-      const float thr = a.gv * (A1 * A1 + A2 * A2) + ez2 * sqrtf(keff) * (r1 + r2) + 1e-12f;
-      const bool zero = live && !(sNu[v] > 0.0);
-      const bool certain = (m2 - m1) > thr;
-      if (live) sIdx[v * IP + b] = (uint16_t)(zero ? 0 : i1);
-      const bool fb = live && !zero && !certain;
+    auto record = [&](int c, bool live, int v, int b, int i1, bool certain) {
+      if (live) sIdx[v * IP + b] = (uint16_t)i1;
+      const bool fb = live && !certain;
       const uint64_t m = __builtin_amdgcn_ballot_w64(fb);
       if (fb) {
         const int pos = nfb + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
@@ -272,30 +384,75 @@ __global__ __launch_bounds__(ENC_WAVES * 64) void encode_kernel(EncArgs a) {
         sFb[pos] = (uint16_t)c;
       }
       nfb += __builtin_popcountll(m);
+    };
+#pragma unroll
+    for (int qb = 0; qb < CPLF; qb += QB) {
+      ColPrep<K, RW> cp[QB];
+#pragma unroll
+      for (int q = 0; q < QB; ++q) {
+        const int c = lane + 64 * (qb + q);
+        const int v = c / NBF, b = c - v * NBF;
+        const bool live = c < NCF && v < nv;
+        prepare_column<K, RW, GRID, false>(cp[q], sZ + v * ZP + K * b, live, a.grid, a.G,
+                                           a.gscale);
+      }
+#pragma unroll
+      for (int q = 0; q < QB; ++q) {
+        const int c = lane + 64 * (qb + q);
+        const int v = c / NBF, b = c - v * NBF;
+        const bool live = c < NCF && v < nv;
+        int i1;
+        bool certain;
+        search_column<K, S, RW, GRID, false>(cp[q], sEnc, N, a.gv, a.ez, i1, certain);
+        record(c, live, v, b, i1, certain);
+      }
+    }
+    if constexpr (Sh::LAST < K) {
+      ColPrep<K, RW> cp;
+      const bool live = lane < nv;
+      const int v = lane < EV ? lane : 0;
+      prepare_column<K, RW, GRID, true>(cp, sZ + v * ZP + K * (NB - 1), live, a.grid1, a.G1,
+                                        a.g1scale);
+      int i1;
+      bool certain;
+      search_column<K, S, RW, GRID, true>(cp, sEnc, N, a.gv, a.ez, i1, certain);
+      record(NCF + v, live, v, NB - 1, i1, certain);
     }
     wave_lds_sync();
 
-    // ---- 5. exact float64 redo of uncertified columns, by the whole wave
-    for (int e = 0; e < nfb; ++e) {
-      const int c = sFb[e];
-      const int v = c / NB, b = c - v * NB;
-      const int rj = (K * (b + 1) > D) ? Sh::LAST : K;
+    // ---- 5. exact float64 redo of uncertified columns: four at a time, one
+    //      per 16-lane group (lane i of a group holds coordinates 4i .. 4i + 3)
+    for (int e0 = 0; e0 < nfb; e0 += 4) {
+      const int l16 = lane & 15;
+      const bool ok = e0 + g < nfb;
+      const int c = sFb[ok ? e0 + g : e0];
+      const bool last = c >= NCF;
+      const int v = last ? c - NCF : c / NBF, b = last ? NB - 1 : c - (c / NBF) * NBF;
+      const int rj = last ? Sh::LAST : K;
       const double nuv = sNu[v];
-      const double xj = (double)x[(base + v) * a.ld + lane];
+      const TX* xr = x + (base + v) * a.ld + 4 * l16;
+      double xq[4];
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) xq[qq] = (double)xr[qq];
+      double pr[K][4];
+#pragma unroll
+      for (int t = 0; t < K; ++t)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          pr[t][qq] = t < rj ? a.pi64[(K * b + t < D ? K * b + t : D - 1) * D + 4 * l16 + qq] : 0.0;
       double zd[K];
 #pragma unroll
       for (int t = 0; t < K; ++t) {
-        double s = 0.0;
-        if (t < rj) {
-          s = a.pi64[(K * b + t) * D + lane] * xj;
+        double sum = 0.0;
 #pragma unroll
-          for (int m = 32; m >= 1; m >>= 1) s += shfl_xor_f64(s, m);
-        }
-        zd[t] = s / nuv;
+        for (int qq = 0; qq < 4; ++qq) sum = fma(pr[t][qq], xq[qq], sum);
+#pragma unroll
+        for (int m = 8; m >= 1; m >>= 1) sum += shfl_xor_f64(sum, m);
+        zd[t] = sum / nuv;
       }
       double best = INFINITY;
       int bi = 0;
-      for (int i = lane; i < N; i += 64) {
+      for (int i = l16; i < N; i += 16) {
         const float* ee = sEnc + i * S;
         double dd = 0.0;
 #pragma unroll
@@ -310,7 +467,7 @@ __global__ __launch_bounds__(ENC_WAVES * 64) void encode_kernel(EncArgs a) {
         }
       }
 #pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) {
+      for (int m = 8; m >= 1; m >>= 1) {
         const double ob = shfl_xor_f64(best, m);
         const int oi = __shfl_xor(bi, m, 64);
         if (ob < best || (ob == best && oi < bi)) {
@@ -318,8 +475,7 @@ __global__ __launch_bounds__(ENC_WAVES * 64) void encode_kernel(EncArgs a) {
           bi = oi;
         }
       }
-      if (lane == 0) sIdx[v * IP + b] = (uint16_t)bi;
-      wave_lds_sync();
+      if (ok && l16 == 0) sIdx[v * IP + b] = (uint16_t)bi;
     }
     wave_lds_sync();
 
@@ -338,15 +494,17 @@ template <int K, int BITS, typename TX>
 hipError_t launch_k(const fq_codebook* cb, const TX* x, int64_t n, int64_t ld, uint32_t* codes,
                     uint16_t* norms, hipStream_t s) {
   using Sh = EncShape<K, BITS>;
-  const size_t shm = ROT_BYTES + enc_table_bytes(cb->N, Sh::S) + ENC_WAVES * Sh::WAVE_BYTES;
-  auto kern = encode_kernel<K, BITS, TX>;
+  constexpr int WAVES = enc_waves<BITS>();
+  const size_t shm = ROT_BYTES + enc_table_bytes(cb->N, Sh::S) + WAVES * Sh::WAVE_BYTES;
+  constexpr bool GRID = (K == 2 || K == 3);
+  auto kern = encode_kernel<K, BITS, TX, GRID>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
   static int64_t cap = 0;
-  if (cap == 0) cap = resident_blocks(reinterpret_cast<const void*>(kern), ENC_WAVES * 64, shm);
+  if (cap == 0) cap = resident_blocks(reinterpret_cast<const void*>(kern), WAVES * 64, shm);
   const int64_t chunks = (n + EV - 1) / EV;
-  int64_t blocks = (chunks + ENC_WAVES - 1) / ENC_WAVES;
+  int64_t blocks = (chunks + WAVES - 1) / WAVES;
   if (cap > 0 && blocks > cap) blocks = cap;
   EncArgs a;
   a.x = x;
@@ -360,7 +518,14 @@ hipError_t launch_k(const fq_codebook* cb, const TX* x, int64_t n, int64_t ld, u
   a.N = cb->N;
   a.ez = sizeof(TX) == 2 ? cb->enc_ez16 : cb->enc_ez32;
   a.gv = (float)((K + 2) * 0x1p-24 * 1.01);
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(ENC_WAVES * 64), shm, s, a);
+  a.grid = cb->t.grid;
+  a.grid1 = cb->t.grid1 ? cb->t.grid1 : cb->t.grid;
+  a.G = cb->grid_G;
+  a.G1 = cb->grid1_G > 0 ? cb->grid1_G : 1;
+  a.gscale = (float)(cb->grid_G / (2.0 * GRID_R));
+  a.g1scale = (float)(a.G1 / (2.0 * GRID_R));
+  if (GRID && (cb->t.grid == nullptr || cb->grid_G <= 0)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(WAVES * 64), shm, s, a);
   return hipGetLastError();
 }
 

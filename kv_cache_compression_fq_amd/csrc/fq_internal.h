@@ -35,8 +35,29 @@ struct DeviceTables {
   _Float16* cb16hi;  // [N][k]   codewords rounded to binary16
   _Float16* cb16lo;  // [N][k]   (c - hi) * 2^11 rounded to binary16
   _Float16* pifrag;  // Pi as v_mfma_f32_16x16x32_f16 B fragments (decode), see fq_api.hip
-  _Float16* encfrag; // Pi hi / lo as v_mfma_f32_16x16x32_f16 A fragments (encode)
+  _Float16* encfrag; // Pi hi / lo as v_mfma_f32_16x16x16_f16 A fragments (encode)
+  uint16_t* grid;     // k = 2, 3: candidate records of the block grid (fq_grid.cpp)
+  uint16_t* grid1;    // k = 3: candidate records of the one-coordinate last block
 };
+
+// Candidate-list grids for the block search (fq_grid.cpp).
+// uint16 entries per cell record: count + up to 7 (k = 2) or 15 (k = 3) candidates
+__host__ __device__ constexpr int grid_record_entries(int k) { return k == 2 ? 8 : 16; }
+constexpr uint16_t GRID_OVERFLOW = 0xFFFF;
+constexpr double GRID_MARGIN = 1e-4;     // box widening: rotation error + float32 cell arithmetic
+constexpr double GRID_R = 0.5;           // the grid covers [-R, R]^dims
+constexpr double GRID_REACH = 0.3;       // distance searched when building a cell's list
+
+struct GridTable {
+  int dims = 0, G = 0, re = 0;
+  double R = 0.0;
+  int max_len = 0, overflow = 0;
+  std::vector<uint16_t> rec;             // [G^dims][re]
+};
+
+// Candidate lists of the first `dims` coordinates of the N x k codebook `cw`
+// over a G^dims grid on [-R, R]^dims, records of `re` entries.
+void build_grid(const float* cw, int N, int k, int dims, int G, double R, int re, GridTable* out);
 
 }  // namespace fq
 
@@ -48,6 +69,8 @@ struct fq_codebook {
   uint64_t hash;
   float enc_ez16;   // encode: bound on |z~ - z| per coordinate, binary16 input
   float enc_ez32;   // the same for float32 input
+  int grid_G;       // cells per dimension of the block grid (0: no grid, full scan)
+  int grid1_G;      // cells of the last-block grid (k = 3)
   std::vector<double> pi;  // host copy of Pi
   std::vector<float> c;    // host copy of C
   void* dev_block;         // the single device allocation
