@@ -21,8 +21,8 @@
 //  * values O^T = Z_v^T P'^T (P' = p * nu_v in binary16): the A operand is
 //    fetched with ds_read_tr16_b64 transpose reads pointed straight at the
 //    value codewords in LDS (k = 4 or 8), or at value rows expanded into LDS
-//    (k = 2 or 3), in binary16 (relative rounding 2^-12 per coordinate: at
-//    most ~1e-3 relative on the same caches, inside the 2e-3 bound);
+//    (k = 2 or 3), again as hi and lo parts (binary16 value codewords alone
+//    leave errors near 1e-3 relative on outlier-heavy caches);
 //  * scores are kept in the log2 domain (the query carries scale * log2 e), so
 //    every softmax weight is one exp2;
 //  * the wave writes its (m, l, o) partial per query head.
@@ -68,7 +68,7 @@ struct AttShape {
   static constexpr bool EXPAND = !(K == 4 || K == 8);   // value rows expanded into LDS
   __host__ __device__ static constexpr size_t wave_lds() {
     return (size_t)2 * TILE * Sh::IDX_PITCH * 2 + 2 * TILE * 4 +
-           (EXPAND ? (size_t)TILE * Z_PITCH * 2 : 0);
+           (EXPAND ? (size_t)2 * TILE * Z_PITCH * 2 : 0);
   }
 };
 
@@ -141,8 +141,8 @@ struct AttLds {
   __host__ __device__ static size_t key_bytes(int N) {   // key table(s)
     return ((size_t)N * 2 * K * 2 + 15) / 16 * 16;
   }
-  __host__ __device__ static size_t val_bytes(int N) {   // value table (binary16)
-    return ((size_t)N * K * 2 + 15) / 16 * 16;
+  __host__ __device__ static size_t val_bytes(int N) {   // value hi and lo tables
+    return 2 * (((size_t)N * K * 2 + 15) / 16 * 16);
   }
   __host__ __device__ static size_t total(int N) {
     return key_bytes(N) + val_bytes(N) + 16 * Q_PITCH * 2 + MAX_G * D * 4 +
@@ -156,8 +156,8 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_split_kernel(
     const uint16_t* __restrict__ kn, const uint32_t* __restrict__ vc,
     const uint16_t* __restrict__ vn, int Hq, int Hkv, int64_t T, int64_t chunk, int S,
     float scale, const float* __restrict__ pi32, const _Float16* __restrict__ kh_g,
-    const _Float16* __restrict__ kl_g, const _Float16* __restrict__ vh_g, int N,
-    float* __restrict__ ws) {
+    const _Float16* __restrict__ kl_g, const _Float16* __restrict__ vh_g,
+    const _Float16* __restrict__ vl_g, int N, float* __restrict__ ws) {
   using Sh = Shape<K, BITS>;
   using AS = AttShape<K, BITS>;
   using L = AttLds<K, BITS>;
@@ -171,6 +171,7 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_split_kernel(
   _Float16* sK = reinterpret_cast<_Float16*>(smem);                      // key table(s)
   _Float16* sKlo = sK + (size_t)N * K;                                   // k = 3 lo table
   _Float16* sVh = reinterpret_cast<_Float16*>(smem + L::key_bytes(N));
+  _Float16* sVl = reinterpret_cast<_Float16*>(smem + L::key_bytes(N) + L::val_bytes(N) / 2);
   _Float16* sQ = reinterpret_cast<_Float16*>(smem + L::key_bytes(N) + L::val_bytes(N));
   float* sQf = reinterpret_cast<float*>(sQ + 16 * Q_PITCH);             // [MAX_G][D] raw q
   unsigned char* wbase = reinterpret_cast<unsigned char*>(sQf + MAX_G * D) +
@@ -182,6 +183,7 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_split_kernel(
   float* sNk = reinterpret_cast<float*>(sVi + TILE * IP);        // [TILE]
   float* sNv = sNk + TILE;                                       // [TILE]
   _Float16* sZh = reinterpret_cast<_Float16*>(sNv + TILE);       // [TILE][Z_PITCH] (expand)
+  _Float16* sZl = sZh + TILE * Z_PITCH;
 
   for (int e = threadIdx.x; e < N * K; e += ATT_THREADS) {
     const int n = e / K, t = e - n * K;
@@ -193,6 +195,7 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_split_kernel(
       sKlo[e] = kl_g[e];
     }
     sVh[e] = vh_g[e];
+    sVl[e] = vl_g[e];
   }
   for (int e = threadIdx.x; e < MAX_G * D; e += ATT_THREADS) {
     const int h = e / D;
@@ -235,9 +238,12 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_split_kernel(
     qf[s] = *reinterpret_cast<const half8*>(sQ + col * Q_PITCH + 32 * s + 8 * grp);
 
   float m_run = NEG_BIG, l_run = 0.f;
-  floatx4 oh[4];
+  floatx4 oh[4], ol[4];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) oh[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < 4; ++mt) {
+    oh[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    ol[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
 
   auto load = [&](TileRegs<W>& t, int64_t tb) {
     const int64_t left = t1 - tb;
@@ -266,14 +272,17 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_split_kernel(
       const uint16_t* vi = sVi + lane * IP;
 #pragma unroll
       for (int c0 = 0; c0 < D; c0 += 8) {
-        half8 hh;
+        half8 hh, ll;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int c = c0 + e, j = c / K;
           hh[e] = sVh[vi[j] * K + (c - j * K)];
+          ll[e] = sVl[vi[j] * K + (c - j * K)];
         }
         *reinterpret_cast<half4*>(sZh + lane * Z_PITCH + c0) = half4{hh[0], hh[1], hh[2], hh[3]};
         *reinterpret_cast<half4*>(sZh + lane * Z_PITCH + c0 + 4) = half4{hh[4], hh[5], hh[6], hh[7]};
+        *reinterpret_cast<half4*>(sZl + lane * Z_PITCH + c0) = half4{ll[0], ll[1], ll[2], ll[3]};
+        *reinterpret_cast<half4*>(sZl + lane * Z_PITCH + c0 + 4) = half4{ll[4], ll[5], ll[6], ll[7]};
       }
     }
   };
@@ -325,7 +334,10 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_split_kernel(
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) oh[mt] *= alpha;
+      for (int mt = 0; mt < 4; ++mt) {
+        oh[mt] *= alpha;
+        ol[mt] *= alpha;
+      }
     }
     m_run = m_new;
     float ps = 0.f;
@@ -352,18 +364,24 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_split_kernel(
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const int c = 16 * mt + 4 * (col & 3);
-        const _Float16 *pa, *pbp;
+        const _Float16 *pah, *pal, *pbh, *pbl;
         if constexpr (AS::EXPAND) {
-          pa = sZh + tok_a * Z_PITCH + c;
-          pbp = sZh + tok_b * Z_PITCH + c;
+          pah = sZh + tok_a * Z_PITCH + c;
+          pal = sZl + tok_a * Z_PITCH + c;
+          pbh = sZh + tok_b * Z_PITCH + c;
+          pbl = sZl + tok_b * Z_PITCH + c;
         } else {
           const uint32_t ia = sVi[tok_a * IP + c / K], ib = sVi[tok_b * IP + c / K];
-          pa = sVh + ia * K + (c % K);
-          pbp = sVh + ib * K + (c % K);
+          pah = sVh + ia * K + (c % K);
+          pal = sVl + ia * K + (c % K);
+          pbh = sVh + ib * K + (c % K);
+          pbl = sVl + ib * K + (c % K);
         }
-        const half4 ha = read_tr(pa), hb = read_tr(pbp);
+        const half4 ha = read_tr(pah), hb = read_tr(pbh), la = read_tr(pal), lb = read_tr(pbl);
         const half8 zh = {ha[0], ha[1], ha[2], ha[3], hb[0], hb[1], hb[2], hb[3]};
+        const half8 zl = {la[0], la[1], la[2], la[3], lb[0], lb[1], lb[2], lb[3]};
         oh[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(zh, pb[ks], oh[mt], 0, 0, 0);
+        ol[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(zl, pb[ks], ol[mt], 0, 0, 0);
       }
     }
   };
@@ -403,7 +421,7 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_split_kernel(
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        mine[2 + 16 * mt + 4 * grp + r] = oh[mt][r];
+        mine[2 + 16 * mt + 4 * grp + r] = fmaf(ol[mt][r], 0x1p-11f, oh[mt][r]);
   }
   __syncthreads();
   for (int e = threadIdx.x; e < G * D; e += ATT_THREADS) {
@@ -488,7 +506,7 @@ hipError_t launch_v(const fq_codebook* ck, const fq_codebook* cv, const uint16_t
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)p.S, Hkv, B), dim3(ATT_THREADS), shm, s, q, kc, kn, vc, vn, Hq,
                      Hkv, T, p.chunk, p.S, scale, ck->t.pi32, ck->t.cb16hi, ck->t.cb16lo,
-                     cv->t.cb16hi, ck->N, ws);
+                     cv->t.cb16hi, cv->t.cb16lo, ck->N, ws);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attend_merge_kernel, dim3(Hq, B), dim3(256), 0, s, ws, p.S, Hq, ck->t.pi32,

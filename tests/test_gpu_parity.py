@@ -252,3 +252,188 @@ def test_attention_tinyllama_sampled(dev):
         worst = max(worst, rel)
     print(f"tinyllama sampled rows: max rel {worst:.2e}")
     assert worst <= 2e-3
+
+
+# ------------------------------------------------- full-size configurations
+def check_sampled_encode(art, x_host_rows, codes_rows, norms_rows):
+    """Oracle check of sampled rows (indices in window, norms, pad bits)."""
+    return check_encode(art, x_host_rows, codes_rows, norms_rows)
+
+
+def sample_rows(n, m, seed):
+    """m distinct row numbers including the first and last rows and chunk edges."""
+    rng = np.random.default_rng(seed)
+    edge = np.array([0, 1, 15, 16, 17, n // 2, n - 17, n - 16, n - 1])
+    return np.unique(np.concatenate([edge, rng.choice(n, size=m, replace=False)]))
+
+
+def all_norms_ok(x_dev, norms_dev, rows=None):
+    """Norms of a device array (all rows, or `rows`) against float64 norms
+    computed on the host and rounded once."""
+    norms = norms_dev.cpu().numpy().view(np.uint16)
+    if rows is not None:
+        norms = norms[rows]
+        xs = x_dev[torch.from_numpy(rows).to(x_dev.device)]
+    else:
+        xs = x_dev
+    nu = np.empty(xs.shape[0])
+    step = 1 << 20
+    for s in range(0, xs.shape[0], step):
+        xh = xs[s:s + step].cpu().numpy().astype(np.float64)
+        nu[s:s + step] = np.sqrt(np.sum(xh * xh, axis=1))
+    return check_norms_from_nu(nu, norms)
+
+
+def check_norms_from_nu(nu, norms):
+    want = codec.f16_round(nu)
+    diff = np.nonzero(norms != want)[0]
+    for r in diff:
+        lo = codec.f16_value(np.array([min(norms[r], want[r])]))[0]
+        hi = codec.f16_value(np.array([max(norms[r], want[r])]))[0]
+        assert abs(int(norms[r]) - int(want[r])) == 1, (r, norms[r], want[r])
+        assert abs(nu[r] - 0.5 * (lo + hi)) <= 1e-6 * nu[r], (r, nu[r])
+    return len(diff)
+
+
+def pad_bits_zero(art, codes_dev):
+    used = art["nb"] * art["bits"] - 32 * (art["W"] - 1)
+    if used >= 32:
+        return True
+    last = codes_dev[:, -1].cpu().numpy().view(np.uint32)
+    return bool(np.all((last >> np.uint32(used)) == 0))
+
+
+_GPT2 = []
+
+
+def gpt2_cache():
+    if not _GPT2:
+        _GPT2.append(synth.kv_cache(2, 12, 4, 12, 1024).reshape(-1, 64))
+    return _GPT2[0]
+
+
+@pytest.mark.parametrize("k,N", [(2, 16), (2, 64), (2, 256), (3, 512)])
+def test_gpt2_cache_full_size(dev, k, N):
+    """GPT-2-small-shaped cache, every vector encoded and decoded on the GPU in
+    the bench's launch configuration; 4096 sampled rows checked against the
+    oracle; every norm and every record's pad bits checked."""
+    print(f"gpt2 cache k{k}N{N}", flush=True)
+    art, cb = book(k, N)
+    x = gpt2_cache()
+    n = len(x)
+    xd = to_dev(x, dev)
+    codes, norms = fq.fq_encode(cb, xd)
+    y = fq.fq_decode(cb, codes, norms)
+    torch.cuda.synchronize()
+    assert pad_bits_zero(art, codes)
+    all_norms_ok(xd, norms)
+    rows = sample_rows(n, 4096, seed=k * 1000 + N)
+    c_s = codes[torch.from_numpy(rows).to(dev)].cpu().numpy().view(np.uint32)
+    n_s = norms[torch.from_numpy(rows).to(dev)].cpu().numpy().view(np.uint16)
+    ex, win = check_encode(art, x[rows], c_s, n_s)
+    idx = codec.unpack(c_s, art["nb"], art["bits"])
+    want = codec.decode(idx, n_s, art["Pi"], art["C"])
+    got = y[torch.from_numpy(rows).to(dev)].float().cpu().numpy().astype(np.float64)
+    nu16 = codec.f16_value(n_s)
+    err = np.max(np.abs(got - want), axis=1)
+    assert np.all(err <= 1e-3 * nu16 + 1e-30)
+    print(f"k{k}N{N}: {n} vectors; sampled {len(rows)}: {ex} exact, {win} in window, "
+          f"decode max err/nu {np.max(err / np.maximum(nu16, 1e-30)):.2e}")
+
+
+@pytest.mark.parametrize("k,N", [(4, 256), (8, 256)])
+def test_tinyllama_cache_encode_and_random_access(dev, k, N):
+    """TinyLlama-shaped cache (22 layers x {K,V} x batch 8 x 4 heads x 2048
+    tokens, generated on the device): full encode, 4096 sampled rows against
+    the oracle, then 2^20 uniformly drawn addresses decoded by address; 4096
+    of those outputs checked against the oracle's decode of the same records."""
+    print(f"tinyllama cache k{k}N{N}", flush=True)
+    art, cb = book(k, N)
+    L, B, H, T = 22, 8, 4, 2048
+    slabs = [synth.kv_slab_device(3, layer, kv, B, H, T, dev).reshape(-1, 64)
+             for layer in range(L) for kv in range(2)]
+    xd = torch.cat(slabs)
+    del slabs
+    n = xd.shape[0]
+    codes, norms = fq.fq_encode(cb, xd)
+    torch.cuda.synchronize()
+    assert pad_bits_zero(art, codes)
+    all_norms_ok(xd, norms)
+    rows = sample_rows(n, 4096, seed=k * 1000 + N + 1)
+    rt = torch.from_numpy(rows).to(dev)
+    x_s = xd[rt].cpu().numpy()
+    ex, win = check_encode(art, x_s, codes[rt].cpu().numpy().view(np.uint32),
+                           norms[rt].cpu().numpy().view(np.uint16))
+    addr = synth.random_rows(n, 1 << 20, seed=33)
+    y = fq.fq_decode(cb, codes, norms, rows=to_dev(addr, dev))
+    torch.cuda.synchronize()
+    pick = np.random.default_rng(7).choice(len(addr), size=4096, replace=False)
+    rec = addr[pick]
+    pt = torch.from_numpy(rec).to(dev)
+    c_s = codes[pt].cpu().numpy().view(np.uint32)
+    n_s = norms[pt].cpu().numpy().view(np.uint16)
+    want = codec.decode(codec.unpack(c_s, art["nb"], art["bits"]), n_s, art["Pi"], art["C"])
+    got = y[torch.from_numpy(pick).to(dev)].float().cpu().numpy().astype(np.float64)
+    nu16 = codec.f16_value(n_s)
+    err = np.max(np.abs(got - want), axis=1)
+    assert np.all(err <= 1e-3 * nu16 + 1e-30)
+    print(f"k{k}N{N}: {n} vectors; sampled {len(rows)}: {ex} exact, {win} in window; "
+          f"random access max err/nu {np.max(err / np.maximum(nu16, 1e-30)):.2e}")
+
+
+@pytest.mark.parametrize("k,N", [(8, 16), (4, 4), (3, 4096)])
+def test_stress_set_2_24(dev, k, N):
+    """2^24 vectors (256 streams x 65536 tokens, generated on the device):
+    full encode and decode; 2048 sampled rows against the oracle; every norm
+    and pad bit."""
+    print(f"stress set k{k}N{N}", flush=True)
+    art, cb = book(k, N)
+    xd = synth.kv_slab_device(4, 0, 0, 1, 256, 65536, dev).reshape(-1, 64)
+    n = xd.shape[0]
+    codes, norms = fq.fq_encode(cb, xd)
+    y = fq.fq_decode(cb, codes, norms)
+    torch.cuda.synchronize()
+    assert pad_bits_zero(art, codes)
+    rows = sample_rows(n, 2048, seed=k * 1000 + N + 2)
+    all_norms_ok(xd, norms, np.random.default_rng(9).choice(n, size=1 << 20, replace=False))
+    rt = torch.from_numpy(rows).to(dev)
+    c_s = codes[rt].cpu().numpy().view(np.uint32)
+    n_s = norms[rt].cpu().numpy().view(np.uint16)
+    ex, win = check_encode(art, xd[rt].cpu().numpy(), c_s, n_s)
+    want = codec.decode(codec.unpack(c_s, art["nb"], art["bits"]), n_s, art["Pi"], art["C"])
+    got = y[rt].float().cpu().numpy().astype(np.float64)
+    nu16 = codec.f16_value(n_s)
+    err = np.max(np.abs(got - want), axis=1)
+    assert np.all(err <= 1e-3 * nu16 + 1e-30)
+    print(f"k{k}N{N}: {n} vectors; sampled {len(rows)}: {ex} exact, {win} in window")
+
+
+@pytest.mark.parametrize("layer", [0, 21])
+def test_attention_tinyllama_layer_full(dev, layer):
+    """One TinyLlama decode-step layer in full: batch 16, 32 query / 4 KV heads,
+    32768 tokens, k4N256 keys and values generated and encoded on the device;
+    every (b, h) output checked against the oracle's decompress-then-attend of
+    the same records."""
+    print(f"attention layer {layer}", flush=True)
+    art, cb = book(4, 256)
+    B, Hq, Hkv, T = 16, 32, 4, 32768
+    enc = []
+    for kv in range(2):
+        x = synth.kv_slab_device(3, layer, kv, B, Hkv, T, dev).reshape(-1, 64)
+        c, nn = fq.fq_encode(cb, x)
+        enc.append((c.view(B, Hkv, T, cb.W), nn.view(B, Hkv, T)))
+        del x
+    q = synth.query(B, Hq, seed=5)
+    out = fq.fq_attend_decode(cb, cb, to_dev(q, dev), enc[0][0], enc[0][1], enc[1][0],
+                              enc[1][1], 0.125)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    kw = enc[0][0].cpu().numpy().view(np.uint32)
+    kn = enc[0][1].cpu().numpy().view(np.uint16)
+    vw = enc[1][0].cpu().numpy().view(np.uint32)
+    vn = enc[1][1].cpu().numpy().view(np.uint16)
+    ref = attend.attend(q, kw, kn, vw, vn, art["Pi"], art["C"], art["C"], 0.125)
+    rel = np.linalg.norm(got - ref, axis=-1) / np.linalg.norm(ref, axis=-1)
+    glob = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    print(f"layer {layer}: max rel {np.max(rel):.2e}, global {glob:.2e}")
+    assert np.max(rel) <= 2e-3
