@@ -184,7 +184,10 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
   memcpy(cb->c.data(), cw_p, 4ull * N * k);
 
   // host-side tables
-  std::vector<float> pi32((size_t)d * d), enc((size_t)N * S, 0.f);
+  // search table: N rows (-2c, |c|^2) and a sentinel row N (zero codeword,
+  // infinite norm) that padded candidate slots point at
+  std::vector<float> pi32((size_t)d * d), enc((size_t)(N + 1) * S, 0.f);
+  enc[(size_t)N * S + k] = INFINITY;
   std::vector<_Float16> pih((size_t)d * d), pil((size_t)d * d), cbh((size_t)N * k),
       cbl((size_t)N * k);
   double rho_pi = 0.0;   // largest |Pi - hi - 2^-11 lo|
@@ -214,8 +217,10 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
   // input the split of x adds 2^-23.
   {
     const double acc = 20.0 * 0x1p-23 * (1.0 + 0x1p-10) * (1.0 + 0x1p-11);
-    cb->enc_ez16 = (float)((acc + 8.0 * rho_pi + 0x1p-22) * 1.01);
-    cb->enc_ez32 = (float)((acc + 8.0 * rho_pi + 0x1p-22 + 0x1p-23) * 1.01);
+    // scaling: norm within 3.3e-7 relative, reciprocal 1 ulp, final fma and product
+    const double scal = 3.3e-7 + 3.0 * 0x1p-24;
+    cb->enc_ez16 = (float)((acc + 8.0 * rho_pi + scal) * 1.01);
+    cb->enc_ez32 = (float)((acc + 8.0 * rho_pi + scal + 0x1p-23 + 0x1p-24) * 1.01);
   }
   // Pi as B fragments of v_mfma_f32_16x16x32_f16 for Y = Z Pi: fragment
   // [part][s][nt][lane][e] = part(Pi)[32 s + 8 (lane / 16) + e][16 nt + lane % 16],
@@ -249,10 +254,10 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
   cb->grid1_G = 0;
   if (k == 2 || k == 3) {
     const int G = (k == 2) ? (N <= 64 ? 32 : 64) : (N <= 512 ? 32 : 64);
-    fq::build_grid(cb->c.data(), N, k, k, G, fq::GRID_R, fq::grid_record_entries(k), &grid);
+    fq::build_grid(cb->c.data(), N, k, k, G, fq::GRID_R, fq::grid_record_entries(k), (uint16_t)N, &grid);
     cb->grid_G = G;
     if (cb->last < k) {
-      fq::build_grid(cb->c.data(), N, k, 1, 4 * N, fq::GRID_R, fq::grid_record_entries(k), &grid1);
+      fq::build_grid(cb->c.data(), N, k, 1, 4 * N, fq::GRID_R, fq::grid_record_entries(k), (uint16_t)N, &grid1);
       cb->grid1_G = 4 * N;
     }
   }
@@ -265,7 +270,7 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
     return o;
   };
   const size_t o_pi64 = take(8ull * d * d), o_pi32 = take(4ull * d * d),
-               o_enc = take(4ull * N * S), o_cbh = take(2ull * N * k),
+               o_enc = take(4ull * (N + 1) * S), o_cbh = take(2ull * N * k),
                o_cbl = take(2ull * N * k), o_frag = take(2ull * frag.size()),
                o_efrag = take(2ull * efrag.size()),
                o_grid = take(2ull * grid.rec.size() + 64), o_grid1 = take(2ull * grid1.rec.size() + 64);
@@ -294,7 +299,7 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
     std::vector<char> staging(off, 0);
     memcpy(staging.data() + o_pi64, cb->pi.data(), 8ull * d * d);
     memcpy(staging.data() + o_pi32, pi32.data(), 4ull * d * d);
-    memcpy(staging.data() + o_enc, enc.data(), 4ull * N * S);
+    memcpy(staging.data() + o_enc, enc.data(), 4ull * (N + 1) * S);
     memcpy(staging.data() + o_cbh, cbh.data(), 2ull * N * k);
     memcpy(staging.data() + o_cbl, cbl.data(), 2ull * N * k);
     memcpy(staging.data() + o_frag, frag.data(), 2ull * frag.size());

@@ -58,7 +58,7 @@ struct EncShape {
   static constexpr int NCOL = EV * NB;              // columns per chunk
   static constexpr int CPL = (NCOL + 63) / 64;      // columns per lane
   static constexpr size_t WAVE_BYTES =
-      ((size_t)EV * ZP * 4 + EV * 8 + (size_t)EV * IP * 2 + (size_t)NCOL * 2 + 15) / 16 * 16;
+      ((size_t)EV * ZP * 4 + (size_t)EV * IP * 2 + (size_t)NCOL * 2 + 15) / 16 * 16;
 };
 
 struct EncArgs {
@@ -78,8 +78,8 @@ struct EncArgs {
   float gscale, g1scale;   // cells per unit length
 };
 
-__host__ __device__ inline size_t enc_table_bytes(int N, int S) {
-  return ((size_t)N * S * 4 + 15) / 16 * 16;
+__host__ __device__ inline size_t enc_table_bytes(int N, int S) {   // N rows + sentinel
+  return ((size_t)(N + 1) * S * 4 + 15) / 16 * 16;
 }
 
 __device__ inline double shfl_xor_f64(double v, int m) {
@@ -96,9 +96,23 @@ __device__ inline double shfl_xor_f64(double v, int m) {
 template <typename TX>
 struct XFrag {
   half4 hi[4], lo[4];
-  double ss;
+  float ss;       // sum of squares of the (scaled) vector, pairwise in float32
   float escale;   // the fragments hold x * 2^-e; escale = 2^e
 };
+
+// Pairwise float32 sum of the 16 squares a lane holds, then across the four
+// lanes of the vector: six rounding levels, so the relative error of the
+// (positive) sum is below 6 * 2^-24, well inside the norm's tolerance.
+__device__ inline float pairwise_squares(const float (&v)[16]) {
+  float t8[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) t8[i] = fmaf(v[2 * i], v[2 * i], v[2 * i + 1] * v[2 * i + 1]);
+  const float t4[4] = {t8[0] + t8[1], t8[2] + t8[3], t8[4] + t8[5], t8[6] + t8[7]};
+  float ss = (t4[0] + t4[1]) + (t4[2] + t4[3]);
+  ss += __shfl_xor(ss, 16, 64);
+  ss += __shfl_xor(ss, 32, 64);
+  return ss;
+}
 
 // Raw loads of one lane's x elements (issued one chunk ahead).
 template <typename TX>
@@ -124,67 +138,75 @@ __device__ inline void finish_x(const XRaw<TX>& r, XFrag<TX>& f);
 
 template <>
 __device__ inline void finish_x<_Float16>(const XRaw<_Float16>& r, XFrag<_Float16>& f) {
-  double ss = 0.0;
+  float v[16];
 #pragma unroll
   for (int kq = 0; kq < 4; ++kq) {
     f.hi[kq] = __builtin_bit_cast(half4, r.q[kq]);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const double t = (double)(float)f.hi[kq][e];
-      ss = fma(t, t, ss);
-    }
+    for (int e = 0; e < 4; ++e) v[4 * kq + e] = (float)f.hi[kq][e];   // squares exact in float32
   }
-  ss += shfl_xor_f64(ss, 16);
-  ss += shfl_xor_f64(ss, 32);
-  f.ss = ss;
+  f.ss = pairwise_squares(v);
   f.escale = 1.f;
 }
 
 template <>
 __device__ inline void finish_x<float>(const XRaw<float>& r, XFrag<float>& f) {
-  double ss = 0.0;
   float mx = 0.f;
 #pragma unroll
   for (int kq = 0; kq < 4; ++kq)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      ss = fma((double)r.q[kq][e], (double)r.q[kq][e], ss);
-      mx = fmaxf(mx, fabsf(r.q[kq][e]));
-    }
-  ss += shfl_xor_f64(ss, 16);
-  ss += shfl_xor_f64(ss, 32);
+    for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(r.q[kq][e]));
   mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
   mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  // scale so that |x| <= 1: binary16 then holds every element without overflow
+  // scale so that |x| <= 1: binary16 then holds every element without overflow,
+  // and the squares cannot overflow float32
   int e = 0;
   if (mx > 0.f && mx <= 3.0e38f) (void)frexpf(mx, &e);
   const float down = ldexpf(1.f, -e);
+  float v[16];
 #pragma unroll
   for (int kq = 0; kq < 4; ++kq)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float sv = r.q[kq][i] * down;
+      v[4 * kq + i] = sv;
       const _Float16 h = (_Float16)sv;
       f.hi[kq][i] = h;
       f.lo[kq][i] = (_Float16)((sv - (float)h) * 2048.f);
     }
-  f.ss = ss;
+  f.ss = pairwise_squares(v);
   f.escale = ldexpf(1.f, e);
 }
 
-// Word w of a record from the staged indices of one vector.
-template <int BITS>
-__device__ inline uint32_t pack_word(const uint16_t* idx, int nb, int w) {
-  const int j0 = (32 * w) / BITS;
-  int j1 = (32 * w + 31) / BITS;
-  if (j1 > nb - 1) j1 = nb - 1;
-  uint32_t v = 0;
-  for (int jj = j0; jj <= j1; ++jj) {
-    const int s = jj * BITS - 32 * w;
-    const uint32_t f = idx[jj];
-    v |= s >= 0 ? (f << s) : (f >> (-s));
+// Word w of a record from the staged indices of one vector (4-byte aligned
+// row of uint16): byte permutes for 8-bit fields, nibble merges for 4-bit
+// fields, a shift loop otherwise.
+template <int BITS, int NB>
+__device__ inline uint32_t pack_word(const uint16_t* idx, int w) {
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(idx);
+  if constexpr (BITS == 8 && NB % 4 == 0) {
+    const uint32_t d0 = p[2 * w], d1 = p[2 * w + 1];   // (i0 | i1 << 16), (i2 | i3 << 16)
+    return __builtin_amdgcn_perm(d1, d0, 0x06040200u);
+  } else if constexpr (BITS == 4 && NB % 8 == 0) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t d = p[4 * w + q];
+      v |= ((d & 0xFu) | ((d >> 12) & 0xF0u)) << (8 * q);
+    }
+    return v;
+  } else {
+    const int j0 = (32 * w) / BITS;
+    int j1 = (32 * w + 31) / BITS;
+    if (j1 > NB - 1) j1 = NB - 1;
+    uint32_t v = 0;
+    for (int jj = j0; jj <= j1; ++jj) {
+      const int sh = jj * BITS - 32 * w;
+      const uint32_t f = idx[jj];
+      v |= sh >= 0 ? (f << sh) : (f >> (-sh));
+    }
+    return v;
   }
-  return v;
 }
 
 // A column (one block of one vector) ready for the search: its coordinates,
@@ -240,16 +262,18 @@ __device__ inline void search_column(const ColPrep<K, RW>& cp, const float* sEnc
   float m1 = INFINITY, m2 = INFINITY;
   int i1 = 0;
   bool listed = true;   // the search covered every possible nearest codeword
+  // list slots past the count hold the sentinel row N (zero codeword with an
+  // infinite norm), so a full block needs no per-slot test
   auto visit = [&](const float* er, int i, bool use) {
     float t;
     if constexpr (LASTB) {
       t = fmaf(er[0], cp.z[0], 0.25f * er[0] * er[0]);
+      t = use ? t : INFINITY;
     } else {
       t = er[K];
 #pragma unroll
       for (int tt = 0; tt < K; ++tt) t = fmaf(er[tt], cp.z[tt], t);
     }
-    t = use ? t : INFINITY;
     const bool p = t < m1;
     m2 = __builtin_amdgcn_fmed3f(m1, m2, t);
     m1 = p ? t : m1;
@@ -275,8 +299,8 @@ __device__ inline void search_column(const ColPrep<K, RW>& cp, const float* sEnc
   constexpr float KSQ = LASTB ? 1.f : (K == 2 ? 1.41421356f : (K == 3 ? 1.73205081f : (K == 4 ? 2.f : 2.82842712f)));
   const float d2 = fmaxf(m2 + cp.zz, 0.f) + SLACK;
   // hardware square root (within 1 ulp), nudged up to stay an upper bound
-  const float rt = __builtin_amdgcn_sqrtf(d2) * 1.0001f;
-  const float thr = 2.f * gv * (2.f * d2 + 18.f * cp.zz) + 4.f * ez * KSQ * rt + 1e-12f;
+  const float rt = __builtin_amdgcn_sqrtf(d2);
+  const float thr = fmaf(4.f * gv, d2, fmaf(36.f * gv, cp.zz, fmaf(4.0004f * ez * KSQ, rt, 1e-12f)));
   // a single listed candidate is the nearest codeword everywhere in the cell
   certain = listed && m1 < INFINITY && (m2 == INFINITY || (m2 - m1) > thr);
   i1out = i1;
@@ -298,13 +322,12 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   unsigned char* wb = smem + ROT_BYTES + enc_table_bytes(N, S) + wave * Sh::WAVE_BYTES;
   float* sZ = reinterpret_cast<float*>(wb);
-  double* sNu = reinterpret_cast<double*>(wb + EV * ZP * 4);
-  uint16_t* sIdx = reinterpret_cast<uint16_t*>(wb + EV * ZP * 4 + EV * 8);
+  uint16_t* sIdx = reinterpret_cast<uint16_t*>(wb + EV * ZP * 4);
   uint16_t* sFb = sIdx + EV * IP;
 
   for (int i = threadIdx.x; i < ROT_BYTES / 16; i += blockDim.x)
     reinterpret_cast<u32x4*>(sRot)[i] = reinterpret_cast<const u32x4*>(a.rotfrag)[i];
-  for (int i = threadIdx.x; i < N * S / 4; i += blockDim.x)
+  for (int i = threadIdx.x; i < (N + 1) * S / 4; i += blockDim.x)
     reinterpret_cast<floatx4*>(sEnc)[i] = reinterpret_cast<const floatx4*>(a.enc)[i];
   __syncthreads();
 
@@ -331,12 +354,14 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
     XFrag<TX> xf;
     finish_x<TX>(xraw, xf);
     if (ch + tw < nchunks) load_raw<TX>(row_of(ch + tw), g, xraw);
-    const double nu = sqrt(xf.ss);
-    const uint16_t nbits = f64_to_f16_bits(nu);
-    // a zero vector gets NaN coordinates: its blocks go to the exact path,
-    // which returns index 0 for them
-    const float inv = nu > 0.0 ? (float)((double)xf.escale / nu) : __builtin_nanf("");
-    if (g == 0) sNu[j] = nu;
+    // norm within 3.3e-7 relative (pairwise sum, hardware square root): its
+    // binary16 rounding differs from that of the exact norm only within that
+    // distance of a rounding midpoint
+    const float nus = __builtin_amdgcn_sqrtf(xf.ss);     // norm of the scaled vector
+    const uint16_t nbits = f32_to_f16_rne(nus * xf.escale);
+    // a zero vector gets NaN coordinates (0 * inf): its blocks go to the exact
+    // path, which returns index 0 for them
+    const float inv = __builtin_amdgcn_rcpf(nus);
 
     // ---- 2. rotation: lane holds z~[vector j][16 ot + 4 g + r]; every
     //      16-product group is accumulated from zero and the groups are summed
@@ -429,11 +454,16 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
       const bool last = c >= NCF;
       const int v = last ? c - NCF : c / NBF, b = last ? NB - 1 : c - (c / NBF) * NBF;
       const int rj = last ? Sh::LAST : K;
-      const double nuv = sNu[v];
       const TX* xr = x + (base + v) * a.ld + 4 * l16;
       double xq[4];
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) xq[qq] = (double)xr[qq];
+      double ssd = 0.0;
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) ssd = fma(xq[qq], xq[qq], ssd);
+#pragma unroll
+      for (int m = 8; m >= 1; m >>= 1) ssd += shfl_xor_f64(ssd, m);
+      const double nuv = sqrt(ssd);
       double pr[K][4];
 #pragma unroll
       for (int t = 0; t < K; ++t)
@@ -483,7 +513,7 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
     uint32_t* __restrict__ out = a.codes + base * Sh::W;
     for (int t = lane; t < nv * Sh::W; t += 64) {
       const int v = t / Sh::W, w = t - v * Sh::W;
-      out[t] = pack_word<BITS>(sIdx + v * IP, NB, w);
+      out[t] = pack_word<BITS, NB>(sIdx + v * IP, w);
     }
     if (g == 0 && j < nv) a.norms[base + j] = nbits;
     wave_lds_sync();

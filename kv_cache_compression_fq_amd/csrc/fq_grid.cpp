@@ -20,7 +20,7 @@
 //
 // Records: `re` uint16 per cell, entry 0 the count (GRID_OVERFLOW when the
 // list does not fit or the cell is far outside the codebook), then the indices
-// in increasing order, zero padded.
+// in increasing order; unused entries hold `pad` (the encoder's sentinel row).
 #include <math.h>
 
 #include <algorithm>
@@ -31,7 +31,8 @@
 
 namespace fq {
 
-void build_grid(const float* cw, int N, int k, int dims, int G, double R, int re, GridTable* out) {
+void build_grid(const float* cw, int N, int k, int dims, int G, double R, int re, uint16_t pad,
+                GridTable* out) {
   const double h = 2.0 * R / G, mu = GRID_MARGIN;
   int ncell = 1;
   for (int t = 0; t < dims; ++t) ncell *= G;
@@ -41,7 +42,7 @@ void build_grid(const float* cw, int N, int k, int dims, int G, double R, int re
   out->R = R;
   out->max_len = 0;
   out->overflow = 0;
-  out->rec.assign((size_t)ncell * re, 0);
+  out->rec.assign((size_t)ncell * re, pad);
 
   // codeword coordinates (first `dims`), norms, bucket = clamped cell
   std::vector<double> P((size_t)N * dims), cc(N);

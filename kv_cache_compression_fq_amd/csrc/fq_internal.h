@@ -31,7 +31,8 @@ inline bool variant_supported(int k, int bits) {
 struct DeviceTables {
   double* pi64;      // [64][64] Pi, row-major (z = Pi u)
   float* pi32;       // [64][64] Pi rounded to float32
-  float* enc;        // [N][S]  search table: -2 c_0 .. -2 c_{k-1}, |c|^2, zero pad; S = enc_stride
+  float* enc;        // [N + 1][S] search table: -2 c_0 .. -2 c_{k-1}, |c|^2, zero pad; S =
+                     // enc_stride; row N is a sentinel (zero codeword, infinite norm)
   _Float16* cb16hi;  // [N][k]   codewords rounded to binary16
   _Float16* cb16lo;  // [N][k]   (c - hi) * 2^11 rounded to binary16
   _Float16* pifrag;  // Pi as v_mfma_f32_16x16x32_f16 B fragments (decode), see fq_api.hip
@@ -56,8 +57,10 @@ struct GridTable {
 };
 
 // Candidate lists of the first `dims` coordinates of the N x k codebook `cw`
-// over a G^dims grid on [-R, R]^dims, records of `re` entries.
-void build_grid(const float* cw, int N, int k, int dims, int G, double R, int re, GridTable* out);
+// over a G^dims grid on [-R, R]^dims, records of `re` entries, unused slots
+// set to `pad`.
+void build_grid(const float* cw, int N, int k, int dims, int G, double R, int re, uint16_t pad,
+                GridTable* out);
 
 }  // namespace fq
 
