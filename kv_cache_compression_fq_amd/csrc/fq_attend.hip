@@ -8,25 +8,34 @@
 // query heads per wave, tiles of 64 tokens:
 //  * lane t loads the K and V records and norms of token t (unconditional
 //    buffer loads, next two tiles in flight) and unpacks them into 16-bit index
-//    tables in LDS;
-//  * scores S^T = Z_k [Q_hi | Q_lo]^T on v_mfma_f32_16x16x32_f16: A = the
-//    tile's key codewords gathered from the LDS codebook (binary16 hi and
-//    lo = (c - hi) 2^11), B = the rotated, scaled queries of the group in
-//    columns 0..G-1 (binary16 hi) and 8..8+G-1 (lo = (q - hi) 2^11); one DPP
-//    rotation folds the lo columns in.  The scores carry ~22 bits, which the
-//    outlier-heavy caches need (rounding only the key codebook to binary16
-//    moves attention outputs by up to 1e-2 relative);
+//    tables in LDS (value indices permuted so that the four a lane needs sit
+//    together);
+//  * scores on v_mfma_f32_16x16x32_f16 as one product over a stacked
+//    contraction: A = [Z_hi | Z_hi | Z_lo] (the tile's key codewords gathered
+//    from the LDS codebook, lo = (c - hi) 2^11), B = [Q_hi ; Q_lo ; Q_hi 2^-11]
+//    (the rotated, scaled queries of the group in columns 0..G-1, lo = q - hi),
+//    so every product has weight one and a single accumulator holds
+//    z_hi q_hi + z_hi q_lo + z_lo q_hi: ~22 bits, which the outlier-heavy caches
+//    need (rounding only the key codebook to binary16 moves attention outputs
+//    by up to 1e-2 relative);
 //  * online softmax in registers: lane (h, g) owns head h and tokens
 //    4g..4g+3 of every 16-token sub-tile;
 //  * values O^T = Z_v^T P'^T (P' = p * nu_v in binary16): the A operand is
 //    fetched with ds_read_tr16_b64 transpose reads pointed straight at the
 //    value codewords in LDS (k = 4 or 8), or at value rows expanded into LDS
 //    (k = 2 or 3), again as hi and lo parts (binary16 value codewords alone
-//    leave errors near 1e-3 relative on outlier-heavy caches);
+//    leave errors near 1e-3 relative on outlier-heavy caches); the lo part
+//    enters the same accumulator through a second K-step with P' 2^-11;
+//  * for k = 4 and 8 both products use v_mfma_f32_16x16x16_f16, whose A
+//    operand is one codeword row per lane (scores) or one transpose read
+//    (values), and whose B operand for the values is the lane's own four
+//    weights, so nothing is repacked;
 //  * scores are kept in the log2 domain (the query carries scale * log2 e), so
 //    every softmax weight is one exp2;
 //  * the wave writes its (m, l, o) partial per query head.
 // Kernel B merges the splits (log-sum-exp), applies Pi^T and writes binary16.
+#include <type_traits>
+
 #include "fq_common.h"
 #include "fq_internal.h"
 
@@ -133,6 +142,32 @@ __device__ inline float rot8(float x) {   // value of lane (l +- 8) within its 1
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
 }
 
+// Value record of one token into LDS with the indices permuted for the value
+// pass: block b = (16 / K) mt + q goes to position 4 q + mt (k = 4, 8), so a
+// lane reads the four blocks of its coordinate quarter with one 8-byte load.
+template <int K, int BITS, int W>
+__device__ inline void unpack_record_vperm(const uint32_t (&w)[W], uint16_t* dst) {
+  constexpr int NB = Shape<K, BITS>::NB;
+  constexpr int QB = 16 / K;
+  static_assert(NB == 4 * QB, "four blocks per coordinate quarter");
+  constexpr uint32_t MASK = (1u << BITS) - 1u;
+  uint32_t f[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int pos = j * BITS, wi = pos >> 5, o = pos & 31;
+    uint32_t v = w[wi] >> o;
+    if (o + BITS > 32) v |= w[wi + 1] << (32 - o);
+    f[j] = v & MASK;
+  }
+  uint32_t* d32 = reinterpret_cast<uint32_t*>(dst);
+#pragma unroll
+  for (int i = 0; i < NB / 2; ++i) {
+    const int p0 = 2 * i, p1 = 2 * i + 1;              // positions 4 q + mt
+    const int b0 = QB * (p0 & 3) + (p0 >> 2), b1 = QB * (p1 & 3) + (p1 >> 2);
+    d32[i] = f[b0] | (f[b1] << 16);
+  }
+}
+
 constexpr int MERGE_PITCH = PART + 2;   // floats per wave partial in the LDS merge area
 
 template <int K, int BITS>
@@ -145,13 +180,13 @@ struct AttLds {
     return 2 * (((size_t)N * K * 2 + 15) / 16 * 16);
   }
   __host__ __device__ static size_t total(int N) {
-    return key_bytes(N) + val_bytes(N) + 16 * Q_PITCH * 2 + MAX_G * D * 4 +
+    return key_bytes(N) + val_bytes(N) + 48 * Q_PITCH * 2 + MAX_G * D * 4 +
            ATT_WAVES * AttShape<K, BITS>::wave_lds() + ATT_WAVES * MAX_G * MERGE_PITCH * 4;
   }
 };
 
 template <int K, int BITS>
-__global__ __launch_bounds__(ATT_THREADS) void attend_split_kernel(
+__global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void attend_split_kernel(
     const uint16_t* __restrict__ q, const uint32_t* __restrict__ kc,
     const uint16_t* __restrict__ kn, const uint32_t* __restrict__ vc,
     const uint16_t* __restrict__ vn, int Hq, int Hkv, int64_t T, int64_t chunk, int S,
@@ -173,7 +208,7 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_split_kernel(
   _Float16* sVh = reinterpret_cast<_Float16*>(smem + L::key_bytes(N));
   _Float16* sVl = reinterpret_cast<_Float16*>(smem + L::key_bytes(N) + L::val_bytes(N) / 2);
   _Float16* sQ = reinterpret_cast<_Float16*>(smem + L::key_bytes(N) + L::val_bytes(N));
-  float* sQf = reinterpret_cast<float*>(sQ + 16 * Q_PITCH);             // [MAX_G][D] raw q
+  float* sQf = reinterpret_cast<float*>(sQ + 48 * Q_PITCH);             // [MAX_G][D] raw q
   unsigned char* wbase = reinterpret_cast<unsigned char*>(sQf + MAX_G * D) +
                          (size_t)wave * AS::wave_lds();
   float* sMerge = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(sQf + MAX_G * D) +
@@ -194,16 +229,22 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_split_kernel(
       sK[e] = kh_g[e];
       sKlo[e] = kl_g[e];
     }
-    sVh[e] = vh_g[e];
-    sVl[e] = vl_g[e];
+    if constexpr (AS::EXPAND) {
+      sVh[e] = vh_g[e];
+      sVl[e] = vl_g[e];
+    } else {   // interleaved rows [hi | lo] like the key table
+      sVh[n * 2 * K + t] = vh_g[e];
+      sVh[n * 2 * K + K + t] = vl_g[e];
+    }
   }
   for (int e = threadIdx.x; e < MAX_G * D; e += ATT_THREADS) {
     const int h = e / D;
     sQf[e] = h < G ? f16_bits_to_f32(q[((int64_t)b * Hq + (int64_t)g * G + h) * D + (e % D)]) : 0.f;
   }
   __syncthreads();
-  // rotated, scaled queries: row h < G = hi part of head h, row 8 + h = lo part;
-  // thread (c, hq) forms coordinate c of heads hq and hq + 4
+  // rotated, scaled queries, three parts of 16 rows (heads; rows >= G are
+  // zero): part 0 = hi, part 1 = lo = q - hi, part 2 = hi 2^-11; thread (c, hq)
+  // forms coordinate c of heads hq and hq + 4
   {
     const int c = threadIdx.x & 63, hq = threadIdx.x >> 6;
     const float4* prow = reinterpret_cast<const float4*>(pi32 + c * D);
@@ -221,8 +262,15 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_split_kernel(
     const _Float16 h0 = (_Float16)a0, h1 = (_Float16)a1;
     sQ[hq * Q_PITCH + c] = h0;
     sQ[(hq + 4) * Q_PITCH + c] = h1;
-    sQ[(8 + hq) * Q_PITCH + c] = (_Float16)((a0 - (float)h0) * 2048.f);
-    sQ[(12 + hq) * Q_PITCH + c] = (_Float16)((a1 - (float)h1) * 2048.f);
+    sQ[(16 + hq) * Q_PITCH + c] = (_Float16)(a0 - (float)h0);
+    sQ[(16 + hq + 4) * Q_PITCH + c] = (_Float16)(a1 - (float)h1);
+    sQ[(32 + hq) * Q_PITCH + c] = (_Float16)((float)h0 * 0x1p-11f);
+    sQ[(32 + hq + 4) * Q_PITCH + c] = (_Float16)((float)h1 * 0x1p-11f);
+#pragma unroll
+    for (int part = 0; part < 3; ++part) {
+      sQ[(16 * part + 8 + hq) * Q_PITCH + c] = (_Float16)0.f;
+      sQ[(16 * part + 12 + hq) * Q_PITCH + c] = (_Float16)0.f;
+    }
   }
   __syncthreads();
 
@@ -231,11 +279,23 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_split_kernel(
   const int64_t stream = (int64_t)b * Hkv + g;
   constexpr int64_t WSTEP = (int64_t)ATT_WAVES * TILE;
 
-  // B operands of the score product: Qcat[col][32 s + 8 grp + e]
-  half8 qf[2];
+  // B operands of the score product, K-steps 0..5: part s / 2, coordinates
+  // 32 (s % 2) + 8 grp + e, column (head) col
+  half8 qf[AS::EXPAND ? 6 : 1];
+  half4 q16[AS::EXPAND ? 1 : 3][AS::EXPAND ? 1 : 4];   // direct path: [part][K-step of 16]
+  if constexpr (AS::EXPAND) {
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
-    qf[s] = *reinterpret_cast<const half8*>(sQ + col * Q_PITCH + 32 * s + 8 * grp);
+    for (int s = 0; s < 6; ++s)
+      qf[s] = *reinterpret_cast<const half8*>(sQ + (16 * (s >> 1) + col) * Q_PITCH +
+                                              32 * (s & 1) + 8 * grp);
+  } else {
+#pragma unroll
+    for (int part = 0; part < 3; ++part)
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        q16[part][m] = *reinterpret_cast<const half4*>(sQ + (16 * part + col) * Q_PITCH + 16 * m +
+                                                       4 * grp);
+  }
 
   float m_run = NEG_BIG, l_run = 0.f;
   floatx4 oh[4], ol[4];
@@ -245,7 +305,7 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_split_kernel(
     ol[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  auto load = [&](TileRegs<W>& t, int64_t tb) {
+  auto load = [&](TileRegs<W>& t, int64_t tb) __attribute__((always_inline)) {
     const int64_t left = t1 - tb;
     const int cnt = left <= 0 ? 0 : (left < TILE ? (int)left : TILE);
     const int64_t rec0 = stream * T + (left <= 0 ? 0 : tb);
@@ -262,9 +322,15 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_split_kernel(
     t.kn = __builtin_amdgcn_raw_buffer_load_b16(rkn, lane * 2, 0, 0);
     t.vn = __builtin_amdgcn_raw_buffer_load_b16(rvn, lane * 2, 0, 0);
   };
-  auto stage = [&](const TileRegs<W>& t) {
-    unpack_record<K, BITS, W>(t.kw, sKi + lane * IP);
-    unpack_record<K, BITS, W>(t.vw, sVi + lane * IP);
+  auto stage = [&](const TileRegs<W>& t) __attribute__((always_inline)) {
+    if constexpr (AS::EXPAND)
+      unpack_record<K, BITS, W>(t.kw, sKi + lane * IP);
+    else
+      unpack_record_vperm<K, BITS, W>(t.kw, sKi + lane * IP);
+    if constexpr (AS::EXPAND)
+      unpack_record<K, BITS, W>(t.vw, sVi + lane * IP);
+    else
+      unpack_record_vperm<K, BITS, W>(t.vw, sVi + lane * IP);
     sNk[lane] = f16_bits_to_f32((uint16_t)t.kn);
     sNv[lane] = f16_bits_to_f32((uint16_t)t.vn);
     if constexpr (AS::EXPAND) {
@@ -287,33 +353,120 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_split_kernel(
     }
   };
 
-  auto process = [&](int64_t tb) {
-    const int64_t left = t1 - tb;
-    const bool partial = left < TILE;                 // uniform
-    const int valid = partial ? (int)left : TILE;
+  // k = 4, 8: v_mfma_f32_16x16x16_f16 throughout.  Scores: lane (col, grp)
+  // gives A = key row of token 16 sub + col, coordinates 16 m + 4 grp .. + 3
+  // (one codeword row for k = 4, half of one for k = 8; hi and lo from one
+  // interleaved table row).  Values: A = value coordinates 16 mt + col of
+  // tokens 16 sub + 4 grp + 0..3 (transpose reads), B = the lane's own four
+  // weights p * nu of sub-tile sub, so no operand needs repacking.
+  auto process_direct = [&](int64_t tb, auto partial_tag) __attribute__((always_inline)) {
+    constexpr bool PARTIAL = decltype(partial_tag)::value;
+    constexpr int QB = 16 / K;                          // blocks per 16 coordinates
+    const int qs = grp / (4 / QB), cs = (4 * grp) % K;  // score: index slot, offset in row
+    const int qv = (col & 3) / (4 / QB), cv = (4 * (col & 3)) % K;   // value: same
+    float sc[4][4];
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) {
+      const u32x2 ix = *reinterpret_cast<const u32x2*>(sKi + (16 * sub + col) * IP + 4 * qs);
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t wd = m < 2 ? ix.x : ix.y;
+        const uint32_t i = (m & 1) ? (wd >> 16) : (wd & 0xFFFFu);
+        const _Float16* row = sK + i * (2 * K) + cs;
+        const half4 zh = *reinterpret_cast<const half4*>(row);
+        const half4 zl = *reinterpret_cast<const half4*>(row + K);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16f16(zh, q16[0][m], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16f16(zh, q16[1][m], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16f16(zl, q16[2][m], acc, 0, 0, 0);
+      }
+      const float4 nk4 = *reinterpret_cast<const float4*>(sNk + 16 * sub + 4 * grp);
+      sc[sub][0] = acc[0] * nk4.x;
+      sc[sub][1] = acc[1] * nk4.y;
+      sc[sub][2] = acc[2] * nk4.z;
+      sc[sub][3] = acc[3] * nk4.w;
+    }
+    if constexpr (PARTIAL) {
+      const int valid = (int)(t1 - tb);
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (16 * sub + 4 * grp + r >= valid) sc[sub][r] = NEG_BIG;
+    }
+    float mx = NEG_BIG;
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[sub][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) oh[mt] *= alpha;
+    }
+    m_run = m_new;
+    float ps = 0.f;
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) {
+      const float4 nv4 = *reinterpret_cast<const float4*>(sNv + 16 * sub + 4 * grp);
+      const float nvv[4] = {nv4.x, nv4.y, nv4.z, nv4.w};
+      half4 pw, pwl;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = __builtin_amdgcn_exp2f(sc[sub][r] - m_new);
+        ps += p;
+        const float w = p * nvv[r];
+        pw[r] = (_Float16)w;
+        pwl[r] = (_Float16)(w * 0x1p-11f);
+      }
+      // values of tokens 16 sub + 4 grp + 0..3; lane (col, grp) addresses token
+      // 16 sub + 4 grp + col / 4 for the transpose reads
+      const u32x2 ixv = *reinterpret_cast<const u32x2*>(sVi + (16 * sub + 4 * grp + (col >> 2)) * IP +
+                                                        4 * qv);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const uint32_t wd = mt < 2 ? ixv.x : ixv.y;
+        const uint32_t i = (mt & 1) ? (wd >> 16) : (wd & 0xFFFFu);
+        const _Float16* row = sVh + i * (2 * K) + cv;
+        const half4 vh = read_tr(row), vl = read_tr(row + K);
+        oh[mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(vh, pw, oh[mt], 0, 0, 0);
+        oh[mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(vl, pwl, oh[mt], 0, 0, 0);
+      }
+    }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    l_run += ps;
+  };
+
+  auto process = [&](int64_t tb, auto partial_tag) __attribute__((always_inline)) {
+    constexpr bool PARTIAL = decltype(partial_tag)::value;
     // ---- scores for the 4 sub-tiles of 16 tokens (lanes of columns >= G hold
-    //      unused but finite values)
+    //      zeros)
     float sc[4][4];
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub) {
       const uint16_t* ki = sKi + (16 * sub + col) * IP;
-      floatx4 ah = {0.f, 0.f, 0.f, 0.f}, al = {0.f, 0.f, 0.f, 0.f};
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
+      for (int s2 = 0; s2 < 2; ++s2) {
         half8 zh, zl;
-        gather8_hl<K>(ki, sK, sKlo, 32 * s + 8 * grp, zh, zl);
-        ah = __builtin_amdgcn_mfma_f32_16x16x32_f16(zh, qf[s], ah, 0, 0, 0);
-        al = __builtin_amdgcn_mfma_f32_16x16x32_f16(zl, qf[s], al, 0, 0, 0);
+        gather8_hl<K>(ki, sK, sKlo, 32 * s2 + 8 * grp, zh, zl);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(zh, qf[s2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(zh, qf[2 + s2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(zl, qf[4 + s2], acc, 0, 0, 0);
       }
       const float4 nk4 = *reinterpret_cast<const float4*>(sNk + 16 * sub + 4 * grp);
-      const float nk[4] = {nk4.x, nk4.y, nk4.z, nk4.w};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float x = fmaf(al[r], 0x1p-11f, ah[r]);
-        sc[sub][r] = fmaf(rot8(x), 0x1p-11f, x) * nk[r];
-      }
+      sc[sub][0] = acc[0] * nk4.x;
+      sc[sub][1] = acc[1] * nk4.y;
+      sc[sub][2] = acc[2] * nk4.z;
+      sc[sub][3] = acc[3] * nk4.w;
     }
-    if (partial) {
+    if constexpr (PARTIAL) {
+      const int valid = (int)(t1 - tb);
 #pragma unroll
       for (int sub = 0; sub < 4; ++sub)
 #pragma unroll
@@ -361,6 +514,15 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_split_kernel(
     for (int ks = 0; ks < 2; ++ks) {
       const int tok_a = 32 * ks + 4 * grp + (col >> 2);
       const int tok_b = tok_a + 16;
+      // value indices of blocks (16 / K) mt + q for mt = 0..3 (permuted layout)
+      constexpr int QB = 16 / (K < 16 ? K : 16);
+      const int qv = (4 * (col & 3)) / K, cin = (4 * (col & 3)) % K;
+      u32x2 ixa = {0u, 0u}, ixb = {0u, 0u};
+      if constexpr (!AS::EXPAND) {
+        ixa = *reinterpret_cast<const u32x2*>(sVi + tok_a * IP + 4 * qv);
+        ixb = *reinterpret_cast<const u32x2*>(sVi + tok_b * IP + 4 * qv);
+      }
+      (void)QB;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const int c = 16 * mt + 4 * (col & 3);
@@ -371,11 +533,13 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_split_kernel(
           pbh = sZh + tok_b * Z_PITCH + c;
           pbl = sZl + tok_b * Z_PITCH + c;
         } else {
-          const uint32_t ia = sVi[tok_a * IP + c / K], ib = sVi[tok_b * IP + c / K];
-          pah = sVh + ia * K + (c % K);
-          pal = sVl + ia * K + (c % K);
-          pbh = sVh + ib * K + (c % K);
-          pbl = sVl + ib * K + (c % K);
+          const uint32_t wa = (mt < 2) ? ixa.x : ixa.y, wb = (mt < 2) ? ixb.x : ixb.y;
+          const uint32_t ia = (mt & 1) ? (wa >> 16) : (wa & 0xFFFFu);
+          const uint32_t ib = (mt & 1) ? (wb >> 16) : (wb & 0xFFFFu);
+          pah = sVh + ia * K + cin;
+          pal = sVl + ia * K + cin;
+          pbh = sVh + ib * K + cin;
+          pbl = sVl + ib * K + cin;
         }
         const half4 ha = read_tr(pah), hb = read_tr(pbh), la = read_tr(pal), lb = read_tr(pbl);
         const half8 zh = {ha[0], ha[1], ha[2], ha[3], hb[0], hb[1], hb[2], hb[3]};
@@ -386,26 +550,41 @@ __global__ __launch_bounds__(ATT_THREADS) void attend_split_kernel(
     }
   };
 
-  // wave w takes tiles t0 + (w + 4 i) TILE of the workgroup's split
+  // wave w takes tiles t0 + (w + 4 i) TILE of the workgroup's split; four tiles
+  // of records are in flight per wave (HBM latency needs the bytes in flight)
   int64_t tb = t0 + (int64_t)wave * TILE;
   if (tb < t1) {
-    TileRegs<W> ra, rb;
-    load(ra, tb);
-    load(rb, tb + WSTEP);
+    auto run = [&](int64_t t) __attribute__((always_inline)) {
+      if constexpr (AS::EXPAND) {
+        if (t1 - t >= TILE)
+          process(t, std::false_type());
+        else
+          process(t, std::true_type());
+      } else {
+        if (t1 - t >= TILE)
+          process_direct(t, std::false_type());
+        else
+          process_direct(t, std::true_type());
+      }
+    };
+    // Every path through the loop issues the same loads (a tile past the end
+    // is a zero-length buffer read that touches no memory), so the compiler's
+    // load counter stays exact across iterations and the waits stay partial;
+    // only the load-free compute is skipped for such tiles.
+    constexpr int DEPTH = AS::EXPAND ? 2 : 4;
+    TileRegs<W> rr[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) load(rr[d], tb + d * WSTEP);
     for (;;) {
-      stage(ra);
-      wave_lds_sync();
-      load(ra, tb + 2 * WSTEP);
-      process(tb);
-      wave_lds_sync();
-      tb += WSTEP;
-      if (tb >= t1) break;
-      stage(rb);
-      wave_lds_sync();
-      load(rb, tb + 2 * WSTEP);
-      process(tb);
-      wave_lds_sync();
-      tb += WSTEP;
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        stage(rr[d]);
+        wave_lds_sync();
+        load(rr[d], tb + DEPTH * WSTEP);
+        if (tb < t1) run(tb);
+        wave_lds_sync();
+        tb += WSTEP;
+      }
       if (tb >= t1) break;
     }
   }
