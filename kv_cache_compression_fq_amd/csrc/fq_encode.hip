@@ -24,6 +24,9 @@
 //     grid) the block is redone exactly by 16 lanes: z's block in float64 from
 //     x and the float64 Pi, then all N codewords with sum_t (z_t - c_t)^2 in
 //     float64, ties to the lowest index.
+//  For k = 3 the one-coordinate last block is searched on its coordinate
+//  computed exactly in float64 (the codewords' first coordinates are packed
+//  too closely for the float32 certificate to settle most of those blocks).
 //  6. the chunk's indices are packed LSB-first into fixed-size records and
 //     written with coalesced word stores, norms beside them.
 //
@@ -57,8 +60,12 @@ struct EncShape {
   static constexpr int IP = (NB + 2) / 2 * 2;       // u16 per staged index row
   static constexpr int NCOL = EV * NB;              // columns per chunk
   static constexpr int CPL = (NCOL + 63) / 64;      // columns per lane
+  static constexpr bool EXACT_LAST = LAST < K;      // one-coordinate last block
   static constexpr size_t WAVE_BYTES =
-      ((size_t)EV * ZP * 4 + (size_t)EV * IP * 2 + (size_t)NCOL * 2 + 15) / 16 * 16;
+      ((size_t)EV * ZP * 4 + (EXACT_LAST ? EV * 8 : 0) + (size_t)EV * IP * 2 + (size_t)NCOL * 2 +
+       15) / 16 * 16;
+  // workgroup-shared bytes after the search table: the last row of Pi (float64)
+  static constexpr size_t SHARED_EXTRA = EXACT_LAST ? D * 8 : 0;
 };
 
 struct EncArgs {
@@ -320,15 +327,20 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
   _Float16* sRot = reinterpret_cast<_Float16*>(smem);
   float* sEnc = reinterpret_cast<float*>(smem + ROT_BYTES);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  unsigned char* wb = smem + ROT_BYTES + enc_table_bytes(N, S) + wave * Sh::WAVE_BYTES;
+  double* sPiL = reinterpret_cast<double*>(smem + ROT_BYTES + enc_table_bytes(N, S));
+  unsigned char* wb = smem + ROT_BYTES + enc_table_bytes(N, S) + Sh::SHARED_EXTRA +
+                      wave * Sh::WAVE_BYTES;
   float* sZ = reinterpret_cast<float*>(wb);
-  uint16_t* sIdx = reinterpret_cast<uint16_t*>(wb + EV * ZP * 4);
+  double* sZL = reinterpret_cast<double*>(wb + EV * ZP * 4);             // k = 3: exact z_63
+  uint16_t* sIdx = reinterpret_cast<uint16_t*>(wb + EV * ZP * 4 + (Sh::EXACT_LAST ? EV * 8 : 0));
   uint16_t* sFb = sIdx + EV * IP;
 
   for (int i = threadIdx.x; i < ROT_BYTES / 16; i += blockDim.x)
     reinterpret_cast<u32x4*>(sRot)[i] = reinterpret_cast<const u32x4*>(a.rotfrag)[i];
   for (int i = threadIdx.x; i < (N + 1) * S / 4; i += blockDim.x)
     reinterpret_cast<floatx4*>(sEnc)[i] = reinterpret_cast<const floatx4*>(a.enc)[i];
+  if constexpr (Sh::EXACT_LAST)
+    for (int i = threadIdx.x; i < D; i += blockDim.x) sPiL[i] = a.pi64[(D - 1) * D + i];
   __syncthreads();
 
   const TX* __restrict__ x = static_cast<const TX*>(a.x);
@@ -353,6 +365,34 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
     // ---- 1. norm (float64) and the binary16 fragments; next chunk's x in flight
     XFrag<TX> xf;
     finish_x<TX>(xraw, xf);
+    if constexpr (Sh::EXACT_LAST) {
+      // k = 3: the first coordinates of the codewords lie too close together
+      // for the float32 certificate on the one-coordinate last block, so its
+      // coordinate z_63 = <Pi row 63, x> / |x| is taken exactly in float64
+      double ss = 0.0, dt = 0.0;
+#pragma unroll
+      for (int kq = 0; kq < 4; ++kq) {
+        double xv[4];
+        if constexpr (sizeof(TX) == 2) {
+          const half4 h = __builtin_bit_cast(half4, xraw.q[kq]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) xv[e] = (double)(float)h[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) xv[e] = (double)xraw.q[kq][e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ss = fma(xv[e], xv[e], ss);
+          dt = fma(sPiL[16 * kq + 4 * g + e], xv[e], dt);
+        }
+      }
+      ss += shfl_xor_f64(ss, 16);
+      ss += shfl_xor_f64(ss, 32);
+      dt += shfl_xor_f64(dt, 16);
+      dt += shfl_xor_f64(dt, 32);
+      if (g == 0) sZL[j] = dt / sqrt(ss);   // a zero vector gives NaN
+    }
     if (ch + tw < nchunks) load_raw<TX>(row_of(ch + tw), g, xraw);
     // norm within 3.3e-7 relative (pairwise sum, hardware square root): its
     // binary16 rounding differs from that of the exact norm only within that
@@ -432,16 +472,43 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
         record(c, live, v, b, i1, certain);
       }
     }
-    if constexpr (Sh::LAST < K) {
-      ColPrep<K, RW> cp;
+    if constexpr (Sh::EXACT_LAST) {
+      // the last block of vector `lane`: its cell's candidates compared in
+      // float64 on the exact coordinate, increasing indices with a strict
+      // comparison (ties to the lowest index); exact, so no gap test
       const bool live = lane < nv;
       const int v = lane < EV ? lane : 0;
-      prepare_column<K, RW, GRID, true>(cp, sZ + v * ZP + K * (NB - 1), live, a.grid1, a.G1,
-                                        a.g1scale);
-      int i1;
-      bool certain;
-      search_column<K, S, RW, GRID, true>(cp, sEnc, N, a.gv, a.ez, i1, certain);
-      record(NCF + v, live, v, NB - 1, i1, certain);
+      const double z0 = sZL[v];
+      const float zf = (float)z0;
+      const bool inside = live && zf >= -(float)GRID_R && zf < (float)GRID_R;
+      int u = (int)((zf + (float)GRID_R) * a.g1scale);
+      u = u < 0 ? 0 : (u >= a.G1 ? a.G1 - 1 : u);
+      const uint32_t* rp = reinterpret_cast<const uint32_t*>(a.grid1 + (size_t)u * (2 * RW));
+      uint32_t rec[RW];
+#pragma unroll
+      for (int h = 0; h < RW / 4; ++h) {
+        const u32x4 r0 = *reinterpret_cast<const u32x4*>(rp + 4 * h);
+        rec[4 * h] = r0.x;
+        rec[4 * h + 1] = r0.y;
+        rec[4 * h + 2] = r0.z;
+        rec[4 * h + 3] = r0.w;
+      }
+      const uint32_t c0 = rec[0] & 0xFFFFu;
+      const int cnt = (inside && c0 != GRID_OVERFLOW) ? (int)c0 : 0;
+      double best = INFINITY;
+      int bi = 0;
+#pragma unroll
+      for (int e = 1; e < 2 * RW; ++e) {
+        if (__builtin_amdgcn_ballot_w64(e <= cnt) == 0) break;
+        const uint32_t i = (e & 1) ? (rec[e >> 1] >> 16) : (rec[e >> 1] & 0xFFFFu);
+        const double df = z0 + 0.5 * (double)sEnc[i * S];   // c_0 = -e_0 / 2, exact
+        const double dd = df * df;
+        if (e <= cnt && dd < best) {
+          best = dd;
+          bi = (int)i;
+        }
+      }
+      record(NCF + v, live, v, NB - 1, bi, cnt > 0);
     }
     wave_lds_sync();
 
@@ -525,7 +592,8 @@ hipError_t launch_k(const fq_codebook* cb, const TX* x, int64_t n, int64_t ld, u
                     uint16_t* norms, hipStream_t s) {
   using Sh = EncShape<K, BITS>;
   constexpr int WAVES = enc_waves<BITS>();
-  const size_t shm = ROT_BYTES + enc_table_bytes(cb->N, Sh::S) + WAVES * Sh::WAVE_BYTES;
+  const size_t shm =
+      ROT_BYTES + enc_table_bytes(cb->N, Sh::S) + Sh::SHARED_EXTRA + WAVES * Sh::WAVE_BYTES;
   constexpr bool GRID = (K == 2 || K == 3);
   auto kern = encode_kernel<K, BITS, TX, GRID>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
