@@ -549,7 +549,7 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
       }
       double best = INFINITY;
       int bi = 0;
-      for (int i = l16; i < N; i += 16) {
+      auto consider = [&](int i) {
         const float* ee = sEnc + i * S;
         double dd = 0.0;
 #pragma unroll
@@ -562,6 +562,37 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
           best = dd;
           bi = i;
         }
+      };
+      // the exact block lies in its own grid cell, whose list holds every
+      // codeword that can be nearest there: one candidate per lane suffices;
+      // outside the grid (or for an over-full cell) scan the whole codebook
+      int cnt = 0;
+      uint32_t entry = 0;
+      if constexpr (GRID) {
+        const int dims = last ? 1 : K;
+        bool inside = true;
+        int cell = 0, mul = 1;
+        const int G = last ? a.G1 : a.G;
+        const float sc = last ? a.g1scale : a.gscale;
+#pragma unroll
+        for (int t = 0; t < K; ++t)
+          if (t < dims) {
+            const float zf = (float)zd[t];
+            inside = inside && zf >= -(float)GRID_R && zf < (float)GRID_R;
+            int u = (int)((zf + (float)GRID_R) * sc);
+            u = u < 0 ? 0 : (u >= G ? G - 1 : u);
+            cell += u * mul;
+            mul *= G;
+          }
+        const uint16_t* rec = (last ? a.grid1 : a.grid) + (size_t)cell * (2 * RW);
+        const uint32_t c0 = rec[0];
+        cnt = (inside && c0 != GRID_OVERFLOW) ? (int)c0 : 0;
+        entry = l16 + 1 < 2 * RW ? rec[l16 + 1] : 0u;
+      }
+      if (cnt > 0) {
+        if (l16 < cnt) consider((int)entry);
+      } else {
+        for (int i = l16; i < N; i += 16) consider(i);
       }
 #pragma unroll
       for (int m = 8; m >= 1; m >>= 1) {
