@@ -38,8 +38,14 @@ Readings (the pages name the parts but not their formulas):
   MSE per unit vector; [BSQ main table] uses the same scale).  When k does
   not divide d the last block keeps only its first r = d - (nb-1) k
   coordinates and is searched with the first r coordinates of each codeword.
-* The table is rounded to float32; that float32 table is what the artifact
-  stores and what every later oracle step reads.
+* Stored precision (the pages fix how the table is built, not the precision
+  it is kept in).  The Lloyd-Max table is rounded, nearest-even, to values
+  that IEEE binary16 represents exactly, and kept as float32: the artifact
+  stores that table and every later oracle step reads it.  Half-precision
+  copies of the table are then exact, so decoders may gather codewords from
+  binary16 tables without rounding them; the move is at most 2^-12 of each
+  coordinate's size (2^-25 absolute below the binary16 normal range), far
+  below the quantisation error.
 """
 import math
 
@@ -202,11 +208,21 @@ def mc_seeds(d, k, N):
     return [d, k, N], [d, k, N, 1], [d, k, N, 2]
 
 
+def half_grid(C):
+    """Round a table to the nearest binary16 values (ties to even), held as float32."""
+    with np.errstate(over="ignore"):
+        h = np.asarray(C, dtype=np.float64).astype(np.float16)
+    if not np.all(np.isfinite(h)):
+        raise ValueError("codeword outside the binary16 range")
+    return h.astype(np.float32)
+
+
 def build_codebook(d, k, N, restarts=8, samples=1 << 20, test_samples=1 << 20,
                    max_iter=200, tol=1e-9, log=None):
-    """The full offline build: start points, multi-restart Lloyd-Max, float32 rounding.
+    """The full offline build: start points, multi-restart Lloyd-Max, binary16-grid rounding.
 
-    Returns a dict with the float32 table ``C`` and its bookkeeping.
+    Returns a dict with the table ``C`` (float32 holding binary16 values) and its
+    bookkeeping.
     """
     s_train, s_test, s_shift = mc_seeds(d, k, N)
     X = source.sample_blocks(d, k, samples, s_train)
@@ -221,7 +237,7 @@ def build_codebook(d, k, N, restarts=8, samples=1 << 20, test_samples=1 << 20,
         if best is None or hist[-1] < best[1][-1]:
             best = (C, hist, r)
     C, hist, r_best = best
-    C32 = C.astype(np.float32)
+    C32 = half_grid(C)
     T = source.sample_blocks(d, k, test_samples, s_test)
     D_test, e_full, e_part = unit_distortion(C32.astype(np.float64), d, T)
     nb, rr = block_layout(d, k)

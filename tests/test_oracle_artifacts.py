@@ -60,6 +60,26 @@ def test_artifact_rate_and_layout(k, N):
     assert float(np.max(np.linalg.norm(a["C"].astype(np.float64), axis=1))) < 1.0
 
 
+@pytest.mark.parametrize("k,N", VARIANTS)
+def test_artifact_table_is_on_the_binary16_grid(k, N):
+    # the stored table holds binary16 numbers (the reading of the table's
+    # precision), so a binary16 copy of it is exact
+    C = load(k, N)["C"]
+    assert np.array_equal(C.astype(np.float16).astype(np.float32), C)
+    assert np.all(np.isfinite(C))
+
+
+def test_half_grid_rounds_to_nearest_even():
+    # binary16 spacing on [1, 2) is 2^-10: halfway cases go to the even neighbour
+    v = np.array([1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 1 + 2.0 ** -11 + 2.0 ** -30,
+                  -(1 + 2.0 ** -11), 1.0 / 3.0, 2.0 ** -25, 2.0 ** -25 + 2.0 ** -40, 0.0])
+    want = np.array([1.0, 1 + 2.0 ** -9, 1 + 2.0 ** -10, -1.0, 1365 * 2.0 ** -12, 0.0,
+                     2.0 ** -24, 0.0])
+    assert np.array_equal(codebook.half_grid(v).astype(np.float64), want)
+    with pytest.raises(ValueError):
+        codebook.half_grid(np.array([1e6]))
+
+
 @pytest.mark.parametrize("k,N", INTEGER_RATE)
 def test_vector_beats_scalar_at_matched_rate(k, N, scalar_d):
     a = load(k, N)
