@@ -197,6 +197,7 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
     pil[i] = (_Float16)((cb->pi[i] - (double)pih[i]) * 2048.0);
     rho_pi = fmax(rho_pi, fabs(cb->pi[i] - (double)pih[i] - (double)pil[i] / 2048.0));
   }
+  cb->half_exact = true;
   for (int n = 0; n < N; ++n) {
     double cc = 0;
     for (int t = 0; t < k; ++t) {
@@ -204,6 +205,7 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
       enc[(size_t)n * S + t] = (float)(-2.0 * v);
       cc += v * v;
       cbh[(size_t)n * k + t] = (_Float16)v;
+      if ((double)cbh[(size_t)n * k + t] != v) cb->half_exact = false;
       cbl[(size_t)n * k + t] = (_Float16)((v - (double)cbh[(size_t)n * k + t]) * 2048.0);
     }
     enc[(size_t)n * S + k] = (float)cc;
@@ -273,7 +275,8 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
                o_enc = take(4ull * (N + 1) * S), o_cbh = take(2ull * N * k),
                o_cbl = take(2ull * N * k), o_frag = take(2ull * frag.size()),
                o_efrag = take(2ull * efrag.size()),
-               o_grid = take(2ull * grid.rec.size() + 64), o_grid1 = take(2ull * grid1.rec.size() + 64);
+               o_grid = take(2ull * grid.rec.size() + 64), o_grid1 = take(2ull * grid1.rec.size() + 64),
+               o_pih = take(2ull * d * d), o_pil = take(2ull * d * d), o_pit = take(4ull * d * d);
   cb->dev_bytes = off;
   {
     DeviceGuard g(device);
@@ -294,6 +297,9 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
     cb->t.cb16lo = reinterpret_cast<_Float16*>(base + o_cbl);
     cb->t.pifrag = reinterpret_cast<_Float16*>(base + o_frag);
     cb->t.encfrag = reinterpret_cast<_Float16*>(base + o_efrag);
+    cb->t.pi16hi = reinterpret_cast<_Float16*>(base + o_pih);
+    cb->t.pi16lo = reinterpret_cast<_Float16*>(base + o_pil);
+    cb->t.pi32t = reinterpret_cast<float*>(base + o_pit);
     cb->t.grid = grid.rec.empty() ? nullptr : reinterpret_cast<uint16_t*>(base + o_grid);
     cb->t.grid1 = grid1.rec.empty() ? nullptr : reinterpret_cast<uint16_t*>(base + o_grid1);
     std::vector<char> staging(off, 0);
@@ -304,6 +310,11 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
     memcpy(staging.data() + o_cbl, cbl.data(), 2ull * N * k);
     memcpy(staging.data() + o_frag, frag.data(), 2ull * frag.size());
     memcpy(staging.data() + o_efrag, efrag.data(), 2ull * efrag.size());
+    memcpy(staging.data() + o_pih, pih.data(), 2ull * d * d);
+    memcpy(staging.data() + o_pil, pil.data(), 2ull * d * d);
+    for (int i = 0; i < d; ++i)
+      for (int j = 0; j < d; ++j)
+        reinterpret_cast<float*>(staging.data() + o_pit)[(size_t)j * d + i] = pi32[(size_t)i * d + j];
     if (!grid.rec.empty()) memcpy(staging.data() + o_grid, grid.rec.data(), 2ull * grid.rec.size());
     if (!grid1.rec.empty())
       memcpy(staging.data() + o_grid1, grid1.rec.data(), 2ull * grid1.rec.size());

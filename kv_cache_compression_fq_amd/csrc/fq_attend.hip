@@ -56,12 +56,14 @@ struct SplitPlan {
   int64_t chunk;  // tokens per workgroup split, a multiple of ATT_WAVES * TILE
 };
 
-// About 1024 workgroups (4096 waves) over the device; each wave gets at least
-// one tile.  The four waves of a workgroup take interleaved tiles of its split.
-SplitPlan plan_splits(int B, int Hkv, int64_t T) {
+// About `target` workgroups over the device; each wave gets at least one
+// tile.  The four waves of a workgroup take interleaved tiles of its split.
+constexpr int64_t SPLIT_TARGET = 512;          // kernel A: two workgroups per compute unit
+constexpr int64_t SPLIT_TARGET_DIRECT = 768;   // kernel A': three
+SplitPlan plan_splits(int B, int Hkv, int64_t T, int64_t target) {
   constexpr int64_t STEP = (int64_t)ATT_WAVES * TILE;
   const int64_t pairs = (int64_t)B * Hkv;
-  int64_t S = (1024 + pairs - 1) / pairs;
+  int64_t S = (target + pairs - 1) / pairs;
   const int64_t max_s = (T + STEP - 1) / STEP;
   if (S > max_s) S = max_s;
   if (S < 1) S = 1;
@@ -139,7 +141,7 @@ __device__ inline half4 read_tr(const _Float16* p) {
 }
 
 __device__ inline float rot8(float x) {   // value of lane (l +- 8) within its 16-lane row
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, true));
 }
 
 // Value record of one token into LDS with the indices permuted for the value
@@ -625,45 +627,481 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2))
   }
 }
 
-// One workgroup per (batch, query head): log-sum-exp merge of the S split
-// partials, then out = Pi^T o_rot in binary16.
+// One workgroup of 256 per (batch, query head): log-sum-exp merge of the S
+// split partials, then out = Pi^T o_rot in binary16.  Thread (c, part) merges
+// the splits s = part (mod 4) for coordinate c and forms the part's quarter
+// of the rotation; every global load is issued before the first barrier, so
+// the whole merge waits on memory once.
 __global__ __launch_bounds__(256) void attend_merge_kernel(const float* __restrict__ ws, int S,
-                                                           int Hq, const float* __restrict__ pi32,
+                                                           const float* __restrict__ pi32t,
                                                            uint16_t* __restrict__ out) {
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const float* src = ws + ((int64_t)b * Hq + h) * S * PART;
-  __shared__ float sRed[256];
-  __shared__ float sO[4][D];
-  __shared__ float sL[4];
-  float M = NEG_BIG;
-  for (int s = tid; s < S; s += 256) M = fmaxf(M, src[(int64_t)s * PART]);
-  sRed[tid] = M;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) sRed[tid] = fmaxf(sRed[tid], sRed[tid + w]);
-    __syncthreads();
+  const int64_t bh = blockIdx.x;   // b * Hq + h
+  const int c = threadIdx.x & 63, part = threadIdx.x >> 6;
+  float4 pr[4];   // Pi^T row c, entries 16 part .. 16 part + 15
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pr[i] = reinterpret_cast<const float4*>(pi32t + c * D + 16 * part)[i];
+  // the head's partials as a buffer: loads past the end read zero (and are
+  // then masked), so each batch of four splits loads with no branch
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(ws + bh * S * PART), (short)0, S * PART * 4, BUF_DWORD3);
+  float m = NEG_BIG, l = 0.f, o = 0.f;
+  for (int s0 = 0; s0 < S; s0 += 16) {   // online merge of this part's splits
+    float ms[4], ls[4], os[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int s = s0 + part + 4 * k;
+      const uint32_t off = (uint32_t)s * PART * 4;
+      ms[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+      ls[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off + 4, 0, 0));
+      os[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off + 8 + 4 * c, 0, 0));
+      if (s >= S) ms[k] = NEG_BIG;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float mn = fmaxf(m, ms[k]);
+      const float a = __builtin_amdgcn_exp2f(m - mn), w = __builtin_amdgcn_exp2f(ms[k] - mn);
+      l = fmaf(l, a, ls[k] * w);
+      o = fmaf(o, a, os[k] * w);
+      m = mn;
+    }
   }
-  M = sRed[0];
-  const int c = tid & 63, part = tid >> 6;
-  float o = 0.f, Ls = 0.f;
-  for (int s = part; s < S; s += 4) {
-    const float* p = src + (int64_t)s * PART;
-    const float wt = __builtin_amdgcn_exp2f(p[0] - M);   // partials are in log2 units
-    Ls = fmaf(wt, p[1], Ls);
-    o = fmaf(wt, p[2 + c], o);
+  __shared__ float sm[4], sl[4], so[4][D], sd[4][D];
+  if (c == 0) {
+    sm[part] = m;
+    sl[part] = l;
   }
-  sO[part][c] = o;
-  if (c == 0) sL[part] = Ls;
+  so[part][c] = o;
   __syncthreads();
-  if (tid < D) {
-    const float Lt = sL[0] + sL[1] + sL[2] + sL[3];
-    sRed[tid] = (sO[0][tid] + sO[1][tid] + sO[2][tid] + sO[3][tid]) / Lt;
+  const float M = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+  float L = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) L = fmaf(sl[q], __builtin_amdgcn_exp2f(sm[q] - M), L);
+  // this thread's quarter of the rotation: coordinates j = 16 part .. + 15
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = 16 * part + 4 * i + e;
+      float oj = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) oj = fmaf(so[q][j], __builtin_amdgcn_exp2f(sm[q] - M), oj);
+      acc = fmaf(pr[i][e], oj, acc);
+    }
+  }
+  sd[part][c] = acc;
+  __syncthreads();
+  if (part == 0)
+    out[bh * D + c] = f32_to_f16_rne((sd[0][c] + sd[1][c] + sd[2][c] + sd[3][c]) / L);
+}
+
+// ---------------------------------------------------------------------------
+// Kernel A', used when both codebooks hold binary16-exact values (binary16
+// tables then lose nothing), k = 4 or 8, and T is a multiple of 8 (every norm
+// row 16-byte aligned).  Per wave and 64-token tile:
+//  * four loads, each one contiguous span: key records and value records (a
+//    record per lane, lanes permuted), key and value norms (8 tokens per lane);
+//  * a record's 64 coordinates split into four quarters of 16 (16 / k whole
+//    blocks); quarters are redistributed in registers -- a 4 x 4 transpose
+//    across the wave's 16-lane rows (permlane swaps) for keys, within lane
+//    quads (DPP) for values -- so no index goes through LDS and the token
+//    loop has no barrier;
+//  * scores on v_mfma_f32_16x16x32_f16, tokens as rows: row i of sub-tile s
+//    is token 16 (i / 4) + 4 s + i % 4, and lane (col, grp) supplies quarter
+//    grp of its row's token; the B operand holds the query hi parts of the
+//    group's heads in columns 0..7 and their lo parts (q - hi, binary16) in
+//    columns 8..15, so score = D[., h] + D[., h + 8] (one row rotation);
+//  * the softmax runs on distinct work per lane: lane (col, grp) takes head
+//    col % 8 and tokens 16 grp + 8 (col / 8) + 0..7;
+//  * values O^T = Z^T P'^T on the same instruction, P' = p nu_v in binary16:
+//    K-step ks covers tokens 16 grp + 8 ks + 0..7, its A operand comes from
+//    transpose reads of 4-coordinate codeword pieces (output row i of slice
+//    mt is coordinate 16 (i / 4) + 4 mt + i % 4) and its B operand holds the
+//    weights of lane (col % 8) + 8 ks of the row; columns 8..15 of the
+//    product are not used.
+template <int K, int BITS>
+struct DirectCfg {
+  static constexpr int W = Shape<K, BITS>::W;
+  static constexpr int QB = 16 / K;              // blocks in a quarter
+  static constexpr int QBITS = QB * BITS;        // bits in a quarter
+  static constexpr uint32_t MASK = (1u << BITS) - 1u;
+  static_assert(K == 4 || K == 8, "direct kernel: k = 4 or 8");
+  static_assert(QBITS * 4 == W * 32, "four quarters fill the record");
+  static_assert(W == 1 || W == 2 || W == 4, "record of 1, 2 or 4 words");
+};
+
+template <int W>
+struct DTile {
+  uint32_t k[W];   // key record of token 16 (col / 4) + 4 grp + col % 4
+  uint32_t v[W];   // value record of token 16 grp + 4 (col % 4) + col / 4
+  u32x4 nk;        // key norms of tokens 16 grp + 8 (col / 8) + 0..7
+  u32x4 nv;        // value norms of the same tokens
+};
+
+template <int K, int BITS>
+struct DirectLds {
+  // at least 16 bytes per thread, so that every thread stores its table load
+  static constexpr int TABLE = (1 << BITS) * K * 2 > ATT_THREADS * 16 ? (1 << BITS) * K * 2
+                                                                       : ATT_THREADS * 16;
+  static constexpr int QOFF = 2 * TABLE;                       // query operand rows
+  static constexpr int MOFF = QOFF + 16 * Q_PITCH * 2;         // wave partials
+  static constexpr int TOTAL = MOFF + ATT_WAVES * MAX_G * MERGE_PITCH * 4;
+};
+
+// The four quarters of a record, each in the low bits of a word.
+template <int K, int BITS, int W>
+__device__ inline void quarters(const uint32_t (&w)[W], uint32_t (&q)[4]) {
+  constexpr int QBITS = DirectCfg<K, BITS>::QBITS;
+  if constexpr (W == 4) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) q[j] = w[j];
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int pos = j * QBITS;
+      q[j] = (w[pos >> 5] >> (pos & 31)) & ((1u << QBITS) - 1u);
+    }
+  }
+}
+
+// 4 x 4 transpose across the four 16-lane rows: on return, register c of the
+// lane in row r holds what register r of the same column's lane in row c held.
+__device__ inline void transpose_rows(uint32_t (&x)[4]) {
+  auto s02 = __builtin_amdgcn_permlane32_swap(x[0], x[2], false, false);
+  auto s13 = __builtin_amdgcn_permlane32_swap(x[1], x[3], false, false);
+  auto s01 = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
+  auto s23 = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
+  x[0] = s01[0];
+  x[1] = s01[1];
+  x[2] = s23[0];
+  x[3] = s23[1];
+}
+
+// 4 x 4 transpose within each quad of lanes: on return, register j of quad
+// lane q holds what register q of quad lane j held.
+__device__ inline void transpose_quads(uint32_t (&x)[4], int lane) {
+  const bool b0 = lane & 1, b1 = lane & 2;
+  // exchange across lane bit 0 / register bit 0
+#pragma unroll
+  for (int p = 0; p < 4; p += 2) {
+    const uint32_t send = b0 ? x[p] : x[p + 1];
+    const uint32_t got = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+    if (b0) x[p] = got; else x[p + 1] = got;
+  }
+  // exchange across lane bit 1 / register bit 1
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const uint32_t send = b1 ? x[p] : x[p + 2];
+    const uint32_t got = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
+    if (b1) x[p] = got; else x[p + 2] = got;
+  }
+}
+
+__device__ inline uint32_t rot8u(uint32_t x) {   // value of lane (l +- 8) within its 16-lane row
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, true);
+}
+
+// Reductions over the four 16-lane rows of the wave (lanes l, l + 16, l + 32,
+// l + 48), on permlane swaps: no LDS round trip.
+__device__ inline float rows_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ inline float rows_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+__device__ inline float half_at(const u32x4& v, int i) {   // binary16 number i of 8
+  const uint32_t w = v[i >> 1];
+  return f16_bits_to_f32((uint16_t)((i & 1) ? (w >> 16) : (w & 0xFFFFu)));
+}
+
+template <int K, int BITS>
+__global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(3))) void attend_direct_kernel(
+    const uint16_t* __restrict__ q, const uint32_t* __restrict__ kc,
+    const uint16_t* __restrict__ kn, const uint32_t* __restrict__ vc,
+    const uint16_t* __restrict__ vn, int Hq, int Hkv, int64_t T, int64_t chunk, int S,
+    float scale, const _Float16* __restrict__ pih_g, const _Float16* __restrict__ pil_g,
+    const _Float16* __restrict__ kh_g, const _Float16* __restrict__ vh_g, int N,
+    float* __restrict__ ws) {
+  using C = DirectCfg<K, BITS>;
+  using L = DirectLds<K, BITS>;
+  constexpr int W = C::W;
+  const int G = Hq / Hkv;
+  const int sw = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  const int half = col >> 3;   // which 8 tokens of the row's 16 the lane's softmax takes
+
+  // static layout, so that table offsets fold into the LDS instructions
+  __shared__ __align__(16) unsigned char smem[L::TOTAL];
+  _Float16* sK = reinterpret_cast<_Float16*>(smem);                 // [N][K]
+  _Float16* sV = reinterpret_cast<_Float16*>(smem + L::TABLE);      // [N][K]
+  _Float16* sQ = reinterpret_cast<_Float16*>(smem + L::QOFF);       // [16][Q_PITCH]
+  float* sMerge = reinterpret_cast<float*>(smem + L::MOFF);         // [wave][h][pitch]
+
+  const int64_t t0 = (int64_t)sw * chunk;
+  const int64_t t1 = t0 + chunk < T ? t0 + chunk : T;
+  const uint32_t ntok = (uint32_t)(t1 - t0);
+  const int64_t rec0 = ((int64_t)b * Hkv + g) * T + t0;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(kc + rec0 * W), (short)0, (int)(ntok * W * 4), BUF_DWORD3);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(vc + rec0 * W), (short)0, (int)(ntok * W * 4), BUF_DWORD3);
+  const __amdgpu_buffer_rsrc_t rkn = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(kn + rec0), (short)0, (int)(ntok * 2), BUF_DWORD3);
+  const __amdgpu_buffer_rsrc_t rvn = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(vn + rec0), (short)0, (int)(ntok * 2), BUF_DWORD3);
+
+  // Every tile load is unconditional: a tile past the split's end reads
+  // nothing (out of the buffer range) and yields zeros.
+  const uint32_t tok_k = 16 * (col >> 2) + 4 * grp + (col & 3);
+  const uint32_t tok_v = 16 * grp + 4 * (col & 3) + (col >> 2);
+  const uint32_t tok_n = 16 * grp + 8 * half;
+  auto load = [&](DTile<W>& t, uint32_t rel) __attribute__((always_inline)) {
+    if constexpr (W == 4) {
+      const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rk, (rel + tok_k) * 16, 0, 0);
+      const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(rv, (rel + tok_v) * 16, 0, 0);
+      t.k[0] = a.x; t.k[1] = a.y; t.k[2] = a.z; t.k[3] = a.w;
+      t.v[0] = c.x; t.v[1] = c.y; t.v[2] = c.z; t.v[3] = c.w;
+    } else if constexpr (W == 2) {
+      const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(rk, (rel + tok_k) * 8, 0, 0);
+      const u32x2 c = __builtin_amdgcn_raw_buffer_load_b64(rv, (rel + tok_v) * 8, 0, 0);
+      t.k[0] = a.x; t.k[1] = a.y;
+      t.v[0] = c.x; t.v[1] = c.y;
+    } else {
+      t.k[0] = __builtin_amdgcn_raw_buffer_load_b32(rk, (rel + tok_k) * 4, 0, 0);
+      t.v[0] = __builtin_amdgcn_raw_buffer_load_b32(rv, (rel + tok_v) * 4, 0, 0);
+    }
+    t.nk = __builtin_amdgcn_raw_buffer_load_b128(rkn, (rel + tok_n) * 2, 0, 0);
+    t.nv = __builtin_amdgcn_raw_buffer_load_b128(rvn, (rel + tok_n) * 2, 0, 0);
+    // one group per tile, in the same order everywhere: the load counter
+    // waits are static, so a reordered group would make every wait in the
+    // loop drain later tiles too
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // ---- prologue loads first (tables, query and rotation fragments), then
+  //      the first tiles, so the tile loads fly while the prologue computes
+  const int tbytes = N * K * 2;
+  const __amdgpu_buffer_rsrc_t rkt = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<_Float16*>(kh_g), (short)0, tbytes, BUF_DWORD3);
+  const __amdgpu_buffer_rsrc_t rvt = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<_Float16*>(vh_g), (short)0, tbytes, BUF_DWORD3);
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(q + ((int64_t)b * Hq + (int64_t)g * G) * D), (short)0, G * D * 2,
+      BUF_DWORD3);
+  const u32x4 kt4 = __builtin_amdgcn_raw_buffer_load_b128(rkt, threadIdx.x * 16, 0, 0);
+  const u32x4 vt4 = __builtin_amdgcn_raw_buffer_load_b128(rvt, threadIdx.x * 16, 0, 0);
+  // rotation on v_mfma_f32_16x16x32_f16: wave w forms rotated coordinates
+  // 16 w .. 16 w + 15 of every head, qrot[h][n] = sum_k q[h][k] Pi[n][k], with
+  // Pi = hi + 2^-11 lo (both binary16): A = query rows (heads), B = Pi rows
+  half8 qa[2], ph[2], pl[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    qa[s] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(
+                                          rq, (col * D + 32 * s + 8 * grp) * 2, 0, 0));
+    ph[s] = *reinterpret_cast<const half8*>(pih_g + (16 * wave + col) * D + 32 * s + 8 * grp);
+    pl[s] = *reinterpret_cast<const half8*>(pil_g + (16 * wave + col) * D + 32 * s + 8 * grp);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  constexpr int DEPTH = 4;
+  constexpr uint32_t WSTEP = ATT_WAVES * TILE;
+  uint32_t rel = (uint32_t)wave * TILE;
+  DTile<W> rr[DEPTH];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) load(rr[d], rel + d * WSTEP);
+
+  // tables (zeros past the end: out-of-range loads)
+  *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(sK) + threadIdx.x * 16) = kt4;
+  *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(sV) + threadIdx.x * 16) = vt4;
+  {
+    floatx4 ah = {0.f, 0.f, 0.f, 0.f}, al = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      ah = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[s], ph[s], ah, 0, 0, 0);
+      al = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[s], pl[s], al, 0, 0, 0);
+    }
+    // lane (col, grp) holds heads 4 grp + r, coordinate 16 wave + col; row h
+    // = binary16 part of head h, row 8 + h = the rest (log2 units)
+    if (grp < 2) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float a = fmaf(al[r], 0x1p-11f, ah[r]) * (scale * 1.4426950408889634f);
+        const _Float16 h = (_Float16)a;
+        sQ[(4 * grp + r) * Q_PITCH + 16 * wave + col] = h;
+        sQ[(8 + 4 * grp + r) * Q_PITCH + 16 * wave + col] = (_Float16)(a - (float)h);
+      }
+    }
   }
   __syncthreads();
-  if (tid < D) {
-    float a = 0.f;
-    for (int j = 0; j < D; ++j) a = fmaf(pi32[j * D + tid], sRed[j], a);
-    out[((int64_t)b * Hq + h) * D + tid] = f32_to_f16_rne(a);
+  // B operands of the scores, K-step s2: coordinates 16 grp + 8 s2 + 0..7
+  half8 qb[2];
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+    qb[s2] = *reinterpret_cast<const half8*>(sQ + col * Q_PITCH + 16 * grp + 8 * s2);
+
+  float m_run = NEG_BIG, l_run = 0.f;
+  floatx4 oacc[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) oacc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  auto process = [&](const DTile<W>& t, uint32_t tr) __attribute__((always_inline)) {
+    uint32_t kq[4], vq[4];
+    quarters<K, BITS, W>(t.k, kq);
+    quarters<K, BITS, W>(t.v, vq);
+    transpose_rows(kq);        // register s: quarter grp of row col's token in sub-tile s
+    transpose_quads(vq, lane);   // register j: quarter col % 4 of token 16 grp + 4 j + col / 4
+    // ---- scores: raw[4 s + r] = D[4 grp + r][col] of sub-tile s = token 16 grp + 4 s + r
+    float raw[16];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t w = kq[s];
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        half8 a;
+        if constexpr (K == 4) {
+          const uint32_t i0 = (w >> (2 * s2 * BITS)) & C::MASK;
+          const uint32_t i1 = (w >> ((2 * s2 + 1) * BITS)) & C::MASK;
+          const half4 c0 = *reinterpret_cast<const half4*>(sK + i0 * 4);
+          const half4 c1 = *reinterpret_cast<const half4*>(sK + i1 * 4);
+          a = half8{c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+        } else {
+          const uint32_t i0 = (w >> (s2 * BITS)) & C::MASK;
+          a = *reinterpret_cast<const half8*>(sK + i0 * 8);
+        }
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[s2], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) raw[4 * s + r] = acc[r];
+    }
+    // hi + lo columns, then this lane's 8 tokens 16 grp + 8 half + i
+    float sc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float a0 = raw[i] + rot8(raw[i]), a1 = raw[8 + i] + rot8(raw[8 + i]);
+      sc[i] = (half ? a1 : a0) * half_at(t.nk, i);
+    }
+    const uint32_t valid = ntok - tr;
+    if (valid < (uint32_t)TILE) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (tok_n + (uint32_t)i >= valid) sc[i] = NEG_BIG;
+    }
+    // ---- online softmax over the row's 16 tokens x 4 rows (lane pair col,
+    //      col + 8 shares head col % 8)
+    float mx = sc[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
+    mx = rows_max(fmaxf(mx, rot8(mx)));
+    const float m_new = fmaxf(m_run, mx);
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) oacc[mt] *= alpha;
+    }
+    m_run = m_new;
+    float ps = 0.f;
+    half8 own;
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(sc[i] - m_new);
+      const float p1 = __builtin_amdgcn_exp2f(sc[i + 1] - m_new);
+      ps += p0 + p1;
+      // P' = p nu_v: p rounded to binary16, times the binary16 norm pair
+      typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+      const uint32_t nw = t.nv[i >> 1];
+      const half2_t nv2 = {__builtin_bit_cast(_Float16, (uint16_t)(nw & 0xFFFFu)),
+                           __builtin_bit_cast(_Float16, (uint16_t)(nw >> 16))};
+      const half2_t pp = {(_Float16)p0, (_Float16)p1};
+      const half2_t w = pp * nv2;
+      own[i] = w[0];
+      own[i + 1] = w[1];
+    }
+    l_run += rows_sum(ps + rot8(ps));
+    // K-step 0 takes this lane's weights, K-step 1 those of lane col + 8
+    half8 pb[2];
+    pb[0] = own;
+    {
+      const u32x4 ow = __builtin_bit_cast(u32x4, own);
+      const u32x4 ot = {rot8u(ow.x), rot8u(ow.y), rot8u(ow.z), rot8u(ow.w)};
+      pb[1] = __builtin_bit_cast(half8, ot);
+    }
+    // ---- values, K-step ks: transpose reads j = 2 ks, 2 ks + 1; slot (grp,
+    //      e) is token 16 grp + 8 ks + e
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint32_t wa = vq[2 * ks], wb = vq[2 * ks + 1];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const _Float16 *pa, *pbp;
+        if constexpr (K == 4) {
+          pa = sV + ((wa >> (mt * BITS)) & C::MASK) * 4;
+          pbp = sV + ((wb >> (mt * BITS)) & C::MASK) * 4;
+        } else {
+          pa = sV + ((wa >> ((mt >> 1) * BITS)) & C::MASK) * 8 + 4 * (mt & 1);
+          pbp = sV + ((wb >> ((mt >> 1) * BITS)) & C::MASK) * 8 + 4 * (mt & 1);
+        }
+        const half4 ha = read_tr(pa), hb = read_tr(pbp);
+        const half8 a = {ha[0], ha[1], ha[2], ha[3], hb[0], hb[1], hb[2], hb[3]};
+        oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb[ks], oacc[mt], 0, 0, 0);
+      }
+    }
+  };
+
+  if (rel < ntok) {
+    for (;;) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        if (rel < ntok) process(rr[d], rel);
+        load(rr[d], rel + DEPTH * WSTEP);
+        rel += WSTEP;
+      }
+      if (rel >= ntok) break;
+    }
+  }
+
+  // ---- merge the four waves' partials (lanes col < G hold head col,
+  //      coordinates 16 grp + 4 mt + r), write one partial per head
+  if (col < G) {
+    float* mine = sMerge + (wave * MAX_G + col) * MERGE_PITCH;
+    if (grp == 0) {
+      mine[0] = m_run;
+      mine[1] = l_run;
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mine[2 + 16 * grp + 4 * mt + r] = oacc[mt][r];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < G * D; e += ATT_THREADS) {
+    const int h = e / D, c = e % D;
+    float M = NEG_BIG;
+#pragma unroll
+    for (int w = 0; w < ATT_WAVES; ++w) M = fmaxf(M, sMerge[(w * MAX_G + h) * MERGE_PITCH]);
+    float Ls = 0.f, o = 0.f;
+#pragma unroll
+    for (int w = 0; w < ATT_WAVES; ++w) {
+      const float* pw = sMerge + (w * MAX_G + h) * MERGE_PITCH;
+      const float wt = pw[1] > 0.f ? __builtin_amdgcn_exp2f(pw[0] - M) : 0.f;
+      Ls = fmaf(wt, pw[1], Ls);
+      o = fmaf(wt, pw[2 + c], o);
+    }
+    float* dst = ws + (((int64_t)b * Hq + (int64_t)g * G + h) * S + sw) * PART;
+    if (c == 0) {
+      dst[0] = M;
+      dst[1] = Ls;
+    }
+    dst[2 + c] = o;
   }
 }
 
@@ -676,20 +1114,35 @@ template <int K, int BITS>
 hipError_t launch_v(const fq_codebook* ck, const fq_codebook* cv, const uint16_t* q,
                     const uint32_t* kc, const uint16_t* kn, const uint32_t* vc,
                     const uint16_t* vn, int B, int Hq, int Hkv, int64_t T, float scale,
-                    float* ws, uint16_t* out, hipStream_t s) {
-  const SplitPlan p = plan_splits(B, Hkv, T);
+                    void* workspace, uint16_t* out, hipStream_t s) {
+  float* ws = static_cast<float*>(workspace);
+  hipError_t e;
+  if constexpr (K == 4 || K == 8) {
+    if (ck->half_exact && cv->half_exact && T % 8 == 0) {
+      const SplitPlan p = plan_splits(B, Hkv, T, SPLIT_TARGET_DIRECT);
+      auto kern = attend_direct_kernel<K, BITS>;
+      hipLaunchKernelGGL(kern, dim3((unsigned)p.S, Hkv, B), dim3(ATT_THREADS), 0, s, q, kc, kn, vc,
+                         vn, Hq, Hkv, T, p.chunk, p.S, scale, ck->t.pi16hi, ck->t.pi16lo,
+                         ck->t.cb16hi, cv->t.cb16hi, ck->N, ws);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(attend_merge_kernel, dim3(Hq * B), dim3(256), 0, s, ws, p.S, ck->t.pi32t,
+                         out);
+      return hipGetLastError();
+    }
+  }
+  const SplitPlan p = plan_splits(B, Hkv, T, SPLIT_TARGET);
   const size_t shm = attend_lds_bytes<K, BITS>(ck->N);
   auto kern = attend_split_kernel<K, BITS>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)p.S, Hkv, B), dim3(ATT_THREADS), shm, s, q, kc, kn, vc, vn, Hq,
                      Hkv, T, p.chunk, p.S, scale, ck->t.pi32, ck->t.cb16hi, ck->t.cb16lo,
                      cv->t.cb16hi, cv->t.cb16lo, ck->N, ws);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attend_merge_kernel, dim3(Hq, B), dim3(256), 0, s, ws, p.S, Hq, ck->t.pi32,
-                     out);
+  hipLaunchKernelGGL(attend_merge_kernel, dim3(Hq * B), dim3(256), 0, s, ws, p.S, ck->t.pi32t, out);
   return hipGetLastError();
 }
 
@@ -704,18 +1157,19 @@ bool attend_supported(const fq_codebook* cb) {
 }
 
 size_t attend_workspace_bytes(const fq_codebook* /*cb_k*/, int B, int Hq, int Hkv, int64_t T) {
-  const SplitPlan p = plan_splits(B, Hkv, T);
-  return ((size_t)B * Hq * p.S * PART * sizeof(float) + 255) / 256 * 256;
+  // room for either kernel's partials
+  const SplitPlan p = plan_splits(B, Hkv, T, SPLIT_TARGET), pd = plan_splits(B, Hkv, T, SPLIT_TARGET_DIRECT);
+  const int S = p.S > pd.S ? p.S : pd.S;
+  return ((size_t)B * Hq * S * PART * sizeof(float) + 255) / 256 * 256;
 }
 
 hipError_t launch_attend(const fq_codebook* ck, const fq_codebook* cv, const uint16_t* q,
                          const uint32_t* kc, const uint16_t* kn, const uint32_t* vc,
                          const uint16_t* vn, int B, int Hq, int Hkv, int64_t T, float scale,
                          void* ws, uint16_t* out, hipStream_t s) {
-  float* w = static_cast<float*>(ws);
 #define FQ_ATT(KK, BB)                                                                           \
   if (ck->k == KK && ck->bits == BB)                                                             \
-    return launch_v<KK, BB>(ck, cv, q, kc, kn, vc, vn, B, Hq, Hkv, T, scale, w, out, s);
+    return launch_v<KK, BB>(ck, cv, q, kc, kn, vc, vn, B, Hq, Hkv, T, scale, ws, out, s);
   FQ_VARIANTS(FQ_ATT)
 #undef FQ_ATT
   return hipErrorInvalidValue;

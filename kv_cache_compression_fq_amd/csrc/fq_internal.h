@@ -31,10 +31,13 @@ inline bool variant_supported(int k, int bits) {
 struct DeviceTables {
   double* pi64;      // [64][64] Pi, row-major (z = Pi u)
   float* pi32;       // [64][64] Pi rounded to float32
+  float* pi32t;      // [64][64] Pi^T rounded to float32
   float* enc;        // [N + 1][S] search table: -2 c_0 .. -2 c_{k-1}, |c|^2, zero pad; S =
                      // enc_stride; row N is a sentinel (zero codeword, infinite norm)
   _Float16* cb16hi;  // [N][k]   codewords rounded to binary16
   _Float16* cb16lo;  // [N][k]   (c - hi) * 2^11 rounded to binary16
+  _Float16* pi16hi;  // [64][64] Pi rounded to binary16, row-major
+  _Float16* pi16lo;  // [64][64] (Pi - hi) * 2^11 rounded to binary16
   _Float16* pifrag;  // Pi as v_mfma_f32_16x16x32_f16 B fragments (decode), see fq_api.hip
   _Float16* encfrag; // Pi hi / lo as v_mfma_f32_16x16x16_f16 A fragments (encode)
   uint16_t* grid;     // k = 2, 3: candidate records of the block grid (fq_grid.cpp)
@@ -74,6 +77,7 @@ struct fq_codebook {
   float enc_ez32;   // the same for float32 input
   int grid_G;       // cells per dimension of the block grid (0: no grid, full scan)
   int grid1_G;      // cells of the last-block grid (k = 3)
+  bool half_exact;  // every codeword coordinate is a binary16 number
   std::vector<double> pi;  // host copy of Pi
   std::vector<float> c;    // host copy of C
   void* dev_block;         // the single device allocation

@@ -169,7 +169,15 @@ def test_random_access_decode(dev):
 
 # ---------------------------------------------------------------- attention
 ATT_CASES = [
-    # (B, Hq, Hkv, T, codebook shared by K and V)
+    # (B, Hq, Hkv, T, codebook shared by K and V); k = 4, 8 with T a multiple
+    # of 8 take the transposed-quarter kernel, the rest the staged-index one
+    (2, 8, 1, 1000, (4, 256)),
+    (3, 24, 3, 1048, (4, 256)),
+    (1, 8, 1, 64, (4, 256)),
+    (1, 16, 2, 2056, (8, 256)),
+    (1, 1, 1, 8, (8, 256)),
+    (2, 4, 1, 512, (8, 16)),
+    (1, 3, 3, 264, (4, 4)),
     (1, 4, 1, 1, (4, 256)),
     (2, 8, 1, 300, (4, 256)),
     (2, 32, 4, 1000, (2, 16)),
