@@ -986,8 +986,11 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(3))
     float sc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float a0 = raw[i] + rot8(raw[i]), a1 = raw[8 + i] + rot8(raw[8 + i]);
-      sc[i] = (half ? a1 : a0) * half_at(t.nk, i);
+      // the lane's own sub-tile value plus the partner lane's part of it
+      const float own = half ? raw[8 + i] : raw[i], give = half ? raw[i] : raw[8 + i];
+      const uint32_t nw = t.nk[i >> 1];
+      const _Float16 nu = __builtin_bit_cast(_Float16, (uint16_t)((i & 1) ? (nw >> 16) : (nw & 0xFFFFu)));
+      sc[i] = __builtin_fmaf(own + rot8(give), (float)nu, 0.f);
     }
     const uint32_t valid = ntok - tr;
     if (valid < (uint32_t)TILE) {
