@@ -3,8 +3,11 @@
 //
 // One wave encodes a chunk of 16 vectors at a time:
 //
-//  1. norm: nu = |x|_2 in float64 from the exact input values; the stored
-//     norm is nu rounded once to binary16.
+//  1. norm: nu = |x|_2 from a pairwise float32 sum of squares (of the input
+//     scaled by a power of two) and the hardware square root, within
+//     3.3e-7 relative of the exact norm; the stored norm is that value
+//     rounded to binary16, the rounding of the exact norm except within that
+//     distance of a rounding midpoint.
 //  2. rotation on the matrix cores: Pi = Pi_hi + 2^-11 Pi_lo (both binary16),
 //     y = Pi_hi x + 2^-11 Pi_lo x with v_mfma_f32_16x16x16_f16 (binary16 input
 //     is exact; float32 input is scaled by a power of two and split the same
@@ -362,7 +365,7 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
     const int64_t base = ch * EV;
     const int nv = (int)((a.n - base) < EV ? (a.n - base) : EV);
 
-    // ---- 1. norm (float64) and the binary16 fragments; next chunk's x in flight
+    // ---- 1. norm (float32) and the binary16 fragments; next chunk's x in flight
     XFrag<TX> xf;
     finish_x<TX>(xraw, xf);
     if constexpr (Sh::EXACT_LAST) {
