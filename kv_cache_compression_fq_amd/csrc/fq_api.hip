@@ -250,12 +250,12 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
                 part == 0 ? pih[src] : pil[src];
           }
 
-  // candidate grids for the block search (k = 2, 3)
+  // candidate grids for the block search (k = 2, 3, and 4 with N >= 64)
   fq::GridTable grid, grid1;
   cb->grid_G = 0;
   cb->grid1_G = 0;
-  if (k == 2 || k == 3) {
-    const int G = (k == 2) ? (N <= 64 ? 32 : 64) : (N <= 512 ? 32 : 64);
+  if (k == 2 || k == 3 || (k == 4 && N >= 64)) {
+    const int G = (k == 2) ? (N <= 64 ? 32 : 64) : (k == 3 ? (N <= 512 ? 32 : 64) : 14);
     fq::build_grid(cb->c.data(), N, k, k, G, fq::GRID_R, fq::grid_record_entries(k), (uint16_t)N, &grid);
     cb->grid_G = G;
     if (cb->last < k) {

@@ -567,10 +567,10 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
         }
       };
       // the exact block lies in its own grid cell, whose list holds every
-      // codeword that can be nearest there: one candidate per lane suffices;
+      // codeword that can be nearest there: each lane takes every 16th one;
       // outside the grid (or for an over-full cell) scan the whole codebook
       int cnt = 0;
-      uint32_t entry = 0;
+      const uint16_t* rec = nullptr;
       if constexpr (GRID) {
         const int dims = last ? 1 : K;
         bool inside = true;
@@ -587,13 +587,12 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
             cell += u * mul;
             mul *= G;
           }
-        const uint16_t* rec = (last ? a.grid1 : a.grid) + (size_t)cell * (2 * RW);
+        rec = (last ? a.grid1 : a.grid) + (size_t)cell * (2 * RW);
         const uint32_t c0 = rec[0];
         cnt = (inside && c0 != GRID_OVERFLOW) ? (int)c0 : 0;
-        entry = l16 + 1 < 2 * RW ? rec[l16 + 1] : 0u;
       }
       if (cnt > 0) {
-        if (l16 < cnt) consider((int)entry);
+        for (int e = l16; e < cnt; e += 16) consider((int)rec[e + 1]);
       } else {
         for (int i = l16; i < N; i += 16) consider(i);
       }
@@ -628,7 +627,9 @@ hipError_t launch_k(const fq_codebook* cb, const TX* x, int64_t n, int64_t ld, u
   constexpr int WAVES = enc_waves<BITS>();
   const size_t shm =
       ROT_BYTES + enc_table_bytes(cb->N, Sh::S) + Sh::SHARED_EXTRA + WAVES * Sh::WAVE_BYTES;
-  constexpr bool GRID = (K == 2 || K == 3);
+  // candidate lists for k = 2, 3 and for k = 4 with N >= 64 (see the codebook
+  // load); full scans otherwise
+  constexpr bool GRID = (K == 2 || K == 3 || (K == 4 && BITS >= 6));
   auto kern = encode_kernel<K, BITS, TX, GRID>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);

@@ -2,8 +2,8 @@
 //
 // The encoder's block search is an exact nearest-codeword problem (FibQuant
 // technical summary, section 2.3: each block goes to its nearest codeword).
-// For block sizes k = 2 and 3 the blocks live in a low-dimensional ball, so the
-// search can be cut down without changing a single index: cover [-R, R]^dims
+// For block sizes k = 2, 3 and 4 the blocks live in a low-dimensional ball, so
+// the search can be cut down without changing a single index: cover [-R, R]^dims
 // with a uniform grid and give every cell the list of codewords that can be
 // nearest to *some* point of the cell (widened by a margin that covers the
 // encoder's rotation error and float32 cell arithmetic).  A point's nearest
@@ -74,8 +74,8 @@ void build_grid(const float* cw, int N, int k, int dims, int G, double R, int re
   const int max_rings = dims < 3 ? (int)ceil(GRID_REACH / h) : std::max(6, (int)ceil(0.5 * GRID_REACH / h));
   std::vector<int> cand, kept;
   std::vector<std::pair<double, int>> order;
-  int u[3] = {0, 0, 0};
-  double lo[3], hi[3];
+  int u[4] = {0, 0, 0, 0};
+  double lo[4], hi[4];
   auto dmax = [&](int j) {
     double s = 0.0;
     for (int t = 0; t < dims; ++t) {
@@ -118,6 +118,44 @@ void build_grid(const float* cw, int N, int k, int dims, int G, double R, int re
     }
   };
 
+  // keep codewords of the candidate set `cand` that no other codeword beats on
+  // the whole box; write the cell's record
+  auto finish_cell = [&](uint16_t* rec) {
+    // 2. drop codewords beaten on the whole box by another one; trying the
+    //    candidates with the smallest worst-case distance first ends most
+    //    checks after a few comparisons
+    order.clear();
+    for (int j : cand) order.push_back({dmax(j), j});
+    std::sort(order.begin(), order.end());
+    kept.clear();
+    for (int i : cand) {
+      bool beaten = false;
+      for (const auto& oj : order) {
+        const int j = oj.second;
+        if (j == i) continue;
+        double f = cc[j] - cc[i];
+        for (int t = 0; t < dims; ++t) {
+          const double g = 2.0 * (P[(size_t)i * dims + t] - P[(size_t)j * dims + t]);
+          f += fmax(g * lo[t], g * hi[t]);
+        }
+        if (f < -1e-12 * (1.0 + cc[i] + cc[j])) {
+          beaten = true;
+          break;
+        }
+      }
+      if (!beaten) kept.push_back(i);
+    }
+    std::sort(kept.begin(), kept.end());
+    out->max_len = std::max(out->max_len, (int)kept.size());
+    if ((int)kept.size() > re - 1) {
+      rec[0] = GRID_OVERFLOW;
+      ++out->overflow;
+    } else {
+      rec[0] = (uint16_t)kept.size();
+      for (size_t m = 0; m < kept.size(); ++m) rec[1 + m] = (uint16_t)kept[m];
+    }
+  };
+
   for (int cell = 0; cell < ncell; ++cell) {
     int rem = cell;
     for (int t = 0; t < dims; ++t) {
@@ -125,6 +163,19 @@ void build_grid(const float* cw, int N, int k, int dims, int G, double R, int re
       rem /= G;
       lo[t] = -R + u[t] * h - mu;
       hi[t] = -R + (u[t] + 1) * h + mu;
+    }
+    if (dims >= 4) {
+      // four dimensions: test every codeword (G^4 cells of a few hundred
+      // codewords each take well under a second)
+      uint16_t* rec = out->rec.data() + (size_t)cell * re;
+      double best = INFINITY;
+      for (int j = 0; j < N; ++j) best = fmin(best, dmax(j));
+      const double lim = best * (1.0 + 1e-9) + 1e-18;
+      cand.clear();
+      for (int j = 0; j < N; ++j)
+        if (dmin(j) <= lim) cand.push_back(j);
+      finish_cell(rec);
+      continue;
     }
     // 1. smallest worst-case distance over the box; codewords in rings beyond r
     //    are at least r h - mu away from the box
@@ -160,39 +211,7 @@ void build_grid(const float* cw, int N, int k, int dims, int G, double R, int re
       ++out->overflow;
       continue;
     }
-    // 2. drop codewords beaten on the whole box by another one; trying the
-    //    candidates with the smallest worst-case distance first ends most
-    //    checks after a few comparisons
-    order.clear();
-    for (int j : cand) order.push_back({dmax(j), j});
-    std::sort(order.begin(), order.end());
-    kept.clear();
-    for (int i : cand) {
-      bool beaten = false;
-      for (const auto& oj : order) {
-        const int j = oj.second;
-        if (j == i) continue;
-        double f = cc[j] - cc[i];
-        for (int t = 0; t < dims; ++t) {
-          const double g = 2.0 * (P[(size_t)i * dims + t] - P[(size_t)j * dims + t]);
-          f += fmax(g * lo[t], g * hi[t]);
-        }
-        if (f < -1e-12 * (1.0 + cc[i] + cc[j])) {
-          beaten = true;
-          break;
-        }
-      }
-      if (!beaten) kept.push_back(i);
-    }
-    std::sort(kept.begin(), kept.end());
-    out->max_len = std::max(out->max_len, (int)kept.size());
-    if ((int)kept.size() > re - 1) {
-      rec[0] = GRID_OVERFLOW;
-      ++out->overflow;
-    } else {
-      rec[0] = (uint16_t)kept.size();
-      for (size_t m = 0; m < kept.size(); ++m) rec[1 + m] = (uint16_t)kept[m];
-    }
+    finish_cell(rec);
   }
 }
 

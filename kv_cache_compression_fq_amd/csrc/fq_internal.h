@@ -46,7 +46,7 @@ struct DeviceTables {
 
 // Candidate-list grids for the block search (fq_grid.cpp).
 // uint16 entries per cell record: count + up to 7 (k = 2) or 15 (k = 3) candidates
-__host__ __device__ constexpr int grid_record_entries(int k) { return k == 2 ? 8 : 16; }
+__host__ __device__ constexpr int grid_record_entries(int k) { return k == 2 ? 8 : (k == 3 ? 16 : 32); }
 constexpr uint16_t GRID_OVERFLOW = 0xFFFF;
 constexpr double GRID_MARGIN = 1e-4;     // box widening: rotation error + float32 cell arithmetic
 constexpr double GRID_R = 0.5;           // the grid covers [-R, R]^dims
