@@ -15,7 +15,7 @@ import time
 from . import artifact, codebook, rotation
 
 VARIANTS = [(2, 16), (2, 64), (2, 256), (3, 512), (4, 256), (8, 256), (8, 16), (4, 4),
-            (3, 4096)]
+            (3, 4096), (2, 32), (2, 128)]
 D = 64
 OUT_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                        "kv_cache_compression_fq_amd", "codebooks")

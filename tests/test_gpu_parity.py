@@ -187,6 +187,8 @@ ATT_CASES = [
     (1, 16, 2, 2049, (8, 256)),
     (2, 6, 3, 100, (4, 4)),
     (1, 8, 1, 64, (2, 256)),
+    (2, 8, 2, 520, (2, 32)),
+    (1, 4, 4, 130, (2, 128)),
 ]
 
 

@@ -114,6 +114,15 @@ def test_recorded_distortion_reproduces(k, N):
     assert abs(D - a["D_test"]) < 6 * se + 1e-12, (D, a["D_test"], se)
 
 
+def test_k2_distortion_falls_with_every_added_bit_half():
+    # the fractional rates 2.5 and 3.5 (N = 32, 128) sit between their integer
+    # neighbours, and each halving of the cell count lowers the distortion by
+    # less than the factor 4 per bit of the Shannon bound and more than 2^0.5
+    Ds = [load(2, N)["D_test"] for N in (16, 32, 64, 128, 256)]
+    for a, b in zip(Ds, Ds[1:]):
+        assert b < a / 2 ** 0.5 and b > a / 4, Ds
+
+
 def test_quality_band_vs_printed_table():
     table = json.load(open(os.path.join(GOLDEN_DIR, "blockquant_printed.json")))
     printed = dict(zip(table["bits"], table["mse"]["BlockQuant_p2"]))
