@@ -159,6 +159,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB device copy three times, so that a "
                          "counter run can scale FETCH_SIZE / WRITE_SIZE by a known size")
+    ap.add_argument("--no-fidelity", action="store_true",
+                    help="skip the attention-fidelity sweep over the rates")
     ap.add_argument("--attend-layers", type=int, default=22)
     ap.add_argument("--attend-steps", type=int, default=10)
     a = ap.parse_args()
@@ -288,6 +290,8 @@ def main():
         torch.cuda.empty_cache()
         attend = bench_attend(torch, fq, synth, dev, a.attend_layers, a.attend_steps, a.warmup)
 
+    fid = None if a.no_fidelity else fidelity(torch, fq, synth, dev)
+
     cpu = None if a.no_cpu_baseline else cpu_baseline(a.cpu_sample)
 
     out = {
@@ -304,9 +308,62 @@ def main():
         "cpu_baseline": cpu,
         "ops": ops,
         "attend_tinyllama": attend,
+        "fidelity": fid,
     }
     print(json.dumps(out))
     return 0
+
+
+FIDELITY_VARIANTS = [(8, 16), (4, 4), (8, 256), (4, 256), (2, 16), (2, 32), (3, 512), (2, 64),
+                     (2, 128), (2, 256)]   # k3N4096's tables exceed the attention kernel's LDS
+
+
+def fidelity(torch, fq, synth, dev, B=2, Hq=32, Hkv=4, T=4096, layers=(0, 11, 21)):
+    """Attention-output fidelity against the compression ratio (quality context).
+
+    TinyLlama-shaped seeded caches (per-channel log-uniform scales, 1 % x20
+    outlier channels), three layers, batch 2, 32 query / 4 KV heads, 4096
+    tokens: the fused attention over the compressed cache against exact
+    softmax attention over the uncompressed binary16 cache (float32), cosine
+    per (batch, query head).  The compression ratio counts the stored record
+    and norm against 64 binary16 values.  With N(0, 1) queries and these
+    channel scales the scores spread over tens of units, so attention is
+    close to an argmax over keys and key errors that swap the top tokens
+    change a head's output entirely: the sweep is a stress case for the rate
+    axis, not a model-quality figure.
+    """
+    import math
+    G = Hq // Hkv
+    n = B * Hkv * T
+    q = torch.from_numpy(synth.query(B, Hq, seed=7)).to(dev)
+    caches = []
+    for layer in layers:
+        K = synth.kv_slab_device(3, layer, 0, B, Hkv, T, dev)
+        V = synth.kv_slab_device(3, layer, 1, B, Hkv, T, dev)
+        qf = q.float().view(B, Hkv, G, 64)
+        s = torch.matmul(qf, K.float().transpose(-1, -2).contiguous()) * 0.125
+        o = torch.matmul(torch.softmax(s, dim=-1), V.float()).reshape(B, Hq, 64)
+        caches.append((K, V, o))
+    rows = []
+    for k, N in FIDELITY_VARIANTS:
+        cb = fq.load_codebook(k, N)
+        cos = []
+        for K, V, o_ref in caches:
+            kc, kn = fq.fq_encode(cb, K.reshape(n, 64))
+            vc, vn = fq.fq_encode(cb, V.reshape(n, 64))
+            o = fq.fq_attend_decode(cb, cb, q, kc.view(B, Hkv, T, cb.W), kn.view(B, Hkv, T),
+                                    vc.view(B, Hkv, T, cb.W), vn.view(B, Hkv, T), 0.125)
+            cos.append(torch.nn.functional.cosine_similarity(o.float(), o_ref, dim=-1).flatten())
+        c = torch.cat(cos)
+        rows.append({"variant": f"k{k}N{N}", "bits_per_coord": math.log2(N) / k,
+                     "compression": 128.0 / (4 * cb.W + 2),
+                     "attn_cos_mean": float(c.mean()),
+                     "attn_cos_p10": float(torch.quantile(c, 0.1)),
+                     "share_cos_ge_0.9": float((c >= 0.9).float().mean())})
+    log("fidelity sweep done")
+    return {"workload": f"tinyllama-shaped caches, layers {list(layers)}, batch {B}, "
+                        f"{Hq} q / {Hkv} kv heads, {T} tokens; exact attention in float32 on "
+                        "the binary16 cache as reference", "rows": rows}
 
 
 def bench_attend(torch, fq, synth, dev, layers, steps, warmup):

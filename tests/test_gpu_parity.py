@@ -447,3 +447,34 @@ def test_attention_tinyllama_layer_full(dev, layer):
     glob = np.linalg.norm(got - ref) / np.linalg.norm(ref)
     print(f"layer {layer}: max rel {np.max(rel):.2e}, global {glob:.2e}")
     assert np.max(rel) <= 2e-3
+
+
+def test_attention_fidelity_rises_with_rate(dev):
+    """Attention over the compressed cache against exact attention over the
+    uncompressed binary16 cache (float64 on the host): the mean cosine over
+    (batch, query head) rises with the rate in the k = 2 family."""
+    B, Hq, Hkv, T = 2, 32, 4, 2048
+    G = Hq // Hkv
+    q = synth.query(B, Hq, seed=7)
+    means = []
+    for N in (16, 64, 256):
+        _, cb = book(2, N)
+        cos = []
+        for layer in (0, 21):
+            K = synth.kv_slab(3, layer, 0, B, Hkv, T)
+            V = synth.kv_slab(3, layer, 1, B, Hkv, T)
+            kc, kn = fq.fq_encode(cb, to_dev(K.reshape(-1, 64), dev))
+            vc, vn = fq.fq_encode(cb, to_dev(V.reshape(-1, 64), dev))
+            o = fq.fq_attend_decode(cb, cb, to_dev(q, dev), kc.view(B, Hkv, T, cb.W),
+                                    kn.view(B, Hkv, T), vc.view(B, Hkv, T, cb.W),
+                                    vn.view(B, Hkv, T), 0.125).float().cpu().numpy()
+            qd = q.astype(np.float64).reshape(B, Hkv, G, 64)
+            s = np.einsum("bgxd,bgtd->bgxt", qd, K.astype(np.float64)) * 0.125
+            p = np.exp(s - s.max(-1, keepdims=True))
+            p /= p.sum(-1, keepdims=True)
+            ref = np.einsum("bgxt,bgtd->bgxd", p, V.astype(np.float64)).reshape(B, Hq, 64)
+            cos.append((o * ref).sum(-1) / (np.linalg.norm(o, axis=-1) * np.linalg.norm(ref, axis=-1)))
+        means.append(float(np.mean(cos)))
+    print("mean attention cosine at 2, 3, 4 bits:", means)
+    assert means[0] < means[1] < means[2]
+    assert means[2] > 0.8
