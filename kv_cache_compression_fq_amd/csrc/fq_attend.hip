@@ -187,6 +187,55 @@ struct AttLds {
   }
 };
 
+// Merge the four waves' partials of each head (held in LDS) and write either
+// the workgroup's partial (m, l, o_rot) for the merge kernel or, when the
+// context has a single split, the head's output out = Pi^T o_rot / l in
+// binary16 (row c of Pi^T from the transposed table).
+__device__ inline void finish_heads(const float* sMerge, int G, int Hq, int b, int g, int S, int sw,
+                                    float* ws, const float* pi32t, uint16_t* out) {
+  __shared__ float sO[MAX_G * D];
+  for (int e = threadIdx.x; e < G * D; e += ATT_THREADS) {
+    const int h = e / D, c = e % D;
+    float M = NEG_BIG;
+#pragma unroll
+    for (int w = 0; w < ATT_WAVES; ++w) M = fmaxf(M, sMerge[(w * MAX_G + h) * MERGE_PITCH]);
+    float Ls = 0.f, o = 0.f;
+#pragma unroll
+    for (int w = 0; w < ATT_WAVES; ++w) {
+      const float* pw = sMerge + (w * MAX_G + h) * MERGE_PITCH;
+      const float wt = pw[1] > 0.f ? __builtin_amdgcn_exp2f(pw[0] - M) : 0.f;
+      Ls = fmaf(wt, pw[1], Ls);
+      o = fmaf(wt, pw[2 + c], o);
+    }
+    if (S > 1) {
+      float* dst = ws + (((int64_t)b * Hq + (int64_t)g * G + h) * S + sw) * PART;
+      if (c == 0) {
+        dst[0] = M;
+        dst[1] = Ls;
+      }
+      dst[2 + c] = o;
+    } else {
+      sO[e] = o / Ls;
+    }
+  }
+  if (S > 1) return;
+  __syncthreads();
+  for (int e = threadIdx.x; e < G * D; e += ATT_THREADS) {
+    const int h = e / D, c = e % D;
+    const float4* pr = reinterpret_cast<const float4*>(pi32t + c * D);
+    float a = 0.f;
+#pragma unroll 4
+    for (int i = 0; i < D / 4; ++i) {
+      const float4 p = pr[i];
+      a = fmaf(p.x, sO[h * D + 4 * i], a);
+      a = fmaf(p.y, sO[h * D + 4 * i + 1], a);
+      a = fmaf(p.z, sO[h * D + 4 * i + 2], a);
+      a = fmaf(p.w, sO[h * D + 4 * i + 3], a);
+    }
+    out[((int64_t)b * Hq + (int64_t)g * G + h) * D + c] = f32_to_f16_rne(a);
+  }
+}
+
 template <int K, int BITS>
 __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void attend_split_kernel(
     const uint16_t* __restrict__ q, const uint32_t* __restrict__ kc,
@@ -194,7 +243,8 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2))
     const uint16_t* __restrict__ vn, int Hq, int Hkv, int64_t T, int64_t chunk, int S,
     float scale, const float* __restrict__ pi32, const _Float16* __restrict__ kh_g,
     const _Float16* __restrict__ kl_g, const _Float16* __restrict__ vh_g,
-    const _Float16* __restrict__ vl_g, int N, float* __restrict__ ws) {
+    const _Float16* __restrict__ vl_g, int N, float* __restrict__ ws,
+    const float* __restrict__ pi32t, uint16_t* __restrict__ out) {
   using Sh = Shape<K, BITS>;
   using AS = AttShape<K, BITS>;
   using L = AttLds<K, BITS>;
@@ -605,26 +655,7 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2))
         mine[2 + 16 * mt + 4 * grp + r] = fmaf(ol[mt][r], 0x1p-11f, oh[mt][r]);
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < G * D; e += ATT_THREADS) {
-    const int h = e / D, c = e % D;
-    float M = NEG_BIG;
-#pragma unroll
-    for (int w = 0; w < ATT_WAVES; ++w) M = fmaxf(M, sMerge[(w * MAX_G + h) * MERGE_PITCH]);
-    float Ls = 0.f, o = 0.f;
-#pragma unroll
-    for (int w = 0; w < ATT_WAVES; ++w) {
-      const float* pw = sMerge + (w * MAX_G + h) * MERGE_PITCH;
-      const float wt = pw[1] > 0.f ? __builtin_amdgcn_exp2f(pw[0] - M) : 0.f;
-      Ls = fmaf(wt, pw[1], Ls);
-      o = fmaf(wt, pw[2 + c], o);
-    }
-    float* dst = ws + (((int64_t)b * Hq + (int64_t)g * G + h) * S + sw) * PART;
-    if (c == 0) {
-      dst[0] = M;
-      dst[1] = Ls;
-    }
-    dst[2 + c] = o;
-  }
+  finish_heads(sMerge, G, Hq, b, g, S, sw, ws, pi32t, out);
 }
 
 // One workgroup of 256 per (batch, query head): log-sum-exp merge of the S
@@ -828,7 +859,7 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(3))
     const uint16_t* __restrict__ vn, int Hq, int Hkv, int64_t T, int64_t chunk, int S,
     float scale, const _Float16* __restrict__ pih_g, const _Float16* __restrict__ pil_g,
     const _Float16* __restrict__ kh_g, const _Float16* __restrict__ vh_g, int N,
-    float* __restrict__ ws) {
+    float* __restrict__ ws, const float* __restrict__ pi32t, uint16_t* __restrict__ out) {
   using C = DirectCfg<K, BITS>;
   using L = DirectLds<K, BITS>;
   constexpr int W = C::W;
@@ -1086,26 +1117,7 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(3))
       for (int r = 0; r < 4; ++r) mine[2 + 16 * grp + 4 * mt + r] = oacc[mt][r];
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < G * D; e += ATT_THREADS) {
-    const int h = e / D, c = e % D;
-    float M = NEG_BIG;
-#pragma unroll
-    for (int w = 0; w < ATT_WAVES; ++w) M = fmaxf(M, sMerge[(w * MAX_G + h) * MERGE_PITCH]);
-    float Ls = 0.f, o = 0.f;
-#pragma unroll
-    for (int w = 0; w < ATT_WAVES; ++w) {
-      const float* pw = sMerge + (w * MAX_G + h) * MERGE_PITCH;
-      const float wt = pw[1] > 0.f ? __builtin_amdgcn_exp2f(pw[0] - M) : 0.f;
-      Ls = fmaf(wt, pw[1], Ls);
-      o = fmaf(wt, pw[2 + c], o);
-    }
-    float* dst = ws + (((int64_t)b * Hq + (int64_t)g * G + h) * S + sw) * PART;
-    if (c == 0) {
-      dst[0] = M;
-      dst[1] = Ls;
-    }
-    dst[2 + c] = o;
-  }
+  finish_heads(sMerge, G, Hq, b, g, S, sw, ws, pi32t, out);
 }
 
 template <int K, int BITS>
@@ -1126,9 +1138,9 @@ hipError_t launch_v(const fq_codebook* ck, const fq_codebook* cv, const uint16_t
       auto kern = attend_direct_kernel<K, BITS>;
       hipLaunchKernelGGL(kern, dim3((unsigned)p.S, Hkv, B), dim3(ATT_THREADS), 0, s, q, kc, kn, vc,
                          vn, Hq, Hkv, T, p.chunk, p.S, scale, ck->t.pi16hi, ck->t.pi16lo,
-                         ck->t.cb16hi, cv->t.cb16hi, ck->N, ws);
+                         ck->t.cb16hi, cv->t.cb16hi, ck->N, ws, ck->t.pi32t, out);
       e = hipGetLastError();
-      if (e != hipSuccess) return e;
+      if (e != hipSuccess || p.S == 1) return e;
       hipLaunchKernelGGL(attend_merge_kernel, dim3(Hq * B), dim3(256), 0, s, ws, p.S, ck->t.pi32t,
                          out);
       return hipGetLastError();
@@ -1142,9 +1154,9 @@ hipError_t launch_v(const fq_codebook* ck, const fq_codebook* cv, const uint16_t
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)p.S, Hkv, B), dim3(ATT_THREADS), shm, s, q, kc, kn, vc, vn, Hq,
                      Hkv, T, p.chunk, p.S, scale, ck->t.pi32, ck->t.cb16hi, ck->t.cb16lo,
-                     cv->t.cb16hi, cv->t.cb16lo, ck->N, ws);
+                     cv->t.cb16hi, cv->t.cb16lo, ck->N, ws, ck->t.pi32t, out);
   e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || p.S == 1) return e;
   hipLaunchKernelGGL(attend_merge_kernel, dim3(Hq * B), dim3(256), 0, s, ws, p.S, ck->t.pi32t, out);
   return hipGetLastError();
 }
@@ -1153,7 +1165,8 @@ hipError_t launch_v(const fq_codebook* ck, const fq_codebook* cv, const uint16_t
 
 bool attend_supported(const fq_codebook* cb) {
 #define FQ_ATS(KK, BB) \
-  if (cb->k == KK && cb->bits == BB) return attend_lds_bytes<KK, BB>(cb->N) <= 160 * 1024;
+  if (cb->k == KK && cb->bits == BB)                                            \
+    return attend_lds_bytes<KK, BB>(cb->N) + MAX_G * D * 4 <= 160 * 1024;   /* + static */
   FQ_VARIANTS(FQ_ATS)
 #undef FQ_ATS
   return false;

@@ -188,6 +188,11 @@ ATT_CASES = [
     (2, 6, 3, 100, (4, 4)),
     (1, 8, 1, 64, (2, 256)),
     (2, 8, 2, 520, (2, 32)),
+    # one split per (batch, KV head) (T <= 256, or 512 or more pairs),
+    # finished without the merge pass
+    (4, 32, 4, 256, (4, 256)),
+    (8, 16, 2, 200, (2, 16)),
+    (128, 8, 8, 130, (2, 64)),
     (1, 4, 4, 130, (2, 128)),
 ]
 
