@@ -68,6 +68,16 @@ __device__ inline void unpack_record(const uint32_t (&w)[W], uint16_t* dst) {
       d32[2 * i] = __builtin_amdgcn_perm(0u, w[i], 0x0c010c00u);
       d32[2 * i + 1] = __builtin_amdgcn_perm(0u, w[i], 0x0c030c02u);
     }
+  } else if constexpr (BITS == 4 && NB % 8 == 0) {
+    // nibble fields: even and odd nibbles into bytes, then one byte permute
+    // per pair of indices (field 2 p from the even bytes, 2 p + 1 from the odd)
+#pragma unroll
+    for (int i = 0; i < NB / 8; ++i) {
+      const uint32_t ev = w[i] & 0x0F0F0F0Fu, od = (w[i] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        d32[4 * i + p] = __builtin_amdgcn_perm(od, ev, 0x0c000c00u | (uint32_t)p | ((uint32_t)(4 + p) << 16));
+    }
   } else {
 #pragma unroll
     for (int j = 0; j < NB; j += 2) d32[j >> 1] = f[j] | (f[j + 1] << 16);
