@@ -131,7 +131,8 @@ _KERNEL_LABEL = {"encode_k2N16": "encode_kernel<2,4,f16,grid>",
 
 def measured_traffic(op):
     """HBM bytes per launch of `op` from the committed counter summary, or None when
-    there is none or the library sources changed since the counters were taken."""
+    there is none or the library sources changed since the counters were taken.  The
+    summary lists each kernel once per grid size; the step's launch is the largest grid."""
     path = os.path.join(ROOT, "profiles", "fq_kernels_gpt2_small_step_and_tinyllama_attend.txt")
     label = _KERNEL_LABEL.get(op)
     if label is None or not os.path.exists(path):
@@ -139,14 +140,21 @@ def measured_traffic(op):
     text = open(path).read().splitlines()
     if f"source-sha256: {source_digest()}" not in text:
         return None
+    best = None
+    in_counters = False
     for line in text:
+        if line.startswith("HBM traffic"):
+            in_counters = True
         f = line.split()
-        if f and f[0] == label and len(f) >= 6:
-            try:
-                return (float(f[4]) + float(f[5])) * 1e6
-            except ValueError:
-                return None
-    return None
+        if not in_counters or len(f) != 7 or f[0] != label:
+            continue
+        try:
+            wg, total = int(f[1]), (float(f[5]) + float(f[6])) * 1e6
+        except ValueError:
+            continue
+        if best is None or wg > best[0]:
+            best = (wg, total)
+    return None if best is None else best[1]
 
 
 def main():
