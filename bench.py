@@ -22,6 +22,7 @@ so that reads are served from HBM rather than the 256 MB Infinity Cache.
 """
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -32,7 +33,9 @@ sys.path.insert(0, ROOT)
 METRIC = "KV vectors/s encode+decode (d=64) and attend HBM GB/s, % of MI355X peak"
 HBM_PEAK_GBS = 8000.0
 VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12     # non-packed lane-ops/s: 39.3 T
+MFMA_F16_PEAK_TFLOPS = 2500.0                      # dense binary16 matrix cores
 VARIANTS = [(2, 16), (2, 64), (2, 256), (3, 512)]
+LARGE_VARIANTS = [(32, 4096), (64, 4096)]
 L, B, H, T = 12, 4, 12, 1024
 N_RAND = 1 << 20
 COPY_BYTES = 1 << 28
@@ -169,6 +172,8 @@ def main():
                          "counter run can scale FETCH_SIZE / WRITE_SIZE by a known size")
     ap.add_argument("--no-fidelity", action="store_true",
                     help="skip the attention-fidelity sweep over the rates")
+    ap.add_argument("--no-large", action="store_true",
+                    help="skip the large-block (k = 32, 64; N = 4096) encode / decode timing")
     ap.add_argument("--attend-layers", type=int, default=22)
     ap.add_argument("--attend-steps", type=int, default=10)
     a = ap.parse_args()
@@ -290,6 +295,9 @@ def main():
         roof = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": traffic}
 
+    # ------------------------------------ large blocks (k = 32, 64; N = 4096)
+    large = None if a.no_large else bench_large(torch, fq, xs[0], ys[0], a.steps, a.warmup)
+
     # ---------------------------------------------- TinyLlama-shaped attention
     attend = None
     if a.attend_layers > 0:
@@ -316,6 +324,7 @@ def main():
         "cpu_baseline": cpu,
         "ops": ops,
         "attend_tinyllama": attend,
+        "large_k": large,
         "fidelity": fid,
     }
     print(json.dumps(out))
@@ -353,14 +362,23 @@ def fidelity(torch, fq, synth, dev, B=2, Hq=32, Hkv=4, T=4096, layers=(0, 11, 21
         o = torch.matmul(torch.softmax(s, dim=-1), V.float()).reshape(B, Hq, 64)
         caches.append((K, V, o))
     rows = []
-    for k, N in FIDELITY_VARIANTS:
+    for k, N in FIDELITY_VARIANTS + LARGE_VARIANTS:
         cb = fq.load_codebook(k, N)
         cos = []
         for K, V, o_ref in caches:
             kc, kn = fq.fq_encode(cb, K.reshape(n, 64))
             vc, vn = fq.fq_encode(cb, V.reshape(n, 64))
-            o = fq.fq_attend_decode(cb, cb, q, kc.view(B, Hkv, T, cb.W), kn.view(B, Hkv, T),
-                                    vc.view(B, Hkv, T, cb.W), vn.view(B, Hkv, T), 0.125)
+            if k < 32:
+                o = fq.fq_attend_decode(cb, cb, q, kc.view(B, Hkv, T, cb.W), kn.view(B, Hkv, T),
+                                        vc.view(B, Hkv, T, cb.W), vn.view(B, Hkv, T), 0.125)
+            else:
+                # no fused attention for tables larger than LDS: decode, then the
+                # same float32 attention as the reference
+                Kd = fq.fq_decode(cb, kc, kn).float().view(B, Hkv, T, 64)
+                Vd = fq.fq_decode(cb, vc, vn).float().view(B, Hkv, T, 64)
+                sd = torch.matmul(q.float().view(B, Hkv, G, 64),
+                                  Kd.transpose(-1, -2).contiguous()) * 0.125
+                o = torch.matmul(torch.softmax(sd, dim=-1), Vd).reshape(B, Hq, 64)
             cos.append(torch.nn.functional.cosine_similarity(o.float(), o_ref, dim=-1).flatten())
         c = torch.cat(cos)
         rows.append({"variant": f"k{k}N{N}", "bits_per_coord": math.log2(N) / k,
@@ -372,6 +390,46 @@ def fidelity(torch, fq, synth, dev, B=2, Hq=32, Hkv=4, T=4096, layers=(0, 11, 21
     return {"workload": f"tinyllama-shaped caches, layers {list(layers)}, batch {B}, "
                         f"{Hq} q / {Hkv} kv heads, {T} tokens; exact attention in float32 on "
                         "the binary16 cache as reference", "rows": rows}
+
+
+def bench_large(torch, fq, x, y, steps, warmup):
+    """Encode and decode of the GPT-2-shaped cache with the k = 32 and k = 64, N = 4096 codes.
+
+    The block search is a dense contraction here (4096 codewords of k
+    coordinates per block, 64 * 4096 multiply-adds per vector at either k), run
+    on the matrix cores: its roofline is the binary16 MFMA peak.  The kernel
+    forms every product twice (z split into binary16 hi and lo parts), so
+    the algorithmic fraction reported here is at most one half.
+    """
+    import numpy as np
+    n = x.shape[0]
+    out = {}
+    for k, N in LARGE_VARIANTS:
+        cb = fq.load_codebook(k, N)
+        codes = torch.empty((n, cb.W), dtype=torch.int32, device=x.device)
+        norms = torch.empty((n,), dtype=torch.int16, device=x.device)
+        timer = Timer(torch)
+        for i in range(warmup + steps):
+            if i == warmup:
+                timer.reset()
+            timer.run("encode", lambda: fq.fq_encode(cb, x, codes, norms))
+            timer.run("decode", lambda: fq.fq_decode(cb, codes, norms, y=y))
+        timer.collect()
+        te = float(np.median(timer.ms["encode"])) * 1e-3
+        td = float(np.median(timer.ms["decode"])) * 1e-3
+        flops = 2.0 * 64 * N * n                  # one multiply-add per codeword coordinate
+        dec_bytes = n * (record_bytes(k, N) + 2 + 128)
+        out[f"k{k}N{N}"] = {
+            "bits_per_coord": math.log2(N) / k, "compression": 128.0 / (4 * cb.W + 2),
+            "encode_ms": te * 1e3, "encode_vectors_per_s": n / te,
+            "encode_mfma_tflops": flops / te / 1e12,
+            "encode_mfma_frac": flops / te / 1e12 / MFMA_F16_PEAK_TFLOPS,
+            "decode_ms": td * 1e3, "decode_gbs": dec_bytes / td / 1e9,
+            "decode_hbm_frac": dec_bytes / td / 1e9 / HBM_PEAK_GBS}
+        del codes, norms
+    log("large-block timing done")
+    return {"workload": f"gpt2-small-kv-cache, {n} vectors, fp16; median of {steps} launches",
+            "peak_mfma_f16_tflops": MFMA_F16_PEAK_TFLOPS, "codes": out}
 
 
 def bench_attend(torch, fq, synth, dev, layers, steps, warmup):

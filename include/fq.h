@@ -78,7 +78,9 @@ const char* fq_status_string(fq_status s);
  * Returns FQ_ERR_BAD_ARTIFACT for a malformed or corrupt blob,
  * FQ_ERR_UNSUPPORTED for a valid blob the kernels are not built for.  Built
  * (k, N): k = 2 with N in {16, 32, 64, 128, 256}; k = 3 with N in {512, 4096};
- * k = 4 with N in {4, 256}; k = 8 with N in {16, 256}.  `out` may be NULL.
+ * k = 4 with N in {4, 256}; k = 8 with N in {16, 256}; k = 32 and k = 64 with
+ * N = 4096 (whose tables must hold binary16 values; fq_codebook_load returns
+ * FQ_ERR_UNSUPPORTED otherwise).  `out` may be NULL.
  */
 fq_status fq_artifact_check(const void* artifact, size_t nbytes, fq_info* out);
 
@@ -156,8 +158,9 @@ fq_status fq_attend_workspace_size(const fq_codebook* cb_k, int B, int Hq, int H
  *   fq_attend_workspace_size bytes, 256-byte aligned, contents need not be
  *   initialised.  cb_k and cb_v may be the same handle; they must be on the
  *   same device and hold the same (k, N) variant (one shared codebook serves
- *   keys and values [FQ 2.1]); the k = 3, N = 4096 tables exceed the kernel's
- *   LDS budget (FQ_ERR_UNSUPPORTED).  All pointers 16-byte aligned.
+ *   keys and values [FQ 2.1]); the k = 3, N = 4096 tables and the k = 32, 64
+ *   tables exceed the kernel's LDS budget (FQ_ERR_UNSUPPORTED).  All pointers
+ *   16-byte aligned.
  */
 fq_status fq_attend_decode(const fq_codebook* cb_k, const fq_codebook* cb_v, const uint16_t* q,
                            const uint32_t* k_codes, const uint16_t* k_norms,

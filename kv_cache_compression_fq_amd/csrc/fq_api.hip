@@ -198,6 +198,8 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
     rho_pi = fmax(rho_pi, fabs(cb->pi[i] - (double)pih[i] - (double)pil[i] / 2048.0));
   }
   cb->half_exact = true;
+  cb->cmax = 0.0;
+  std::vector<float> hnorm(fq::large_block(k) ? N : 0);
   for (int n = 0; n < N; ++n) {
     double cc = 0;
     for (int t = 0; t < k; ++t) {
@@ -209,6 +211,25 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
       cbl[(size_t)n * k + t] = (_Float16)((v - (double)cbh[(size_t)n * k + t]) * 2048.0);
     }
     enc[(size_t)n * S + k] = (float)cc;
+    cb->cmax = fmax(cb->cmax, sqrt(cc));
+    if (!hnorm.empty()) hnorm[n] = (float)(-0.5 * cc);
+  }
+  // k >= 32: the codebook as A fragments of v_mfma_f32_16x16x32_f16 (binary16;
+  // the large-block kernels need a table on the binary16 grid)
+  std::vector<_Float16> lfrag;
+  if (fq::large_block(k)) {
+    if (!cb->half_exact || k % 32 != 0 || N % 16 != 0) {
+      delete cb;
+      return FQ_ERR_UNSUPPORTED;
+    }
+    const int kcs = k / 32;
+    lfrag.resize((size_t)N * k);
+    for (int tile = 0; tile < N / 16; ++tile)
+      for (int kc = 0; kc < kcs; ++kc)
+        for (int lane = 0; lane < 64; ++lane)
+          for (int e = 0; e < 8; ++e)
+            lfrag[(((size_t)tile * kcs + kc) * 64 + lane) * 8 + e] =
+                cbh[(size_t)(16 * tile + lane % 16) * k + 32 * kc + 8 * (lane / 16) + e];
   }
   // Encode rotation error bound per coordinate of a unit vector.  Each output
   // is a float32 sum of four 16-product groups (each accumulated from zero,
@@ -276,7 +297,8 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
                o_cbl = take(2ull * N * k), o_frag = take(2ull * frag.size()),
                o_efrag = take(2ull * efrag.size()),
                o_grid = take(2ull * grid.rec.size() + 64), o_grid1 = take(2ull * grid1.rec.size() + 64),
-               o_pih = take(2ull * d * d), o_pil = take(2ull * d * d), o_pit = take(4ull * d * d);
+               o_pih = take(2ull * d * d), o_pil = take(2ull * d * d), o_pit = take(4ull * d * d),
+               o_lfrag = take(2ull * lfrag.size()), o_hn = take(4ull * hnorm.size());
   cb->dev_bytes = off;
   {
     DeviceGuard g(device);
@@ -302,6 +324,8 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
     cb->t.pi32t = reinterpret_cast<float*>(base + o_pit);
     cb->t.grid = grid.rec.empty() ? nullptr : reinterpret_cast<uint16_t*>(base + o_grid);
     cb->t.grid1 = grid1.rec.empty() ? nullptr : reinterpret_cast<uint16_t*>(base + o_grid1);
+    cb->t.lfrag = lfrag.empty() ? nullptr : reinterpret_cast<_Float16*>(base + o_lfrag);
+    cb->t.hnorm = hnorm.empty() ? nullptr : reinterpret_cast<float*>(base + o_hn);
     std::vector<char> staging(off, 0);
     memcpy(staging.data() + o_pi64, cb->pi.data(), 8ull * d * d);
     memcpy(staging.data() + o_pi32, pi32.data(), 4ull * d * d);
@@ -315,6 +339,8 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
     for (int i = 0; i < d; ++i)
       for (int j = 0; j < d; ++j)
         reinterpret_cast<float*>(staging.data() + o_pit)[(size_t)j * d + i] = pi32[(size_t)i * d + j];
+    if (!lfrag.empty()) memcpy(staging.data() + o_lfrag, lfrag.data(), 2ull * lfrag.size());
+    if (!hnorm.empty()) memcpy(staging.data() + o_hn, hnorm.data(), 4ull * hnorm.size());
     if (!grid.rec.empty()) memcpy(staging.data() + o_grid, grid.rec.data(), 2ull * grid.rec.size());
     if (!grid1.rec.empty())
       memcpy(staging.data() + o_grid1, grid1.rec.data(), 2ull * grid1.rec.size());
@@ -368,8 +394,11 @@ fq_status fq_encode(const fq_codebook* cb, const void* x, fq_dtype x_dtype, int6
   DeviceGuard g(cb->device);
   if (g.err != hipSuccess) return FQ_ERR_DEVICE;
   (void)hipGetLastError();
-  hipError_t e = fq::launch_encode(cb, x, x_dtype, n, x_ld, codes, norms,
-                                   static_cast<hipStream_t>(stream));
+  hipError_t e = fq::large_block(cb->k)
+                     ? fq::launch_encode_large(cb, x, x_dtype, n, x_ld, codes, norms,
+                                               static_cast<hipStream_t>(stream))
+                     : fq::launch_encode(cb, x, x_dtype, n, x_ld, codes, norms,
+                                         static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FQ_OK : FQ_ERR_DEVICE;
 }
 

@@ -100,6 +100,9 @@ __device__ inline half8 gather8(const uint16_t* idx, const _Float16* cbh, int c0
     const uint32_t* h = reinterpret_cast<const uint32_t*>(cbh);
     const u32x4 hv = {h[i0], h[i1], h[i2], h[i3]};
     return __builtin_bit_cast(half8, hv);
+  } else if constexpr (K % 8 == 0 && K >= 16) {   // 8 coordinates of one codeword
+    const uint32_t i0 = idx[c0 / K];
+    return *reinterpret_cast<const half8*>(cbh + i0 * K + c0 % K);
   } else {  // K = 3: one coordinate at a time; the last block may be partial
     half8 hi;
 #pragma unroll
@@ -120,9 +123,11 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
     int N) {
   using Sh = Shape<K, BITS>;
   constexpr int W = Sh::W;
+  // large blocks: the table (N k binary16) stays in global memory (L2-resident)
+  constexpr bool GTAB = large_block(K);
   extern __shared__ __align__(16) unsigned char smem[];
   _Float16* sCbh = reinterpret_cast<_Float16*>(smem);
-  const size_t cb_bytes = ((size_t)N * K * sizeof(_Float16) + 15) / 16 * 16;
+  const size_t cb_bytes = GTAB ? 0 : ((size_t)N * K * sizeof(_Float16) + 15) / 16 * 16;
   // the wave index is uniform: keep it (and the buffer descriptors derived from
   // it) in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -131,7 +136,8 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
   float* sNu = reinterpret_cast<float*>(wbase + CHUNK * Sh::IDX_PITCH * 2);  // [CHUNK]
   TY* sOut = reinterpret_cast<TY*>(wbase + CHUNK * Sh::IDX_PITCH * 2 + CHUNK * 4);
 
-  for (int e = threadIdx.x; e < N * K; e += DEC_THREADS) sCbh[e] = cbh_g[e];
+  if constexpr (!GTAB)
+    for (int e = threadIdx.x; e < N * K; e += DEC_THREADS) sCbh[e] = cbh_g[e];
   // A operands: Pi^T as 16 x 32 fragments, [mt][s] = Pi[32 s + 8 grp + e][16 mt + col]
   half8 pa[4][2];
   const int col = lane & 15, grp = lane >> 4;
@@ -168,6 +174,15 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
     sNu[lane] = f16_bits_to_f32((uint16_t)t.nu_bits);
   };
   auto decode_chunk = [&](int64_t base) {
+    // global-table gathers of the whole chunk are issued together, ahead of use
+    half8 zg[CHUNK / TILE][2];
+    if constexpr (GTAB) {
+#pragma unroll
+      for (int m = 0; m < CHUNK / TILE; ++m)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          zg[m][s] = gather8<K>(sIdx + (TILE * m + col) * Sh::IDX_PITCH, cbh_g, 32 * s + 8 * grp);
+    }
 #pragma unroll
     for (int m = 0; m < CHUNK / TILE; ++m) {
       const uint16_t* vidx = sIdx + (TILE * m + col) * Sh::IDX_PITCH;
@@ -176,7 +191,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
       for (int mt = 0; mt < 4; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const half8 zh = gather8<K>(vidx, sCbh, 32 * s + 8 * grp);
+        const half8 zh = GTAB ? zg[m][s] : gather8<K>(vidx, sCbh, 32 * s + 8 * grp);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
           acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[mt][s], zh, acc[mt], 0, 0, 0);
@@ -249,7 +264,7 @@ template <int K, int BITS, typename TY, bool GATHER>
 hipError_t launch_k(const fq_codebook* cb, const uint32_t* codes, const uint16_t* norms,
                     const int64_t* rows, int64_t n_records, int64_t n, TY* y, int64_t ld,
                     hipStream_t s) {
-  const size_t cb_bytes = ((size_t)cb->N * K * sizeof(_Float16) + 15) / 16 * 16;
+  const size_t cb_bytes = large_block(K) ? 0 : ((size_t)cb->N * K * sizeof(_Float16) + 15) / 16 * 16;
   const size_t shm = cb_bytes + DEC_WAVES * wave_lds<K, BITS, TY>();
   auto kern = decode_kernel<K, BITS, TY, GATHER>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -275,6 +290,7 @@ hipError_t dispatch(const fq_codebook* cb, const uint32_t* codes, const uint16_t
   if (cb->k == KK && cb->bits == BB)                                                       \
     return launch_k<KK, BB, TY, GATHER>(cb, codes, norms, rows, n_records, n, y, ld, s);
   FQ_VARIANTS(FQ_DEC)
+  FQ_VARIANTS_LARGE(FQ_DEC)
 #undef FQ_DEC
   return hipErrorInvalidValue;
 }

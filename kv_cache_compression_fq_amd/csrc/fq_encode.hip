@@ -38,20 +38,18 @@
 // most one rounding of 2^-23 relative per accumulated term, then the groups
 // added in float32) and the final scaling; it is computed on the host from the
 // actual split residuals.
-#include <type_traits>
-
 #include "fq_common.h"
+#include "fq_encode_x.h"
 #include "fq_internal.h"
 
 namespace fq {
 namespace {
 
-constexpr int EV = 16;          // vectors per wave chunk
+using namespace encx;
+
 // waves per workgroup: 4, or 8 when the codebook table fills most of LDS
 template <int BITS>
 constexpr int enc_waves() { return BITS >= 10 ? 8 : 4; }
-constexpr int ZP = 68;          // floats per staged z row
-constexpr int ROT_BYTES = 2 * 4 * 4 * 64 * 4 * 2;   // Pi fragments, [part][ot][kq][lane][4]
 constexpr float SLACK = 1e-5f;  // covers |D~ - D| inside the square roots of the bound
 
 template <int K, int BITS>
@@ -90,102 +88,6 @@ struct EncArgs {
 
 __host__ __device__ inline size_t enc_table_bytes(int N, int S) {   // N rows + sentinel
   return ((size_t)(N + 1) * S * 4 + 15) / 16 * 16;
-}
-
-__device__ inline double shfl_xor_f64(double v, int m) {
-  int2 p = __builtin_bit_cast(int2, v);
-  p.x = __shfl_xor(p.x, m, 64);
-  p.y = __shfl_xor(p.y, m, 64);
-  return __builtin_bit_cast(double, p);
-}
-
-// x fragments of one vector for v_mfma_f32_16x16x16_f16 (lane's vector
-// j = lane % 16, coordinates 16 kq + 4 (lane / 16) .. + 3) as binary16 hi parts
-// (and lo parts, scaled by 2^11, for float32 input), the float64 sum of
-// squares, and for float32 input the power of two the fragments were scaled by.
-template <typename TX>
-struct XFrag {
-  half4 hi[4], lo[4];
-  float ss;       // sum of squares of the (scaled) vector, pairwise in float32
-  float escale;   // the fragments hold x * 2^-e; escale = 2^e
-};
-
-// Pairwise float32 sum of the 16 squares a lane holds, then across the four
-// lanes of the vector: six rounding levels, so the relative error of the
-// (positive) sum is below 6 * 2^-24, well inside the norm's tolerance.
-__device__ inline float pairwise_squares(const float (&v)[16]) {
-  float t8[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) t8[i] = fmaf(v[2 * i], v[2 * i], v[2 * i + 1] * v[2 * i + 1]);
-  const float t4[4] = {t8[0] + t8[1], t8[2] + t8[3], t8[4] + t8[5], t8[6] + t8[7]};
-  float ss = (t4[0] + t4[1]) + (t4[2] + t4[3]);
-  ss += __shfl_xor(ss, 16, 64);
-  ss += __shfl_xor(ss, 32, 64);
-  return ss;
-}
-
-// Raw loads of one lane's x elements (issued one chunk ahead).
-template <typename TX>
-struct XRaw;
-template <>
-struct XRaw<_Float16> {
-  u32x2 q[4];
-};
-template <>
-struct XRaw<float> {
-  floatx4 q[4];
-};
-
-template <typename TX>
-__device__ inline void load_raw(const TX* xr, int g, XRaw<TX>& r) {
-#pragma unroll
-  for (int kq = 0; kq < 4; ++kq)
-    r.q[kq] = *reinterpret_cast<const std::remove_reference_t<decltype(r.q[0])>*>(xr + 16 * kq + 4 * g);
-}
-
-template <typename TX>
-__device__ inline void finish_x(const XRaw<TX>& r, XFrag<TX>& f);
-
-template <>
-__device__ inline void finish_x<_Float16>(const XRaw<_Float16>& r, XFrag<_Float16>& f) {
-  float v[16];
-#pragma unroll
-  for (int kq = 0; kq < 4; ++kq) {
-    f.hi[kq] = __builtin_bit_cast(half4, r.q[kq]);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[4 * kq + e] = (float)f.hi[kq][e];   // squares exact in float32
-  }
-  f.ss = pairwise_squares(v);
-  f.escale = 1.f;
-}
-
-template <>
-__device__ inline void finish_x<float>(const XRaw<float>& r, XFrag<float>& f) {
-  float mx = 0.f;
-#pragma unroll
-  for (int kq = 0; kq < 4; ++kq)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(r.q[kq][e]));
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  // scale so that |x| <= 1: binary16 then holds every element without overflow,
-  // and the squares cannot overflow float32
-  int e = 0;
-  if (mx > 0.f && mx <= 3.0e38f) (void)frexpf(mx, &e);
-  const float down = ldexpf(1.f, -e);
-  float v[16];
-#pragma unroll
-  for (int kq = 0; kq < 4; ++kq)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float sv = r.q[kq][i] * down;
-      v[4 * kq + i] = sv;
-      const _Float16 h = (_Float16)sv;
-      f.hi[kq][i] = h;
-      f.lo[kq][i] = (_Float16)((sv - (float)h) * 2048.f);
-    }
-  f.ss = pairwise_squares(v);
-  f.escale = ldexpf(1.f, e);
 }
 
 // Word w of a record from the staged indices of one vector (4-byte aligned
@@ -406,34 +308,8 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
     // path, which returns index 0 for them
     const float inv = __builtin_amdgcn_rcpf(nus);
 
-    // ---- 2. rotation: lane holds z~[vector j][16 ot + 4 g + r]; every
-    //      16-product group is accumulated from zero and the groups are summed
-    //      in float32, which keeps the rounding bound small
-#pragma unroll
-    for (int ot = 0; ot < 4; ++ot) {
-      const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
-      constexpr int NP = sizeof(TX) == 4 ? 3 : 2;
-      floatx4 pp[4][NP];
-#pragma unroll
-      for (int kq = 0; kq < 4; ++kq) {
-        const half4 ph = *reinterpret_cast<const half4*>(sRot + (((0 * 4 + ot) * 4 + kq) * 64 + lane) * 4);
-        const half4 pl = *reinterpret_cast<const half4*>(sRot + (((1 * 4 + ot) * 4 + kq) * 64 + lane) * 4);
-        pp[kq][0] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, xf.hi[kq], zero, 0, 0, 0);
-        pp[kq][1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, xf.hi[kq], zero, 0, 0, 0);
-        if constexpr (NP == 3)
-          pp[kq][2] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, xf.lo[kq], zero, 0, 0, 0);
-      }
-      floatx4 zv;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float zh = (pp[0][0][r] + pp[1][0][r]) + (pp[2][0][r] + pp[3][0][r]);
-        float zl = (pp[0][1][r] + pp[1][1][r]) + (pp[2][1][r] + pp[3][1][r]);
-        if constexpr (NP == 3)
-          zl += (pp[0][2][r] + pp[1][2][r]) + (pp[2][2][r] + pp[3][2][r]);
-        zv[r] = fmaf(zl, 0x1p-11f, zh) * inv;
-      }
-      *reinterpret_cast<floatx4*>(sZ + j * ZP + 16 * ot + 4 * g) = zv;
-    }
+    // ---- 2. rotation: lane holds z~[vector j][16 ot + 4 g + r]
+    rotate_to_lds<TX>(xf, sRot, inv, sZ, lane);
     wave_lds_sync();
 
     // ---- 3-4. search + certification.  Full blocks first, in batches of QB

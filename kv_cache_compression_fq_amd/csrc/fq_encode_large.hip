@@ -1,0 +1,416 @@
+// FibQuant encode for large blocks: k = 32 and k = 64 (one or two blocks per
+// vector) with N = 4096 codewords (FibQuant technical summary, sections 2.2
+// and 2.3; the extreme rates below one bit per coordinate of section 4).
+//
+// The nearest-codeword search is a dense contraction here: every block is
+// compared with all 4096 codewords of k coordinates, 4096 k multiply-adds per
+// block, and the table (N k binary16 values, 256 or 512 KB) is larger than
+// LDS.  So the search runs on the matrix cores:
+//
+//  * One workgroup of 8 waves streams the codebook through LDS in stages of
+//    256 codewords (double-buffered, each stage loaded once per workgroup and
+//    shared by its 8 waves).  A wave holds 64 block columns (64 vectors at
+//    k = 64, 32 vectors at k = 32) as binary16 B operands, split
+//    z~ = z_hi + z_lo (both binary16, the lo part unscaled so it accumulates
+//    into the same sum), and for every tile of 16 codewords forms
+//    s(n) = <c_n, z~> - |c_n|^2 / 2 with v_mfma_f32_16x16x32_f16, the
+//    accumulator starting at -|c_n|^2 / 2 (float32 from the host).  The
+//    nearest codeword maximises s.
+//  * Each lane keeps, for its 4 accumulator rows ("slots": the codewords
+//    16 t + 4 (lane / 16) + r of every tile t), the best and second-best key,
+//    where a key is the float32 score with its low 8 mantissa bits replaced by
+//    the tile number t, compared as a signed integer (the scores' order for
+//    scores >= 0).  The 16 slots of a column are merged at the end.
+//  * Certification.  The computed score of every codeword is within
+//    E = EA |z~| + EB of its exact value at z~ (binary16 split of z~: 2^-22
+//    relative plus 2^-25 absolute per coordinate; float32 accumulation of
+//    2k + 2 terms, taken as one rounding of 2^-23 per term relative to the
+//    sum of their magnitudes; the rounded |c|^2 / 2), z~ is within ez of the
+//    exact z per coordinate, which moves a score difference by at most
+//    2 ez sqrt(k) max|c|, and a key is within 2^-15 of its score relative.
+//    A codeword whose key is more than M below the best key cannot be the
+//    exact nearest.  When the best key exceeds M, only the best slot is
+//    within M and no slot's second key is, the float32 winner is final.
+//  * Otherwise the block is settled exactly in float64 by the whole wave:
+//    z's block from x and the float64 Pi, then the candidates (the slot
+//    leaders within M) or, when a slot may hide a further candidate, all N
+//    codewords; ties go to the lowest index.
+//  * Records (one 32-bit word: one or two 12-bit fields) and norms are
+//    written with coalesced stores.
+#include "fq_common.h"
+#include "fq_encode_x.h"
+#include "fq_internal.h"
+
+namespace fq {
+namespace {
+
+using namespace encx;
+
+constexpr int LW = 8;        // waves per workgroup
+constexpr int CG = 4;        // column groups of 16 per wave pass
+constexpr int TCW = 256;     // codewords per LDS stage
+constexpr int LBITS = 12;    // log2 N
+constexpr int LN = 1 << LBITS;
+constexpr int NSTAGE = LN / TCW;
+
+template <int K>
+struct LShape {
+  static constexpr int NB = D / K;                 // blocks per vector (k divides d)
+  static constexpr int KC = K / 32;                // 32-coordinate steps per block
+  static constexpr int VPW = 16 * CG / NB;         // vectors per wave pass
+  static constexpr int BATCHES = VPW / EV;         // rotation batches of 16 vectors per pass
+  static constexpr int STAGE_BYTES = TCW * K * 2;  // one stage of codebook fragments
+  static constexpr int LOADS = STAGE_BYTES / (16 * LW * 64);   // 16-byte loads per thread
+  static constexpr size_t WAVE_BYTES = (size_t)EV * ZP * 4 + 2 * 64 * 8;
+  static constexpr size_t LDS = 2 * (size_t)STAGE_BYTES + LN * 4 + ROT_BYTES + LW * WAVE_BYTES;
+};
+
+struct LArgs {
+  const void* x;
+  int64_t n, ld;
+  uint32_t* codes;
+  uint16_t* norms;
+  const _Float16* rotfrag;  // Pi hi / lo as 16x16x16 A fragments
+  const _Float16* lfrag;    // codebook as 16x16x32 A fragments [tile][kc][lane][8]
+  const float* hn;          // -|c_n|^2 / 2, float32
+  const float* enc;         // [N + 1][S] search table (-2 c, |c|^2): c = -enc / 2 exactly
+  int S;
+  const double* pi64;
+  float EA, EB, ZT;         // certification constants (see the header)
+};
+
+__device__ inline double wave_sum_f64(double v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_f64(v, m);
+  return v;
+}
+
+// Keys compare as signed integers: the order of the float scores for scores
+// >= 0 (the only ones a certified or listed winner can have, see the margin
+// test), below every non-negative score otherwise.
+__device__ inline uint32_t key_tile(int key) { return (uint32_t)key & 0xFFu; }
+__device__ inline float key_value(int key) { return __int_as_float(key); }
+
+template <int K, typename TX>
+__global__ __launch_bounds__(LW * 64) void encode_large_kernel(LArgs a) {
+  using Sh = LShape<K>;
+  constexpr int NB = Sh::NB, KC = Sh::KC;
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* sStage = smem;                                           // 2 stages
+  float* sHn = reinterpret_cast<float*>(smem + 2 * Sh::STAGE_BYTES);      // [N]
+  _Float16* sRot = reinterpret_cast<_Float16*>(smem + 2 * Sh::STAGE_BYTES + LN * 4);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  unsigned char* wb = smem + 2 * Sh::STAGE_BYTES + LN * 4 + ROT_BYTES + wave * Sh::WAVE_BYTES;
+  float* sZ = reinterpret_cast<float*>(wb);                               // [EV][ZP]
+  double* sX = reinterpret_cast<double*>(wb + EV * ZP * 4);              // exact path: x
+  double* sZd = sX + 64;                                                  // exact path: z block
+  const int j = lane & 15, grp = lane >> 4;
+
+  for (int i = threadIdx.x; i < ROT_BYTES / 16; i += blockDim.x)
+    reinterpret_cast<u32x4*>(sRot)[i] = reinterpret_cast<const u32x4*>(a.rotfrag)[i];
+  for (int i = threadIdx.x; i < LN / 4; i += blockDim.x)
+    reinterpret_cast<floatx4*>(sHn)[i] = reinterpret_cast<const floatx4*>(a.hn)[i];
+  const u32x4* gfrag = reinterpret_cast<const u32x4*>(a.lfrag);
+  constexpr int STAGE_Q = Sh::STAGE_BYTES / 16;   // 16-byte pieces per stage
+#pragma unroll
+  for (int u = 0; u < Sh::LOADS; ++u)
+    reinterpret_cast<u32x4*>(sStage)[threadIdx.x + LW * 64 * u] = gfrag[threadIdx.x + LW * 64 * u];
+  __syncthreads();
+
+  const TX* __restrict__ x = static_cast<const TX*>(a.x);
+  const int64_t n = a.n;
+  const int64_t wg_vecs = (int64_t)LW * Sh::VPW;
+  const int64_t passes = (n + wg_vecs - 1) / wg_vecs;
+  int sbuf = 0;
+
+  for (int64_t gp = blockIdx.x; gp < passes; gp += gridDim.x) {
+    const int64_t vbase = gp * wg_vecs + (int64_t)wave * Sh::VPW;
+
+    // ---- norm, rotation and B operands of the wave's 64 columns.  Column
+    //      group c = h NB + b holds block b of batch h (vectors 16 h .. + 15).
+    half8 bh[CG][KC], bl[CG][KC];
+    float zz[CG];
+#pragma unroll
+    for (int h = 0; h < Sh::BATCHES; ++h) {
+      const int64_t row0 = vbase + EV * h;
+      const int64_t last = n - 1 - row0;   // rows past the end repeat the last one
+      const TX* xr = x + (row0 + (j < last ? j : (last < 0 ? 0 : last))) * a.ld;
+      if (last < 0) xr = x + (n - 1) * a.ld;
+      XRaw<TX> xraw;
+      load_raw<TX>(xr, grp, xraw);
+      XFrag<TX> xf;
+      finish_x<TX>(xraw, xf);
+      const float nus = __builtin_amdgcn_sqrtf(xf.ss);
+      if (grp == 0 && j <= last) a.norms[row0 + j] = f32_to_f16_rne(nus * xf.escale);
+      rotate_to_lds<TX>(xf, sRot, __builtin_amdgcn_rcpf(nus), sZ, lane);
+      wave_lds_sync();
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int c = h * NB + b;
+        float ss = 0.f;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          const float* zr = sZ + j * ZP + b * K + 32 * kc + 8 * grp;
+          const floatx4 z0 = *reinterpret_cast<const floatx4*>(zr);
+          const floatx4 z1 = *reinterpret_cast<const floatx4*>(zr + 4);
+          const float zv[8] = {z0[0], z0[1], z0[2], z0[3], z1[0], z1[1], z1[2], z1[3]};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const _Float16 hi = (_Float16)zv[e];
+            bh[c][kc][e] = hi;
+            bl[c][kc][e] = (_Float16)(zv[e] - (float)hi);
+            ss = fmaf(zv[e], zv[e], ss);
+          }
+        }
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+        zz[c] = ss;
+      }
+      wave_lds_sync();
+    }
+
+    // ---- the codebook sweep
+    int m1[CG][4], m2[CG][4];
+#pragma unroll
+    for (int c = 0; c < CG; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) m1[c][r] = m2[c][r] = INT32_MIN;
+    for (int s = 0; s < NSTAGE; ++s) {
+      // next stage (cyclic: the last one fetches stage 0 of the next pass)
+      u32x4 pre[Sh::LOADS];
+      const int sn = s + 1 < NSTAGE ? s + 1 : 0;
+#pragma unroll
+      for (int u = 0; u < Sh::LOADS; ++u) pre[u] = gfrag[sn * STAGE_Q + threadIdx.x + LW * 64 * u];
+      const unsigned char* st = sStage + sbuf * Sh::STAGE_BYTES;
+#pragma unroll 2
+      for (int i = 0; i < TCW / 16; ++i) {
+        const uint32_t t = (uint32_t)(16 * s + i);
+        half8 av[KC];
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+          av[kc] = *reinterpret_cast<const half8*>(st + ((i * KC + kc) * 64 + lane) * 16);
+        const floatx4 c0 = *reinterpret_cast<const floatx4*>(sHn + 16 * t + 4 * grp);
+        floatx4 acc[CG];
+#pragma unroll
+        for (int c = 0; c < CG; ++c) acc[c] = c0;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+#pragma unroll
+          for (int c = 0; c < CG; ++c)
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[kc], bh[c][kc], acc[c], 0, 0, 0);
+#pragma unroll
+          for (int c = 0; c < CG; ++c)
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[kc], bl[c][kc], acc[c], 0, 0, 0);
+        }
+#pragma unroll
+        for (int c = 0; c < CG; ++c)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            // bytes 3..1 of the score, byte 0 = the tile number
+            const int key = (int)__builtin_amdgcn_perm(__float_as_uint(acc[c][r]), t, 0x07060500u);
+            // median of the three (the canonical form of v_med3_i32)
+            m2[c][r] = max(min(m1[c][r], m2[c][r]), min(max(m1[c][r], m2[c][r]), key));
+            m1[c][r] = max(m1[c][r], key);
+          }
+      }
+#pragma unroll
+      for (int u = 0; u < Sh::LOADS; ++u)
+        reinterpret_cast<u32x4*>(sStage + (sbuf ^ 1) * Sh::STAGE_BYTES)[threadIdx.x + LW * 64 * u] =
+            pre[u];
+      __syncthreads();
+      sbuf ^= 1;
+    }
+
+    // ---- merge the slots, certify, settle the rest exactly
+    int res[CG];
+#pragma unroll
+    for (int c = 0; c < CG; ++c) {
+      int b1 = m1[c][0], b2 = m2[c][0];
+      int r1 = 0;
+#pragma unroll
+      for (int r = 1; r < 4; ++r) {
+        const int o1 = m1[c][r], o2 = m2[c][r];
+        b2 = max(max(b2, o2), min(b1, o1));
+        const bool tk = o1 > b1;
+        b1 = tk ? o1 : b1;
+        r1 = tk ? r : r1;
+      }
+      int n1 = 16 * (int)key_tile(b1) + 4 * grp + r1;
+#pragma unroll
+      for (int m = 16; m <= 32; m <<= 1) {
+        const int o1 = __shfl_xor(b1, m, 64), o2 = __shfl_xor(b2, m, 64);
+        const int on = __shfl_xor(n1, m, 64);
+        b2 = max(max(b2, o2), min(b1, o1));
+        const bool tk = o1 > b1 || (o1 == b1 && on < n1);
+        b1 = tk ? o1 : b1;
+        n1 = tk ? on : n1;
+      }
+      const float bv = key_value(b1);
+      const float zn = __builtin_amdgcn_sqrtf(zz[c]);
+      const float E = fmaf(a.EA, zn, a.EB);
+      const float M = fmaf(2.f, E, fmaf(0x1p-14f, fabsf(bv), a.ZT)) * 1.0001f + 1e-12f;
+      const float lim = bv - M;
+      int ncand = 0;
+      bool hidden = false;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        ncand += key_value(m1[c][r]) >= lim ? 1 : 0;
+        hidden = hidden || key_value(m2[c][r]) >= lim;
+      }
+      ncand += __shfl_xor(ncand, 16, 64);
+      ncand += __shfl_xor(ncand, 32, 64);
+      int hid = hidden ? 1 : 0;
+      hid |= __shfl_xor(hid, 16, 64);
+      hid |= __shfl_xor(hid, 32, 64);
+      // a winner at or below the margin may compete with negative scores,
+      // whose keys do not order like the scores: settle those exactly
+      const bool finite = __builtin_isfinite(bv) && __builtin_isfinite(zz[c]) &&
+                          __builtin_isfinite(lim) && lim > 0.f;
+      const bool certain = finite && hid == 0 && ncand == 1;
+      const bool full = !finite || hid != 0;
+      res[c] = n1;
+
+      uint64_t need = __builtin_amdgcn_ballot_w64(lane < 16 && !certain);
+      while (need) {
+        const int jj = __builtin_ctzll(need);
+        need &= need - 1;
+        const int b = NB == 1 ? 0 : (c % NB);
+        const int vec = NB == 1 ? 16 * c + jj : 16 * (c / NB) + jj;
+        const int64_t row = vbase + vec;
+        if (row >= n) continue;
+        const bool col_full = __builtin_amdgcn_readlane((int)full, jj) != 0;
+        const float col_lim = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(lim), jj));
+        // exact z block: lane t < K holds z_t
+        const TX* xr = x + row * a.ld;
+        const double xv = (double)(float)xr[lane];
+        const double nu = sqrt(wave_sum_f64(xv * xv));
+        sX[lane] = xv;
+        wave_lds_sync();
+        double zd = 0.0;
+        if (lane < K) {
+          const double* pr = a.pi64 + (size_t)(b * K + lane) * D;
+          double acc = 0.0;
+          for (int i = 0; i < D; ++i) acc = fma(pr[i], sX[i], acc);
+          zd = acc / nu;   // a zero vector gives NaN: every distance is NaN, index 0
+        }
+        sZd[lane] = zd;
+        wave_lds_sync();
+        double best = INFINITY;
+        int bi = 0;
+        if (!col_full) {
+          // the slot leaders within the margin, each scored by the whole wave
+#pragma unroll
+          for (int lg = 0; lg < 4; ++lg)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int key = __builtin_amdgcn_readlane(m1[c][r], 16 * lg + jj);
+              if (key_value(key) >= col_lim) {
+                const int cn = 16 * (int)key_tile(key) + 4 * lg + r;
+                const double df = lane < K ? zd + 0.5 * (double)a.enc[(size_t)cn * a.S + lane] : 0.0;
+                const double dd = wave_sum_f64(df * df);
+                if (dd < best || (dd == best && cn < bi)) {
+                  best = dd;
+                  bi = cn;
+                }
+              }
+            }
+        } else {
+          // every codeword: lane l takes l, l + 64, ...; lowest index on ties
+          for (int cn = lane; cn < LN; cn += 64) {
+            const float* er = a.enc + (size_t)cn * a.S;
+            double dd = 0.0;
+            for (int t2 = 0; t2 < K; ++t2) {
+              const double df = sZd[t2] + 0.5 * (double)er[t2];
+              dd = fma(df, df, dd);
+            }
+            if (dd < best) {
+              best = dd;
+              bi = cn;
+            }
+          }
+#pragma unroll
+          for (int m = 32; m >= 1; m >>= 1) {
+            const double ob = shfl_xor_f64(best, m);
+            const int oi = __shfl_xor(bi, m, 64);
+            if (ob < best || (ob == best && oi < bi)) {
+              best = ob;
+              bi = oi;
+            }
+          }
+        }
+        if ((lane & 15) == jj) res[c] = bi;
+        wave_lds_sync();
+      }
+    }
+
+    // ---- records: lane l writes vector l of the wave (k = 64) or, for
+    //      l < 32, vector l with fields from groups 2 (l / 16) and + 1 (k = 32)
+    if constexpr (NB == 1) {
+      const int row_in = lane;
+      const int v0 = res[0], v1 = res[1], v2 = res[2], v3 = res[3];
+      const int vv = grp == 0 ? v0 : (grp == 1 ? v1 : (grp == 2 ? v2 : v3));
+      if (vbase + row_in < n) a.codes[vbase + row_in] = (uint32_t)vv;
+    } else {
+      const int h = grp & 1;
+      const uint32_t f0 = (uint32_t)(h == 0 ? res[0] : res[2]);
+      const uint32_t f1 = (uint32_t)(h == 0 ? res[1] : res[3]);
+      if (lane < 32 && vbase + lane < n) a.codes[vbase + lane] = f0 | (f1 << LBITS);
+    }
+  }
+}
+
+template <int K, typename TX>
+hipError_t launch_large_k(const fq_codebook* cb, const TX* x, int64_t n, int64_t ld,
+                          uint32_t* codes, uint16_t* norms, hipStream_t s) {
+  using Sh = LShape<K>;
+  if (cb->N != LN || cb->t.lfrag == nullptr || cb->t.hnorm == nullptr) return hipErrorInvalidValue;
+  auto kern = encode_large_kernel<K, TX>;
+  const size_t shm = Sh::LDS;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  if (e != hipSuccess) return e;
+  static const int64_t cap = resident_blocks(reinterpret_cast<const void*>(kern), LW * 64, shm);
+  if (cap <= 0) return hipErrorInvalidConfiguration;
+  const int64_t wg_vecs = (int64_t)LW * Sh::VPW;
+  int64_t blocks = (n + wg_vecs - 1) / wg_vecs;
+  if (blocks > cap) blocks = cap;
+  LArgs a;
+  a.x = x;
+  a.n = n;
+  a.ld = ld;
+  a.codes = codes;
+  a.norms = norms;
+  a.rotfrag = cb->t.encfrag;
+  a.lfrag = cb->t.lfrag;
+  a.hn = cb->t.hnorm;
+  a.enc = cb->t.enc;
+  a.S = cb->enc_stride;
+  a.pi64 = cb->t.pi64;
+  // certification constants (bounds in the header), from the largest codeword norm
+  const double cm = cb->cmax, kk = K;
+  const double acc = (2.0 * kk + 2.0) * 0x1p-23;
+  a.EA = (float)(cm * (0x1p-22 + acc * 1.001) * 1.01);
+  a.EB = (float)((0x1p-25 * sqrt(kk) * cm + (acc + 0x1p-24) * cm * cm * 0.5) * 1.01);
+  const double ez = sizeof(TX) == 2 ? cb->enc_ez16 : cb->enc_ez32;
+  a.ZT = (float)(2.0 * ez * sqrt(kk) * cm * 1.01);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(LW * 64), shm, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_encode_large(const fq_codebook* cb, const void* x, fq_dtype xt, int64_t n,
+                               int64_t ld, uint32_t* codes, uint16_t* norms, hipStream_t s) {
+  if (xt == FQ_F16) {
+    const _Float16* xx = static_cast<const _Float16*>(x);
+    if (cb->k == 32) return launch_large_k<32, _Float16>(cb, xx, n, ld, codes, norms, s);
+    if (cb->k == 64) return launch_large_k<64, _Float16>(cb, xx, n, ld, codes, norms, s);
+  } else {
+    const float* xx = static_cast<const float*>(x);
+    if (cb->k == 32) return launch_large_k<32, float>(cb, xx, n, ld, codes, norms, s);
+    if (cb->k == 64) return launch_large_k<64, float>(cb, xx, n, ld, codes, norms, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fq

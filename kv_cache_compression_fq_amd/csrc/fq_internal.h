@@ -20,12 +20,20 @@ constexpr int MAX_WORDS = 12;     // record words for k >= 2, N <= 4096: ceil(32
 #define FQ_VARIANTS(X) \
   X(2, 4) X(2, 5) X(2, 6) X(2, 7) X(2, 8) X(3, 9) X(3, 12) X(4, 2) X(4, 8) X(8, 4) X(8, 8)
 
+// Large blocks (k = d/2 and k = d, N = 4096): the table exceeds LDS, so they
+// have their own encode kernel (fq_encode_large.hip) and a decode that gathers
+// codewords from the L2-resident table.
+#define FQ_VARIANTS_LARGE(X) X(32, 12) X(64, 12)
+
 inline bool variant_supported(int k, int bits) {
 #define FQ_IS(KK, BB) if (k == KK && bits == BB) return true;
   FQ_VARIANTS(FQ_IS)
+  FQ_VARIANTS_LARGE(FQ_IS)
 #undef FQ_IS
   return false;
 }
+
+__host__ __device__ constexpr bool large_block(int k) { return k >= 32; }
 
 // Per-codebook device tables, all inside one allocation.
 struct DeviceTables {
@@ -42,6 +50,9 @@ struct DeviceTables {
   _Float16* encfrag; // Pi hi / lo as v_mfma_f32_16x16x16_f16 A fragments (encode)
   uint16_t* grid;     // k = 2, 3: candidate records of the block grid (fq_grid.cpp)
   uint16_t* grid1;    // k = 3: candidate records of the one-coordinate last block
+  _Float16* lfrag;    // k >= 32: codebook as v_mfma_f32_16x16x32_f16 A fragments,
+                      // [tile][kc][lane][8] = C[16 tile + lane % 16][32 kc + 8 (lane / 16) + e]
+  float* hnorm;       // k >= 32: -|c_n|^2 / 2 in float32
 };
 
 // Candidate-list grids for the block search (fq_grid.cpp).
@@ -78,6 +89,7 @@ struct fq_codebook {
   int grid_G;       // cells per dimension of the block grid (0: no grid, full scan)
   int grid1_G;      // cells of the last-block grid (k = 3)
   bool half_exact;  // every codeword coordinate is a binary16 number
+  double cmax;      // largest codeword norm
   std::vector<double> pi;  // host copy of Pi
   std::vector<float> c;    // host copy of C
   void* dev_block;         // the single device allocation
@@ -91,6 +103,8 @@ namespace fq {
 // the caller; pointers are device pointers.
 hipError_t launch_encode(const fq_codebook* cb, const void* x, fq_dtype xt, int64_t n,
                          int64_t ld, uint32_t* codes, uint16_t* norms, hipStream_t s);
+hipError_t launch_encode_large(const fq_codebook* cb, const void* x, fq_dtype xt, int64_t n,
+                               int64_t ld, uint32_t* codes, uint16_t* norms, hipStream_t s);
 hipError_t launch_decode(const fq_codebook* cb, const uint32_t* codes, const uint16_t* norms,
                          const int64_t* rows, int64_t n_records, int64_t n, void* y,
                          fq_dtype yt, int64_t ld, hipStream_t s);

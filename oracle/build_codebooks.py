@@ -15,7 +15,12 @@ import time
 from . import artifact, codebook, rotation
 
 VARIANTS = [(2, 16), (2, 64), (2, 256), (3, 512), (4, 256), (8, 256), (8, 16), (4, 4),
-            (3, 4096), (2, 32), (2, 128)]
+            (3, 4096), (2, 32), (2, 128), (32, 4096), (64, 4096)]
+# Large-k codebooks (k = d/2 and k = d, N = 4096): one Lloyd iteration costs
+# about N k times a k = 2 one, so they train on 2^18 samples with 2 restarts
+# and at most 30 iterations (recorded in the artifact header).
+LARGE = {(32, 4096): dict(samples=1 << 18, restarts=2, max_iter=30),
+         (64, 4096): dict(samples=1 << 18, restarts=2, max_iter=30)}
 D = 64
 OUT_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                        "kv_cache_compression_fq_amd", "codebooks")
@@ -28,8 +33,9 @@ def artifact_name(k, N):
 def build_one(k, N, samples, restarts, out_dir, log):
     Pi = rotation.make_rotation(D, rotation.SEED_ROT)
     t0 = time.time()
-    book = codebook.build_codebook(D, k, N, restarts=restarts, samples=samples,
-                                   test_samples=samples, log=log)
+    opts = dict(samples=samples, restarts=restarts)
+    opts.update(LARGE.get((k, N), {}))
+    book = codebook.build_codebook(D, k, N, test_samples=opts["samples"], log=log, **opts)
     book["seed_rot"] = rotation.SEED_ROT
     book["law_a"], book["law_b"] = codebook.radius_law(D, k)
     blob = artifact.write_artifact(Pi, book)

@@ -109,6 +109,8 @@ def encode(x, Pi, C, chunk=2048):
     nb = -(-d // k)
     idx = np.zeros((n, nb), dtype=np.int64)
     nu_all = np.zeros(n)
+    # bound the [chunk, N, k] difference array (large codebooks, large k)
+    chunk = max(1, min(chunk, (1 << 25) // (N * k)))
     for s in range(0, n, chunk):
         nu, z = rotate_units(x[s:s + chunk], Pi)
         nu_all[s:s + chunk] = nu
@@ -130,6 +132,7 @@ def accept_indices(x, Pi, C, got, window=1e-6, chunk=2048):
     N, k = C.shape
     nb = got.shape[1]
     exact = window_ok = bad = 0
+    chunk = max(1, min(chunk, (1 << 25) // (N * k)))
     for s in range(0, n, chunk):
         nu, z = rotate_units(x[s:s + chunk], Pi)
         g = got[s:s + chunk]

@@ -100,6 +100,51 @@ def test_encode_variants_fp16(dev, k, N):
     print(f"k{k}N{N}: {ex} exact, {win} in window")
 
 
+@pytest.mark.parametrize("k", [32, 64])
+def test_encode_large_blocks_fp32_and_tiny(dev, k):
+    """k = 32 / 64, N = 4096 (matrix-core search): float32 input with the
+    special vectors, then inputs shorter than one wave's share (5 rows) and one
+    row past a workgroup's share (513 rows)."""
+    art, cb = book(k, 4096)
+    x = np.concatenate([synth.tiny_vectors(700, seed=3), synth.special_vectors(dtype=np.float32)])
+    codes, norms = gpu_encode(cb, x, dev)
+    ex, win = check_encode(art, x, codes, norms)
+    for m in (5, 513):
+        xs = synth.kv_slab(2, 1, 0, 1, 1, m).reshape(-1, 64)
+        c, nn = gpu_encode(cb, xs, dev)
+        check_encode(art, xs, c, nn)
+    print(f"k{k}N4096 fp32: {ex} exact, {win} in window")
+
+
+@pytest.mark.parametrize("k", [32, 64])
+def test_large_blocks_gpt2_cache_full_size(dev, k):
+    """k = 32 / 64, N = 4096 on the whole GPT-2-small-shaped cache in the bench's
+    launch configuration: 2048 sampled rows against the oracle, every norm and
+    pad bit, and the decode of the sampled records."""
+    print(f"gpt2 cache k{k}N4096", flush=True)
+    art, cb = book(k, 4096)
+    x = gpt2_cache()
+    n = len(x)
+    xd = to_dev(x, dev)
+    codes, norms = fq.fq_encode(cb, xd)
+    y = fq.fq_decode(cb, codes, norms)
+    torch.cuda.synchronize()
+    assert pad_bits_zero(art, codes)
+    all_norms_ok(xd, norms)
+    rows = sample_rows(n, 2048, seed=k * 1000 + 4096)
+    rt = torch.from_numpy(rows).to(dev)
+    c_s = codes[rt].cpu().numpy().view(np.uint32)
+    n_s = norms[rt].cpu().numpy().view(np.uint16)
+    ex, win = check_encode(art, x[rows], c_s, n_s)
+    want = codec.decode(codec.unpack(c_s, art["nb"], art["bits"]), n_s, art["Pi"], art["C"])
+    got = y[rt].float().cpu().numpy().astype(np.float64)
+    nu16 = codec.f16_value(n_s)
+    err = np.max(np.abs(got - want), axis=1)
+    assert np.all(err <= 1e-3 * nu16 + 1e-30)
+    print(f"k{k}N4096: {n} vectors; sampled {len(rows)}: {ex} exact, {win} in window, "
+          f"decode max err/nu {np.max(err / np.maximum(nu16, 1e-30)):.2e}")
+
+
 def test_encode_strided_rows_and_empty(dev):
     art, cb = book(3, 512)
     x = synth.kv_slab(2, 1, 1, 1, 2, 300).reshape(-1, 64)
@@ -234,6 +279,12 @@ def test_attention_rejects_unsupported(dev):
     assert e.value.status == fq.FQ_ERR_UNSUPPORTED
     with pytest.raises((fq.FQError, ValueError)):   # K and V codebooks of different variants
         fq.fq_attend_decode(c4, c2, q[:, :8], kw, nn, kw, nn, 0.125)
+    _, c64 = book(64, 4096)                          # table larger than LDS
+    q8 = torch.zeros((1, 8, 64), dtype=torch.float16, device=dev)
+    k1 = torch.zeros((1, 1, 8, c64.W), dtype=torch.int32, device=dev)
+    with pytest.raises(fq.FQError) as e:
+        fq.fq_attend_decode(c64, c64, q8, k1, nn, k1, nn, 0.125)
+    assert e.value.status == fq.FQ_ERR_UNSUPPORTED
 
 
 def test_attention_tinyllama_sampled(dev):

@@ -102,7 +102,7 @@ def test_sub_one_bit_band(k, N):
     assert 0.5 <= a["D_test"] < 1.0
 
 
-@pytest.mark.parametrize("k,N", [(2, 16), (2, 256), (3, 512)])
+@pytest.mark.parametrize("k,N", [(2, 16), (2, 256), (3, 512), (32, 4096), (64, 4096)])
 def test_recorded_distortion_reproduces(k, N):
     a = load(k, N)
     C = a["C"].astype(np.float64)
@@ -112,6 +112,25 @@ def test_recorded_distortion_reproduces(k, N):
     _, d2 = codebook.nearest(C, X)
     se = a["nb"] * float(np.std(d2)) / math.sqrt(len(d2))
     assert abs(D - a["D_test"]) < 6 * se + 1e-12, (D, a["D_test"], se)
+
+
+def test_large_block_codes():
+    # k = d: the block is the whole unit vector, so the source has radius 1
+    # exactly; k = d/2 doubles the rate of k = d at the same N, so it must
+    # quantise better; both are coarser than any code at one bit per coordinate
+    X = source.sample_blocks(64, 64, 1000, [1, 2, 3])
+    assert np.allclose(np.linalg.norm(X, axis=1), 1.0, rtol=0, atol=1e-12)
+    D32, D64 = load(32, 4096)["D_test"], load(64, 4096)["D_test"]
+    assert D32 < D64 < 1.0
+    assert D32 > load(8, 256)["D_test"]
+    # the nearest-codeword search of the large tables (matrix-product form)
+    # against plain squared distances on a tiny input
+    C = load(64, 4096)["C"].astype(np.float64)
+    Y = source.sample_blocks(64, 64, 64, [4, 5, 6])
+    idx, d2 = codebook.nearest(C, Y)
+    full = np.sum((Y[:, None, :] - C[None, :, :]) ** 2, axis=2)
+    assert np.array_equal(idx, np.argmin(full, axis=1))
+    assert np.allclose(d2, np.min(full, axis=1), rtol=1e-12, atol=0)
 
 
 def test_k2_distortion_falls_with_every_added_bit_half():
