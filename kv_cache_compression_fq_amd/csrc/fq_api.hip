@@ -298,7 +298,8 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
                o_efrag = take(2ull * efrag.size()),
                o_grid = take(2ull * grid.rec.size() + 64), o_grid1 = take(2ull * grid1.rec.size() + 64),
                o_pih = take(2ull * d * d), o_pil = take(2ull * d * d), o_pit = take(4ull * d * d),
-               o_lfrag = take(2ull * lfrag.size()), o_hn = take(4ull * hnorm.size());
+               o_lfrag = take(2ull * lfrag.size()), o_hn = take(4ull * hnorm.size()),
+               o_pi64t = take(8ull * d * d);
   cb->dev_bytes = off;
   {
     DeviceGuard g(device);
@@ -313,6 +314,7 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
     }
     char* base = static_cast<char*>(cb->dev_block);
     cb->t.pi64 = reinterpret_cast<double*>(base + o_pi64);
+    cb->t.pi64t = reinterpret_cast<double*>(base + o_pi64t);
     cb->t.pi32 = reinterpret_cast<float*>(base + o_pi32);
     cb->t.enc = reinterpret_cast<float*>(base + o_enc);
     cb->t.cb16hi = reinterpret_cast<_Float16*>(base + o_cbh);
@@ -337,8 +339,10 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
     memcpy(staging.data() + o_pih, pih.data(), 2ull * d * d);
     memcpy(staging.data() + o_pil, pil.data(), 2ull * d * d);
     for (int i = 0; i < d; ++i)
-      for (int j = 0; j < d; ++j)
+      for (int j = 0; j < d; ++j) {
         reinterpret_cast<float*>(staging.data() + o_pit)[(size_t)j * d + i] = pi32[(size_t)i * d + j];
+        reinterpret_cast<double*>(staging.data() + o_pi64t)[(size_t)j * d + i] = cb->pi[(size_t)i * d + j];
+      }
     if (!lfrag.empty()) memcpy(staging.data() + o_lfrag, lfrag.data(), 2ull * lfrag.size());
     if (!hnorm.empty()) memcpy(staging.data() + o_hn, hnorm.data(), 4ull * hnorm.size());
     if (!grid.rec.empty()) memcpy(staging.data() + o_grid, grid.rec.data(), 2ull * grid.rec.size());

@@ -31,10 +31,15 @@
 //    A codeword whose key is more than M below the best key cannot be the
 //    exact nearest.  When the best key exceeds M, only the best slot is
 //    within M and no slot's second key is, the float32 winner is final.
-//  * Otherwise the block is settled exactly in float64 by the whole wave:
-//    z's block from x and the float64 Pi, then the candidates (the slot
-//    leaders within M) or, when a slot may hide a further candidate, all N
-//    codewords; ties go to the lowest index.
+//  * Otherwise the block goes to the wave's list (its row, its candidates:
+//    the slot leaders within M, and the slots whose second key is within M)
+//    and its record keeps the float32 winner for now.  After the last pass
+//    the workgroup settles its lists exactly in float64, shared out over its
+//    waves: z's block from x and the float64 Pi, then the candidates and every
+//    codeword of each such slot (all N codewords for non-finite scores or
+//    more than 8 candidates); ties go to the lowest index; the exact index
+//    replaces the field.  A list that could overflow during a pass is
+//    settled at the start of the pass instead.
 //  * Records (one 32-bit word: one or two 12-bit fields) and norms are
 //    written with coalesced stores.
 #include "fq_common.h"
@@ -52,6 +57,13 @@ constexpr int TCW = 256;     // codewords per LDS stage
 constexpr int LBITS = 12;    // log2 N
 constexpr int LN = 1 << LBITS;
 constexpr int NSTAGE = LN / TCW;
+// Uncertain blocks listed per wave: row (2 words), block | count << 8 |
+// all-codewords flag << 16, hidden-slot mask, up to 8 candidate indices
+// (u16; more set the all-codewords flag).  A pass adds at most 64 entries,
+// so the list is settled early when fewer than 64 places are left.
+constexpr int FL_MAX = 84;
+constexpr int FL_WORDS = 8;
+constexpr int FL_CAND = 8;
 
 template <int K>
 struct LShape {
@@ -61,8 +73,8 @@ struct LShape {
   static constexpr int BATCHES = VPW / EV;         // rotation batches of 16 vectors per pass
   static constexpr int STAGE_BYTES = TCW * K * 2;  // one stage of codebook fragments
   static constexpr int LOADS = STAGE_BYTES / (16 * LW * 64);   // 16-byte loads per thread
-  static constexpr size_t WAVE_BYTES = (size_t)EV * ZP * 4 + 2 * 64 * 8;
-  static constexpr size_t LDS = 2 * (size_t)STAGE_BYTES + LN * 4 + ROT_BYTES + LW * WAVE_BYTES;
+  static constexpr size_t WAVE_BYTES = (size_t)EV * ZP * 4 + 2 * 64 * 8 + FL_MAX * FL_WORDS * 4;
+  static constexpr size_t LDS = 2 * (size_t)STAGE_BYTES + LN * 4 + ROT_BYTES + LW * WAVE_BYTES + LW * 4;
 };
 
 struct LArgs {
@@ -73,9 +85,10 @@ struct LArgs {
   const _Float16* rotfrag;  // Pi hi / lo as 16x16x16 A fragments
   const _Float16* lfrag;    // codebook as 16x16x32 A fragments [tile][kc][lane][8]
   const float* hn;          // -|c_n|^2 / 2, float32
+  const _Float16* cbh;      // [N][k] codebook, binary16 (exact)
   const float* enc;         // [N + 1][S] search table (-2 c, |c|^2): c = -enc / 2 exactly
   int S;
-  const double* pi64;
+  const double* pi64t;       // Pi^T, float64
   float EA, EB, ZT;         // certification constants (see the header)
 };
 
@@ -91,6 +104,110 @@ __device__ inline double wave_sum_f64(double v) {
 __device__ inline uint32_t key_tile(int key) { return (uint32_t)key & 0xFFu; }
 __device__ inline float key_value(int key) { return __int_as_float(key); }
 
+// The exact nearest codeword of one listed block (the whole wave): z's block
+// in float64 from x and Pi (lane t < k holds z_t), then float64 distances to
+// the listed candidates, to every codeword 16 t + s of each hidden slot s,
+// or to all N codewords; ties to the lowest index.
+template <int K, typename TX>
+__device__ int settle_block(const LArgs& a, const TX* x, const uint32_t* ent, double* sX,
+                            double* sZd, int lane) {
+  const int64_t row = (int64_t)((uint64_t)ent[0] | ((uint64_t)ent[1] << 32));
+  const uint32_t info = ent[2], hm = ent[3];
+  const int b = (int)(info & 0xFFu), nc = (int)((info >> 8) & 0xFFu);
+  const bool full = (info >> 16) & 1u;
+  const uint16_t* ce = reinterpret_cast<const uint16_t*>(ent + 4);
+  // every load first (the block is latency-bound): x, column b K + t of Pi^T
+  // (row b K + t of Pi, one coalesced line per i) and the candidates' rows
+  const double xv = (double)(float)x[row * a.ld + lane];
+  const double* pt = a.pi64t + b * K + (lane < K ? lane : 0);
+  constexpr int PH = D / 2;   // Pi^T lines per batch of loads
+  double pv[PH];
+#pragma unroll
+  for (int i = 0; i < PH; ++i) pv[i] = pt[(size_t)i * D];
+  float cv[FL_CAND];
+#pragma unroll
+  for (int e = 0; e < FL_CAND; ++e)
+    cv[e] = (!full && e < nc && lane < K) ? a.enc[(size_t)ce[e] * a.S + lane] : 0.f;
+  const double nu = sqrt(wave_sum_f64(xv * xv));
+  sX[lane] = xv;
+  wave_lds_sync();
+  double acc = 0.0;
+#pragma unroll
+  for (int i = 0; i < PH; ++i) acc = fma(pv[i], sX[i], acc);
+#pragma unroll
+  for (int i = 0; i < PH; ++i) pv[i] = pt[(size_t)(PH + i) * D];
+#pragma unroll
+  for (int i = 0; i < PH; ++i) acc = fma(pv[i], sX[PH + i], acc);
+  const double zd = lane < K ? acc / nu : 0.0;   // a zero vector gives NaN: index 0
+  sZd[lane] = zd;
+  wave_lds_sync();
+  double best = INFINITY;
+  int bi = 0;
+  auto dist = [&](int cn) {   // this lane's codeword, all k coordinates (binary16, exact)
+    const half8* cr = reinterpret_cast<const half8*>(a.cbh + (size_t)cn * K);
+    half8 hv[K / 8];
+#pragma unroll
+    for (int q = 0; q < K / 8; ++q) hv[q] = cr[q];
+    double dd = 0.0;
+#pragma unroll
+    for (int q = 0; q < K / 8; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const double df = sZd[8 * q + e] - (double)(float)hv[q][e];
+        dd = fma(df, df, dd);
+      }
+    return dd;
+  };
+  if (!full) {
+#pragma unroll
+    for (int e = 0; e < FL_CAND; ++e) {
+      if (e < nc) {
+        const int cn = ce[e];
+        const double df = lane < K ? zd + 0.5 * (double)cv[e] : 0.0;   // c = -enc / 2, exact
+        const double dd = wave_sum_f64(df * df);
+        if (dd < best || (dd == best && cn < bi)) {
+          best = dd;
+          bi = cn;
+        }
+      }
+    }
+    uint32_t h = hm;
+    while (h) {
+      const int slot = __builtin_ctz(h);
+      h &= h - 1;
+#pragma unroll 1
+      for (int m = 0; m < LN / 16 / 64; ++m) {
+        const int cn = 16 * (lane + 64 * m) + slot;
+        const double dd = dist(cn);
+        if (dd < best || (dd == best && cn < bi)) {
+          best = dd;
+          bi = cn;
+        }
+      }
+    }
+  } else {
+#pragma unroll 1
+    for (int cn = lane; cn < LN; cn += 64) {
+      const double dd = dist(cn);
+      if (dd < best) {
+        best = dd;
+        bi = cn;
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const double ob = shfl_xor_f64(best, m);
+    const int oi = __shfl_xor(bi, m, 64);
+    if (ob < best || (ob == best && oi < bi)) {
+      best = ob;
+      bi = oi;
+    }
+  }
+  wave_lds_sync();
+  return bi;
+}
+
 template <int K, typename TX>
 __global__ __launch_bounds__(LW * 64) void encode_large_kernel(LArgs a) {
   using Sh = LShape<K>;
@@ -104,6 +221,10 @@ __global__ __launch_bounds__(LW * 64) void encode_large_kernel(LArgs a) {
   float* sZ = reinterpret_cast<float*>(wb);                               // [EV][ZP]
   double* sX = reinterpret_cast<double*>(wb + EV * ZP * 4);              // exact path: x
   double* sZd = sX + 64;                                                  // exact path: z block
+  uint32_t* sList = reinterpret_cast<uint32_t*>(sZd + 64);                // uncertain blocks
+  int* sCount = reinterpret_cast<int*>(smem + 2 * Sh::STAGE_BYTES + LN * 4 + ROT_BYTES +
+                                       LW * Sh::WAVE_BYTES);              // list lengths
+  int nfl = 0;
   const int j = lane & 15, grp = lane >> 4;
 
   for (int i = threadIdx.x; i < ROT_BYTES / 16; i += blockDim.x)
@@ -123,8 +244,36 @@ __global__ __launch_bounds__(LW * 64) void encode_large_kernel(LArgs a) {
   const int64_t passes = (n + wg_vecs - 1) / wg_vecs;
   int sbuf = 0;
 
+  // the lane's x row of batch h of pass gp (rows past the end repeat the last one)
+  auto xrow = [&](int64_t gp, int h) {
+    const int64_t row0 = gp * wg_vecs + (int64_t)wave * Sh::VPW + EV * h;
+    const int64_t last = n - 1 - row0;
+    return x + (last < 0 ? n - 1 : row0 + (j < last ? j : last)) * a.ld;
+  };
+  // x of the next batch is always in flight: batch h + 1 while batch h is
+  // rotated, the next pass's batch 0 during the last codebook stage
+  XRaw<TX> xnext;
+  if (blockIdx.x < passes) load_raw<TX>(xrow(blockIdx.x, 0), grp, xnext);
+
+  // settle one listed block and replace its field of the record
+  auto settle_fix = [&](const uint32_t* ent) {
+    const int bi = settle_block<K, TX>(a, x, ent, sX, sZd, lane);
+    if (lane == 0) {
+      const int64_t row = (int64_t)((uint64_t)ent[0] | ((uint64_t)ent[1] << 32));
+      const int sh = LBITS * (int)(ent[2] & 0xFFu);
+      uint32_t* rp = a.codes + row;
+      atomicAnd(rp, ~(((uint32_t)LN - 1u) << sh));
+      atomicOr(rp, (uint32_t)bi << sh);
+    }
+  };
+
   for (int64_t gp = blockIdx.x; gp < passes; gp += gridDim.x) {
     const int64_t vbase = gp * wg_vecs + (int64_t)wave * Sh::VPW;
+    if (nfl > FL_MAX - 16 * CG) {   // room for this pass's blocks: settle the list now
+      __builtin_amdgcn_s_waitcnt(0);   // this wave's record stores have completed
+      for (int e = 0; e < nfl; ++e) settle_fix(sList + e * FL_WORDS);
+      nfl = 0;
+    }
 
     // ---- norm, rotation and B operands of the wave's 64 columns.  Column
     //      group c = h NB + b holds block b of batch h (vectors 16 h .. + 15).
@@ -133,11 +282,9 @@ __global__ __launch_bounds__(LW * 64) void encode_large_kernel(LArgs a) {
 #pragma unroll
     for (int h = 0; h < Sh::BATCHES; ++h) {
       const int64_t row0 = vbase + EV * h;
-      const int64_t last = n - 1 - row0;   // rows past the end repeat the last one
-      const TX* xr = x + (row0 + (j < last ? j : (last < 0 ? 0 : last))) * a.ld;
-      if (last < 0) xr = x + (n - 1) * a.ld;
-      XRaw<TX> xraw;
-      load_raw<TX>(xr, grp, xraw);
+      const int64_t last = n - 1 - row0;
+      const XRaw<TX> xraw = xnext;
+      if (h + 1 < Sh::BATCHES) load_raw<TX>(xrow(gp, h + 1), grp, xnext);
       XFrag<TX> xf;
       finish_x<TX>(xraw, xf);
       const float nus = __builtin_amdgcn_sqrtf(xf.ss);
@@ -177,20 +324,26 @@ __global__ __launch_bounds__(LW * 64) void encode_large_kernel(LArgs a) {
       for (int r = 0; r < 4; ++r) m1[c][r] = m2[c][r] = INT32_MIN;
     for (int s = 0; s < NSTAGE; ++s) {
       // next stage (cyclic: the last one fetches stage 0 of the next pass)
-      u32x4 pre[Sh::LOADS];
+      // straight into the other LDS buffer (free since the last barrier):
+      // lane l of a wave writes 16 bytes at the wave's base + 16 l
       const int sn = s + 1 < NSTAGE ? s + 1 : 0;
+      if (s == NSTAGE - 1 && gp + gridDim.x < passes) load_raw<TX>(xrow(gp + gridDim.x, 0), grp, xnext);
 #pragma unroll
-      for (int u = 0; u < Sh::LOADS; ++u) pre[u] = gfrag[sn * STAGE_Q + threadIdx.x + LW * 64 * u];
+      for (int u = 0; u < Sh::LOADS; ++u) {
+        const int piece = LW * 64 * u + 64 * wave;
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(gfrag + sn * STAGE_Q + piece + lane),
+            (__attribute__((address_space(3))) void*)(sStage + (sbuf ^ 1) * Sh::STAGE_BYTES + 16 * piece),
+            16, 0, 0);
+      }
       const unsigned char* st = sStage + sbuf * Sh::STAGE_BYTES;
-#pragma unroll 2
-      for (int i = 0; i < TCW / 16; ++i) {
-        const uint32_t t = (uint32_t)(16 * s + i);
+      // scores of codeword tile i (16 codewords) for the wave's 64 columns
+      auto scores = [&](int i, floatx4 (&acc)[CG]) {
         half8 av[KC];
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc)
           av[kc] = *reinterpret_cast<const half8*>(st + ((i * KC + kc) * 64 + lane) * 16);
-        const floatx4 c0 = *reinterpret_cast<const floatx4*>(sHn + 16 * t + 4 * grp);
-        floatx4 acc[CG];
+        const floatx4 c0 = *reinterpret_cast<const floatx4*>(sHn + 16 * (16 * s + i) + 4 * grp);
 #pragma unroll
         for (int c = 0; c < CG; ++c) acc[c] = c0;
 #pragma unroll
@@ -202,6 +355,9 @@ __global__ __launch_bounds__(LW * 64) void encode_large_kernel(LArgs a) {
           for (int c = 0; c < CG; ++c)
             acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[kc], bl[c][kc], acc[c], 0, 0, 0);
         }
+      };
+      auto track = [&](const floatx4 (&acc)[CG], int i) {
+        const uint32_t t = (uint32_t)(16 * s + i);
 #pragma unroll
         for (int c = 0; c < CG; ++c)
 #pragma unroll
@@ -212,11 +368,31 @@ __global__ __launch_bounds__(LW * 64) void encode_large_kernel(LArgs a) {
             m2[c][r] = max(min(m1[c][r], m2[c][r]), min(max(m1[c][r], m2[c][r]), key));
             m1[c][r] = max(m1[c][r], key);
           }
-      }
+      };
+      // software pipeline: the key updates of tile i - 1 run in the shadow of
+      // tile i's matrix-core work (one MFMA, then VALU work, in turn)
+      constexpr int NM = 2 * KC * CG;        // MFMAs per tile
+      constexpr int NV = 3 * 4 * CG;         // VALU operations per tile
+      floatx4 accA[CG], accB[CG];
+      scores(0, accA);
 #pragma unroll
-      for (int u = 0; u < Sh::LOADS; ++u)
-        reinterpret_cast<u32x4*>(sStage + (sbuf ^ 1) * Sh::STAGE_BYTES)[threadIdx.x + LW * 64 * u] =
-            pre[u];
+      for (int i = 1; i < TCW / 16; ++i) {
+        if (i & 1) {
+          scores(i, accB);
+          track(accA, i - 1);
+        } else {
+          scores(i, accA);
+          track(accB, i - 1);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, KC + 1, 0);   // this tile's LDS reads
+#pragma unroll
+        for (int u = 0; u < NM; ++u) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, NV / NM, 0);
+        }
+      }
+      track(accB, TCW / 16 - 1);
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the stage has landed in LDS
       __syncthreads();
       sbuf ^= 1;
     }
@@ -270,6 +446,9 @@ __global__ __launch_bounds__(LW * 64) void encode_large_kernel(LArgs a) {
       const bool full = !finite || hid != 0;
       res[c] = n1;
 
+      // uncertain blocks: their candidates go to the wave's list and are
+      // settled after the last pass (no workgroup waits on them); the
+      // record gets the float32 winner meanwhile
       uint64_t need = __builtin_amdgcn_ballot_w64(lane < 16 && !certain);
       while (need) {
         const int jj = __builtin_ctzll(need);
@@ -280,66 +459,33 @@ __global__ __launch_bounds__(LW * 64) void encode_large_kernel(LArgs a) {
         if (row >= n) continue;
         const bool col_full = __builtin_amdgcn_readlane((int)full, jj) != 0;
         const float col_lim = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(lim), jj));
-        // exact z block: lane t < K holds z_t
-        const TX* xr = x + row * a.ld;
-        const double xv = (double)(float)xr[lane];
-        const double nu = sqrt(wave_sum_f64(xv * xv));
-        sX[lane] = xv;
-        wave_lds_sync();
-        double zd = 0.0;
-        if (lane < K) {
-          const double* pr = a.pi64 + (size_t)(b * K + lane) * D;
-          double acc = 0.0;
-          for (int i = 0; i < D; ++i) acc = fma(pr[i], sX[i], acc);
-          zd = acc / nu;   // a zero vector gives NaN: every distance is NaN, index 0
-        }
-        sZd[lane] = zd;
-        wave_lds_sync();
-        double best = INFINITY;
-        int bi = 0;
+        uint32_t* ent = sList + nfl * FL_WORDS;
+        uint16_t* ce = reinterpret_cast<uint16_t*>(ent + 4);
+        int nc = 0;
+        uint32_t hm = 0;
         if (!col_full) {
-          // the slot leaders within the margin, each scored by the whole wave
 #pragma unroll
           for (int lg = 0; lg < 4; ++lg)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int key = __builtin_amdgcn_readlane(m1[c][r], 16 * lg + jj);
+              const int key2 = __builtin_amdgcn_readlane(m2[c][r], 16 * lg + jj);
               if (key_value(key) >= col_lim) {
-                const int cn = 16 * (int)key_tile(key) + 4 * lg + r;
-                const double df = lane < K ? zd + 0.5 * (double)a.enc[(size_t)cn * a.S + lane] : 0.0;
-                const double dd = wave_sum_f64(df * df);
-                if (dd < best || (dd == best && cn < bi)) {
-                  best = dd;
-                  bi = cn;
-                }
+                if (lane == 0 && nc < FL_CAND) ce[nc] = (uint16_t)(16 * (int)key_tile(key) + 4 * lg + r);
+                ++nc;
               }
+              if (key_value(key2) >= col_lim) hm |= 1u << (4 * lg + r);
             }
-        } else {
-          // every codeword: lane l takes l, l + 64, ...; lowest index on ties
-          for (int cn = lane; cn < LN; cn += 64) {
-            const float* er = a.enc + (size_t)cn * a.S;
-            double dd = 0.0;
-            for (int t2 = 0; t2 < K; ++t2) {
-              const double df = sZd[t2] + 0.5 * (double)er[t2];
-              dd = fma(df, df, dd);
-            }
-            if (dd < best) {
-              best = dd;
-              bi = cn;
-            }
-          }
-#pragma unroll
-          for (int m = 32; m >= 1; m >>= 1) {
-            const double ob = shfl_xor_f64(best, m);
-            const int oi = __shfl_xor(bi, m, 64);
-            if (ob < best || (ob == best && oi < bi)) {
-              best = ob;
-              bi = oi;
-            }
-          }
         }
-        if ((lane & 15) == jj) res[c] = bi;
+        if (lane == 0) {
+          ent[0] = (uint32_t)row;
+          ent[1] = (uint32_t)(row >> 32);
+          ent[2] = (uint32_t)b | ((uint32_t)(nc < FL_CAND ? nc : FL_CAND) << 8) |
+                   ((col_full || nc > FL_CAND ? 1u : 0u) << 16);
+          ent[3] = hm;
+        }
         wave_lds_sync();
+        ++nfl;
       }
     }
 
@@ -356,6 +502,23 @@ __global__ __launch_bounds__(LW * 64) void encode_large_kernel(LArgs a) {
       const uint32_t f1 = (uint32_t)(h == 0 ? res[1] : res[3]);
       if (lane < 32 && vbase + lane < n) a.codes[vbase + lane] = f0 | (f1 << LBITS);
     }
+  }
+
+  // ---- the workgroup's uncertain blocks, settled exactly and shared out
+  //      over its waves; each replaces its field of a record stored above
+  //      (every wave's stores have completed before the barrier)
+  __builtin_amdgcn_s_waitcnt(0);
+  if (lane == 0) sCount[wave] = nfl;
+  __syncthreads();
+  int tot = 0;
+  for (int w = 0; w < LW; ++w) tot += sCount[w];
+  for (int g = wave; g < tot; g += LW) {
+    int w = 0, e = g;
+    while (e >= sCount[w]) e -= sCount[w++];
+    const uint32_t* ent = reinterpret_cast<const uint32_t*>(
+        reinterpret_cast<const unsigned char*>(sList) + (ptrdiff_t)(w - wave) * (ptrdiff_t)Sh::WAVE_BYTES) +
+        e * FL_WORDS;
+    settle_fix(ent);
   }
 }
 
@@ -383,9 +546,10 @@ hipError_t launch_large_k(const fq_codebook* cb, const TX* x, int64_t n, int64_t
   a.rotfrag = cb->t.encfrag;
   a.lfrag = cb->t.lfrag;
   a.hn = cb->t.hnorm;
+  a.cbh = cb->t.cb16hi;
   a.enc = cb->t.enc;
   a.S = cb->enc_stride;
-  a.pi64 = cb->t.pi64;
+  a.pi64t = cb->t.pi64t;
   // certification constants (bounds in the header), from the largest codeword norm
   const double cm = cb->cmax, kk = K;
   const double acc = (2.0 * kk + 2.0) * 0x1p-23;

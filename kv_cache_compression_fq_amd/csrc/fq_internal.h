@@ -38,6 +38,7 @@ __host__ __device__ constexpr bool large_block(int k) { return k >= 32; }
 // Per-codebook device tables, all inside one allocation.
 struct DeviceTables {
   double* pi64;      // [64][64] Pi, row-major (z = Pi u)
+  double* pi64t;     // [64][64] Pi^T, row-major
   float* pi32;       // [64][64] Pi rounded to float32
   float* pi32t;      // [64][64] Pi^T rounded to float32
   float* enc;        // [N + 1][S] search table: -2 c_0 .. -2 c_{k-1}, |c|^2, zero pad; S =

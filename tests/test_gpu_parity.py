@@ -117,6 +117,21 @@ def test_encode_large_blocks_fp32_and_tiny(dev, k):
 
 
 @pytest.mark.parametrize("k", [32, 64])
+def test_encode_large_blocks_many_uncertain(dev, k):
+    """Runs of zero vectors (every block uncertain: all codewords scanned,
+    index 0) between ordinary rows, more than one pass's worth per wave, so
+    the list of uncertain blocks is settled early as well as at the end."""
+    art, cb = book(k, 4096)
+    xs = synth.kv_slab(2, 3, 1, 1, 1, 9000).reshape(-1, 64).copy()
+    xs[100:700] = 0.0
+    xs[5000:5100] = 0.0
+    codes, norms = gpu_encode(cb, xs, dev)
+    ex, win = check_encode(art, xs, codes, norms)
+    assert np.all(codes[100:700] == 0) and np.all(norms[100:700] == 0)
+    print(f"k{k}N4096 with zero runs: {ex} exact, {win} in window")
+
+
+@pytest.mark.parametrize("k", [32, 64])
 def test_large_blocks_gpt2_cache_full_size(dev, k):
     """k = 32 / 64, N = 4096 on the whole GPT-2-small-shaped cache in the bench's
     launch configuration: 2048 sampled rows against the oracle, every norm and
