@@ -168,6 +168,47 @@ fq_status fq_attend_decode(const fq_codebook* cb_k, const fq_codebook* cb_v, con
                            int Hkv, int64_t T, float scale, void* workspace,
                            size_t workspace_bytes, uint16_t* out, void* stream);
 
+/*
+ * Attention of several queries per head over a compressed cache: the steps on
+ * either side of decode-step attention in a serving loop [FQ 5] (a prefill
+ * chunk, or the draft tokens of speculative decoding).  The M queries of
+ * every head are the last M positions: query m of head h sees tokens
+ * 0 .. T - M + m (causal), with the same scores and softmax as
+ * fq_attend_decode (which is the case M = 1).  Computed by the same kernels,
+ * the M queries of a head taking M of the query columns of its KV head.
+ *
+ *   q        [B, Hq, M, 64] binary16;  out [B, Hq, M, 64] binary16
+ *   k_codes  [B, Hkv, T_ld, Wk], k_norms [B, Hkv, T_ld]: token t of (b, g) is
+ *            record (b Hkv + g) T_ld + t; the first T of each row are read.
+ *   v_codes / v_norms likewise.
+ *   1 <= M <= 8, M <= T <= T_ld < 2^31, (Hq / Hkv) * M <= 8; workspace of at
+ *   least fq_attend_workspace_size(cb_k, B, Hq * M, Hkv, T) bytes.  Other
+ *   requirements and errors as fq_attend_decode.
+ */
+fq_status fq_attend_queries(const fq_codebook* cb_k, const fq_codebook* cb_v, const uint16_t* q,
+                            const uint32_t* k_codes, const uint16_t* k_norms,
+                            const uint32_t* v_codes, const uint16_t* v_norms, int B, int Hq,
+                            int Hkv, int64_t T, int64_t T_ld, int M, float scale, void* workspace,
+                            size_t workspace_bytes, uint16_t* out, void* stream);
+
+/*
+ * One decode step with encode-on-append [FQ 1, 2.3, 5]: encode the M new keys
+ * and values of every (batch, KV head) into cache slots pos .. pos + M - 1
+ * (exactly as fq_encode would), then attend as fq_attend_queries over the
+ * T = pos + M tokens now in the cache.  Three kernels queued on `stream`, no
+ * host synchronisation and no intermediate buffers.
+ *
+ *   k_new, v_new  [B, Hkv, M, 64] binary16
+ *   caches        as fq_attend_queries, capacity T_ld tokens; slots >= pos + M
+ *                 are neither read nor written
+ *   0 <= pos <= T_ld - M; other arguments as fq_attend_queries.
+ */
+fq_status fq_decode_step(const fq_codebook* cb_k, const fq_codebook* cb_v, const uint16_t* q,
+                         const uint16_t* k_new, const uint16_t* v_new, uint32_t* k_codes,
+                         uint16_t* k_norms, uint32_t* v_codes, uint16_t* v_norms, int B, int Hq,
+                         int Hkv, int64_t T_ld, int64_t pos, int M, float scale, void* workspace,
+                         size_t workspace_bytes, uint16_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -468,7 +468,80 @@ fq_status fq_attend_decode(const fq_codebook* cb_k, const fq_codebook* cb_v, con
   if (g.err != hipSuccess) return FQ_ERR_DEVICE;
   (void)hipGetLastError();
   hipError_t e = fq::launch_attend(cb_k, cb_v, q, k_codes, k_norms, v_codes, v_norms, B, Hq, Hkv,
-                                   T, scale, workspace, out, static_cast<hipStream_t>(stream));
+                                   T, T, 1, scale, workspace, out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FQ_OK : FQ_ERR_DEVICE;
+}
+
+static fq_status check_queries(const fq_codebook* cb_k, const fq_codebook* cb_v, int B, int Hq,
+                               int Hkv, int64_t T, int64_t T_ld, int M) {
+  if (M < 1 || M > fq::MAX_QUERIES || T < M || T_ld < T) return FQ_ERR_INVALID_ARG;
+  if (Hq < 1 || (int64_t)Hq * M > (1 << 20)) return FQ_ERR_INVALID_ARG;
+  fq_status st = check_attend_shape(cb_k, B, Hq * M, Hkv, T);
+  if (st != FQ_OK) return st;
+  if (!cb_v || cb_v->device != cb_k->device) return FQ_ERR_INVALID_ARG;
+  if (cb_v->k != cb_k->k || cb_v->N != cb_k->N) return FQ_ERR_UNSUPPORTED;
+  if (T_ld > (int64_t(1) << 31)) return FQ_ERR_UNSUPPORTED;
+  return FQ_OK;
+}
+
+fq_status fq_attend_queries(const fq_codebook* cb_k, const fq_codebook* cb_v, const uint16_t* q,
+                            const uint32_t* k_codes, const uint16_t* k_norms,
+                            const uint32_t* v_codes, const uint16_t* v_norms, int B, int Hq,
+                            int Hkv, int64_t T, int64_t T_ld, int M, float scale, void* workspace,
+                            size_t workspace_bytes, uint16_t* out, void* stream) {
+  fq_status st = check_queries(cb_k, cb_v, B, Hq, Hkv, T, T_ld, M);
+  if (st != FQ_OK) return st;
+  if (!q || !k_codes || !k_norms || !v_codes || !v_norms || !workspace || !out)
+    return FQ_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) ||
+      !aligned(k_norms, 16) || !aligned(v_norms, 16) || !aligned(workspace, 256))
+    return FQ_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return FQ_ERR_INVALID_ARG;
+  if (workspace_bytes < fq::attend_workspace_bytes(cb_k, B, Hq * M, Hkv, T))
+    return FQ_ERR_INVALID_ARG;
+  DeviceGuard g(cb_k->device);
+  if (g.err != hipSuccess) return FQ_ERR_DEVICE;
+  (void)hipGetLastError();
+  hipError_t e = fq::launch_attend(cb_k, cb_v, q, k_codes, k_norms, v_codes, v_norms, B, Hq * M,
+                                   Hkv, T, T_ld, M, scale, workspace, out,
+                                   static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FQ_OK : FQ_ERR_DEVICE;
+}
+
+fq_status fq_decode_step(const fq_codebook* cb_k, const fq_codebook* cb_v, const uint16_t* q,
+                         const uint16_t* k_new, const uint16_t* v_new, uint32_t* k_codes,
+                         uint16_t* k_norms, uint32_t* v_codes, uint16_t* v_norms, int B, int Hq,
+                         int Hkv, int64_t T_ld, int64_t pos, int M, float scale, void* workspace,
+                         size_t workspace_bytes, uint16_t* out, void* stream) {
+  if (pos < 0 || M < 1 || pos > T_ld - M) return FQ_ERR_INVALID_ARG;
+  const int64_t T = pos + M;
+  fq_status st = check_queries(cb_k, cb_v, B, Hq, Hkv, T, T_ld, M);
+  if (st != FQ_OK) return st;
+  if (!q || !k_new || !v_new || !k_codes || !k_norms || !v_codes || !v_norms || !workspace || !out)
+    return FQ_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) ||
+      !aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(k_norms, 16) ||
+      !aligned(v_norms, 16) || !aligned(workspace, 256))
+    return FQ_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return FQ_ERR_INVALID_ARG;
+  if (workspace_bytes < fq::attend_workspace_bytes(cb_k, B, Hq * M, Hkv, T))
+    return FQ_ERR_INVALID_ARG;
+  DeviceGuard g(cb_k->device);
+  if (g.err != hipSuccess) return FQ_ERR_DEVICE;
+  (void)hipGetLastError();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // the M new tokens of stream (b, h) are rows (b Hkv + h) M + m: record
+  // (b Hkv + h) T_ld + pos + m of the caches
+  fq::OutRows rows;
+  rows.inner = M;
+  rows.stride = T_ld;
+  rows.pos = pos;
+  const int64_t n = (int64_t)B * Hkv * M;
+  hipError_t e = fq::launch_encode(cb_k, k_new, FQ_F16, n, fq::D, k_codes, k_norms, s, rows);
+  if (e == hipSuccess) e = fq::launch_encode(cb_v, v_new, FQ_F16, n, fq::D, v_codes, v_norms, s, rows);
+  if (e == hipSuccess)
+    e = fq::launch_attend(cb_k, cb_v, q, k_codes, k_norms, v_codes, v_norms, B, Hq * M, Hkv, T,
+                          T_ld, M, scale, workspace, out, s);
   return e == hipSuccess ? FQ_OK : FQ_ERR_DEVICE;
 }
 

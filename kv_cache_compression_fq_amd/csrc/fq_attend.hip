@@ -240,7 +240,8 @@ template <int K, int BITS>
 __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void attend_split_kernel(
     const uint16_t* __restrict__ q, const uint32_t* __restrict__ kc,
     const uint16_t* __restrict__ kn, const uint32_t* __restrict__ vc,
-    const uint16_t* __restrict__ vn, int Hq, int Hkv, int64_t T, int64_t chunk, int S,
+    const uint16_t* __restrict__ vn, int Hq, int Hkv, int64_t T, int64_t Tld, int Mq,
+    int64_t chunk, int S,
     float scale, const float* __restrict__ pi32, const _Float16* __restrict__ kh_g,
     const _Float16* __restrict__ kl_g, const _Float16* __restrict__ vh_g,
     const _Float16* __restrict__ vl_g, int N, float* __restrict__ ws,
@@ -360,7 +361,7 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2))
   auto load = [&](TileRegs<W>& t, int64_t tb) __attribute__((always_inline)) {
     const int64_t left = t1 - tb;
     const int cnt = left <= 0 ? 0 : (left < TILE ? (int)left : TILE);
-    const int64_t rec0 = stream * T + (left <= 0 ? 0 : tb);
+    const int64_t rec0 = stream * Tld + (left <= 0 ? 0 : tb);
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint32_t*>(kc + rec0 * W), (short)0, cnt * W * 4, BUF_DWORD3);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
@@ -439,12 +440,15 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2))
       sc[sub][3] = acc[3] * nk4.w;
     }
     if constexpr (PARTIAL) {
+      // past the split's end, or past this query's causal limit
       const int valid = (int)(t1 - tb);
+      const int64_t lim = T - Mq + (col % MAX_G) % Mq - tb;   // last token this query sees
+      const int vq = lim + 1 < (int64_t)valid ? (int)(lim + 1) : valid;
 #pragma unroll
       for (int sub = 0; sub < 4; ++sub)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (16 * sub + 4 * grp + r >= valid) sc[sub][r] = NEG_BIG;
+          if (16 * sub + 4 * grp + r >= vq) sc[sub][r] = NEG_BIG;
     }
     float mx = NEG_BIG;
 #pragma unroll
@@ -518,12 +522,15 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2))
       sc[sub][3] = acc[3] * nk4.w;
     }
     if constexpr (PARTIAL) {
+      // past the split's end, or past this query's causal limit
       const int valid = (int)(t1 - tb);
+      const int64_t lim = T - Mq + (col % MAX_G) % Mq - tb;   // last token this query sees
+      const int vq = lim + 1 < (int64_t)valid ? (int)(lim + 1) : valid;
 #pragma unroll
       for (int sub = 0; sub < 4; ++sub)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (16 * sub + 4 * grp + r >= valid) sc[sub][r] = NEG_BIG;
+          if (16 * sub + 4 * grp + r >= vq) sc[sub][r] = NEG_BIG;
     }
     // ---- online softmax (lane owns head col; its group lanes share the head)
     float mx = NEG_BIG;
@@ -606,14 +613,17 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2))
   // of records are in flight per wave (HBM latency needs the bytes in flight)
   int64_t tb = t0 + (int64_t)wave * TILE;
   if (tb < t1) {
+    // masked tiles: a partial last tile, or (several queries per head) a
+    // tile reaching past T - Mq, where later queries see more tokens
     auto run = [&](int64_t t) __attribute__((always_inline)) {
+      const bool plain = t1 - t >= TILE && t + TILE <= T - Mq + 1;
       if constexpr (AS::EXPAND) {
-        if (t1 - t >= TILE)
+        if (plain)
           process(t, std::false_type());
         else
           process(t, std::true_type());
       } else {
-        if (t1 - t >= TILE)
+        if (plain)
           process_direct(t, std::false_type());
         else
           process_direct(t, std::true_type());
@@ -856,7 +866,8 @@ template <int K, int BITS>
 __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(3))) void attend_direct_kernel(
     const uint16_t* __restrict__ q, const uint32_t* __restrict__ kc,
     const uint16_t* __restrict__ kn, const uint32_t* __restrict__ vc,
-    const uint16_t* __restrict__ vn, int Hq, int Hkv, int64_t T, int64_t chunk, int S,
+    const uint16_t* __restrict__ vn, int Hq, int Hkv, int64_t T, int64_t Tld, int Mq,
+    int64_t chunk, int S,
     float scale, const _Float16* __restrict__ pih_g, const _Float16* __restrict__ pil_g,
     const _Float16* __restrict__ kh_g, const _Float16* __restrict__ vh_g, int N,
     float* __restrict__ ws, const float* __restrict__ pi32t, uint16_t* __restrict__ out) {
@@ -879,7 +890,7 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(3))
   const int64_t t0 = (int64_t)sw * chunk;
   const int64_t t1 = t0 + chunk < T ? t0 + chunk : T;
   const uint32_t ntok = (uint32_t)(t1 - t0);
-  const int64_t rec0 = ((int64_t)b * Hkv + g) * T + t0;
+  const int64_t rec0 = ((int64_t)b * Hkv + g) * Tld + t0;
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint32_t*>(kc + rec0 * W), (short)0, (int)(ntok * W * 4), BUF_DWORD3);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
@@ -1024,10 +1035,14 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(3))
       sc[i] = __builtin_fmaf(own + rot8(give), (float)nu, 0.f);
     }
     const uint32_t valid = ntok - tr;
-    if (valid < (uint32_t)TILE) {
+    if (valid < (uint32_t)TILE || t0 + (int64_t)tr + TILE > T - Mq + 1) {
+      // past the split's end, or past this query's causal limit (several
+      // queries per head: query m of Mq sees tokens up to T - Mq + m)
+      const int64_t lim = T - Mq + (col % MAX_G) % Mq - t0 - (int64_t)tr;
+      const uint32_t vq = lim + 1 < (int64_t)valid ? (uint32_t)(lim + 1) : valid;
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        if (tok_n + (uint32_t)i >= valid) sc[i] = NEG_BIG;
+        if (tok_n + (uint32_t)i >= vq) sc[i] = NEG_BIG;
     }
     // ---- online softmax over the row's 16 tokens x 4 rows (lane pair col,
     //      col + 8 shares head col % 8)
@@ -1128,16 +1143,16 @@ size_t attend_lds_bytes(int N) {
 template <int K, int BITS>
 hipError_t launch_v(const fq_codebook* ck, const fq_codebook* cv, const uint16_t* q,
                     const uint32_t* kc, const uint16_t* kn, const uint32_t* vc,
-                    const uint16_t* vn, int B, int Hq, int Hkv, int64_t T, float scale,
-                    void* workspace, uint16_t* out, hipStream_t s) {
+                    const uint16_t* vn, int B, int Hq, int Hkv, int64_t T, int64_t Tld, int Mq,
+                    float scale, void* workspace, uint16_t* out, hipStream_t s) {
   float* ws = static_cast<float*>(workspace);
   hipError_t e;
   if constexpr (K == 4 || K == 8) {
-    if (ck->half_exact && cv->half_exact && T % 8 == 0) {
+    if (ck->half_exact && cv->half_exact && T % 8 == 0 && Tld % 8 == 0) {
       const SplitPlan p = plan_splits(B, Hkv, T, SPLIT_TARGET_DIRECT);
       auto kern = attend_direct_kernel<K, BITS>;
       hipLaunchKernelGGL(kern, dim3((unsigned)p.S, Hkv, B), dim3(ATT_THREADS), 0, s, q, kc, kn, vc,
-                         vn, Hq, Hkv, T, p.chunk, p.S, scale, ck->t.pi16hi, ck->t.pi16lo,
+                         vn, Hq, Hkv, T, Tld, Mq, p.chunk, p.S, scale, ck->t.pi16hi, ck->t.pi16lo,
                          ck->t.cb16hi, cv->t.cb16hi, ck->N, ws, ck->t.pi32t, out);
       e = hipGetLastError();
       if (e != hipSuccess || p.S == 1) return e;
@@ -1153,7 +1168,7 @@ hipError_t launch_v(const fq_codebook* ck, const fq_codebook* cv, const uint16_t
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)p.S, Hkv, B), dim3(ATT_THREADS), shm, s, q, kc, kn, vc, vn, Hq,
-                     Hkv, T, p.chunk, p.S, scale, ck->t.pi32, ck->t.cb16hi, ck->t.cb16lo,
+                     Hkv, T, Tld, Mq, p.chunk, p.S, scale, ck->t.pi32, ck->t.cb16hi, ck->t.cb16lo,
                      cv->t.cb16hi, cv->t.cb16lo, ck->N, ws, ck->t.pi32t, out);
   e = hipGetLastError();
   if (e != hipSuccess || p.S == 1) return e;
@@ -1181,11 +1196,11 @@ size_t attend_workspace_bytes(const fq_codebook* /*cb_k*/, int B, int Hq, int Hk
 
 hipError_t launch_attend(const fq_codebook* ck, const fq_codebook* cv, const uint16_t* q,
                          const uint32_t* kc, const uint16_t* kn, const uint32_t* vc,
-                         const uint16_t* vn, int B, int Hq, int Hkv, int64_t T, float scale,
-                         void* ws, uint16_t* out, hipStream_t s) {
+                         const uint16_t* vn, int B, int Hq, int Hkv, int64_t T, int64_t Tld,
+                         int Mq, float scale, void* ws, uint16_t* out, hipStream_t s) {
 #define FQ_ATT(KK, BB)                                                                           \
   if (ck->k == KK && ck->bits == BB)                                                             \
-    return launch_v<KK, BB>(ck, cv, q, kc, kn, vc, vn, B, Hq, Hkv, T, scale, ws, out, s);
+    return launch_v<KK, BB>(ck, cv, q, kc, kn, vc, vn, B, Hq, Hkv, T, Tld, Mq, scale, ws, out, s);
   FQ_VARIANTS(FQ_ATT)
 #undef FQ_ATT
   return hipErrorInvalidValue;

@@ -84,6 +84,7 @@ struct EncArgs {
   const uint16_t* grid1;   // candidate records of the one-coordinate last block
   int G, G1;               // cells per dimension
   float gscale, g1scale;   // cells per unit length
+  OutRows rows;            // record of each encoded row
 };
 
 __host__ __device__ inline size_t enc_table_bytes(int N, int S) {   // N rows + sentinel
@@ -485,20 +486,29 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
     }
     wave_lds_sync();
 
-    // ---- 6. pack + store
-    uint32_t* __restrict__ out = a.codes + base * Sh::W;
-    for (int t = lane; t < nv * Sh::W; t += 64) {
-      const int v = t / Sh::W, w = t - v * Sh::W;
-      out[t] = pack_word<BITS, NB>(sIdx + v * IP, w);
+    // ---- 6. pack + store (contiguous records, or appended to caches)
+    if (a.rows.inner == 0) {
+      uint32_t* __restrict__ out = a.codes + base * Sh::W;
+      for (int t = lane; t < nv * Sh::W; t += 64) {
+        const int v = t / Sh::W, w = t - v * Sh::W;
+        out[t] = pack_word<BITS, NB>(sIdx + v * IP, w);
+      }
+      if (g == 0 && j < nv) a.norms[base + j] = nbits;
+    } else {
+      auto rec_of = [&](int64_t r) { return (r / a.rows.inner) * a.rows.stride + a.rows.pos + r % a.rows.inner; };
+      for (int t = lane; t < nv * Sh::W; t += 64) {
+        const int v = t / Sh::W, w = t - v * Sh::W;
+        a.codes[rec_of(base + v) * Sh::W + w] = pack_word<BITS, NB>(sIdx + v * IP, w);
+      }
+      if (g == 0 && j < nv) a.norms[rec_of(base + j)] = nbits;
     }
-    if (g == 0 && j < nv) a.norms[base + j] = nbits;
     wave_lds_sync();
   }
 }
 
 template <int K, int BITS, typename TX>
 hipError_t launch_k(const fq_codebook* cb, const TX* x, int64_t n, int64_t ld, uint32_t* codes,
-                    uint16_t* norms, hipStream_t s) {
+                    uint16_t* norms, hipStream_t s, OutRows rows) {
   using Sh = EncShape<K, BITS>;
   constexpr int WAVES = enc_waves<BITS>();
   const size_t shm =
@@ -533,6 +543,7 @@ hipError_t launch_k(const fq_codebook* cb, const TX* x, int64_t n, int64_t ld, u
   a.G1 = cb->grid1_G > 0 ? cb->grid1_G : 1;
   a.gscale = (float)(cb->grid_G / (2.0 * GRID_R));
   a.g1scale = (float)(a.G1 / (2.0 * GRID_R));
+  a.rows = rows;
   if (GRID && (cb->t.grid == nullptr || cb->grid_G <= 0)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(WAVES * 64), shm, s, a);
   return hipGetLastError();
@@ -540,9 +551,9 @@ hipError_t launch_k(const fq_codebook* cb, const TX* x, int64_t n, int64_t ld, u
 
 template <typename TX>
 hipError_t dispatch(const fq_codebook* cb, const TX* x, int64_t n, int64_t ld, uint32_t* codes,
-                    uint16_t* norms, hipStream_t s) {
+                    uint16_t* norms, hipStream_t s, OutRows rows) {
 #define FQ_ENC_CASE(KK, BB) \
-  if (cb->k == KK && cb->bits == BB) return launch_k<KK, BB, TX>(cb, x, n, ld, codes, norms, s);
+  if (cb->k == KK && cb->bits == BB) return launch_k<KK, BB, TX>(cb, x, n, ld, codes, norms, s, rows);
   FQ_VARIANTS(FQ_ENC_CASE)
 #undef FQ_ENC_CASE
   return hipErrorInvalidValue;
@@ -551,10 +562,10 @@ hipError_t dispatch(const fq_codebook* cb, const TX* x, int64_t n, int64_t ld, u
 }  // namespace
 
 hipError_t launch_encode(const fq_codebook* cb, const void* x, fq_dtype xt, int64_t n, int64_t ld,
-                         uint32_t* codes, uint16_t* norms, hipStream_t s) {
+                         uint32_t* codes, uint16_t* norms, hipStream_t s, OutRows rows) {
   if (xt == FQ_F16)
-    return dispatch<_Float16>(cb, static_cast<const _Float16*>(x), n, ld, codes, norms, s);
-  return dispatch<float>(cb, static_cast<const float*>(x), n, ld, codes, norms, s);
+    return dispatch<_Float16>(cb, static_cast<const _Float16*>(x), n, ld, codes, norms, s, rows);
+  return dispatch<float>(cb, static_cast<const float*>(x), n, ld, codes, norms, s, rows);
 }
 
 }  // namespace fq

@@ -13,6 +13,7 @@ namespace fq {
 constexpr int D = 64;             // vector length handled by the kernels
 constexpr int MAX_N = 4096;       // largest codebook
 constexpr int MAX_WORDS = 12;     // record words for k >= 2, N <= 4096: ceil(32*12/32)
+constexpr int MAX_QUERIES = 8;    // queries per head in one attention call
 
 // (k, index bits) pairs the kernels are built for: the configurations' rates
 // (k=2: N 16 / 64 / 256, k=3: N 512 / 4096, k=4: N 4 / 256, k=8: N 16 / 256)
@@ -102,8 +103,15 @@ namespace fq {
 
 // Launchers (return hipSuccess or the launch error).  Shapes are validated by
 // the caller; pointers are device pointers.
+// Where encoded row r is stored: record r (inner == 0), or record
+// (r / inner) * stride + pos + r % inner (appending to caches of row stride
+// `stride` records).
+struct OutRows {
+  int64_t inner = 0, stride = 0, pos = 0;
+};
 hipError_t launch_encode(const fq_codebook* cb, const void* x, fq_dtype xt, int64_t n,
-                         int64_t ld, uint32_t* codes, uint16_t* norms, hipStream_t s);
+                         int64_t ld, uint32_t* codes, uint16_t* norms, hipStream_t s,
+                         OutRows rows = OutRows());
 hipError_t launch_encode_large(const fq_codebook* cb, const void* x, fq_dtype xt, int64_t n,
                                int64_t ld, uint32_t* codes, uint16_t* norms, hipStream_t s);
 hipError_t launch_decode(const fq_codebook* cb, const uint32_t* codes, const uint16_t* norms,
@@ -111,10 +119,13 @@ hipError_t launch_decode(const fq_codebook* cb, const uint32_t* codes, const uin
                          fq_dtype yt, int64_t ld, hipStream_t s);
 bool attend_supported(const fq_codebook* cb);  // the codebooks fit the kernel's LDS
 size_t attend_workspace_bytes(const fq_codebook* cb_k, int B, int Hq, int Hkv, int64_t T);
+// Attention over T tokens of caches whose per-(b, KV head) rows are Tld
+// records apart; with Mq > 1 every Mq consecutive query heads are the Mq
+// queries of one head, query m seeing tokens 0 .. T - Mq + m (causal).
 hipError_t launch_attend(const fq_codebook* ck, const fq_codebook* cv, const uint16_t* q,
                          const uint32_t* kc, const uint16_t* kn, const uint32_t* vc,
-                         const uint16_t* vn, int B, int Hq, int Hkv, int64_t T, float scale,
-                         void* ws, uint16_t* out, hipStream_t s);
+                         const uint16_t* vn, int B, int Hq, int Hkv, int64_t T, int64_t Tld,
+                         int Mq, float scale, void* ws, uint16_t* out, hipStream_t s);
 
 // Workgroups of `kern` that fit on the current device at once (CUs x blocks per CU),
 // or 0 if the runtime cannot say.

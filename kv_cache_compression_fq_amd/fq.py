@@ -19,7 +19,7 @@ FQ_OK, FQ_ERR_INVALID_ARG, FQ_ERR_BAD_ARTIFACT, FQ_ERR_UNSUPPORTED, FQ_ERR_NO_ME
 
 EXPORTS = ["fq_status_string", "fq_artifact_check", "fq_codebook_load", "fq_codebook_info",
            "fq_codebook_free", "fq_encode", "fq_decode", "fq_attend_workspace_size",
-           "fq_attend_decode"]
+           "fq_attend_decode", "fq_attend_queries", "fq_decode_step"]
 
 
 class FQError(RuntimeError):
@@ -68,6 +68,12 @@ def library(path=LIB_PATH):
     lib.fq_attend_decode.argtypes = [_P, _P, _P, _P, _P, _P, _P, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int, _I64, ctypes.c_float, _P, ctypes.c_size_t, _P,
                                      _P]
+    lib.fq_attend_queries.argtypes = [_P, _P, _P, _P, _P, _P, _P, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, _I64, _I64, ctypes.c_int, ctypes.c_float, _P,
+                                      ctypes.c_size_t, _P, _P]
+    lib.fq_decode_step.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int, _I64, _I64, ctypes.c_int, ctypes.c_float, _P,
+                                   ctypes.c_size_t, _P, _P]
     for name in EXPORTS:
         if name not in ("fq_status_string", "fq_codebook_free"):
             getattr(lib, name).restype = ctypes.c_int
@@ -242,4 +248,67 @@ def fq_attend_decode(cb_k, cb_v, q, k_codes, k_norms, v_codes, v_norms, scale, w
                                       _ptr(k_norms), _ptr(v_codes), _ptr(v_norms), B, Hq, Hkv, T,
                                       float(scale), _ptr(workspace), workspace.numel(), _ptr(out),
                                       _stream(stream, q.device)), "fq_attend_decode")
+    return out
+
+
+def _check_cache(cb, codes, norms, B, Hkv, name):
+    if codes.dim() != 4 or codes.shape[0] != B or codes.shape[1] != Hkv or codes.shape[3] != cb.W:
+        raise ValueError(f"{name} codes must be [B, Hkv, T_ld, W]")
+    if norms.shape != codes.shape[:3]:
+        raise ValueError(f"{name} norms must be [B, Hkv, T_ld]")
+    if not codes.is_contiguous() or not norms.is_contiguous():
+        raise ValueError(f"{name} cache must be contiguous")
+
+
+def fq_attend_queries(cb_k, cb_v, q, k_codes, k_norms, v_codes, v_norms, T, scale,
+                      workspace=None, out=None, stream=None):
+    """Causal attention of M queries per head; q [B, Hq, M, 64] fp16, caches
+    [B, Hkv, T_ld, W] / [B, Hkv, T_ld] of which the first T tokens are read."""
+    import torch
+    B, Hq, M, d = q.shape
+    if d != 64 or not q.is_contiguous():
+        raise ValueError("q must be contiguous [B, Hq, M, 64]")
+    Hkv, T_ld = k_codes.shape[1], k_codes.shape[2]
+    _check_cache(cb_k, k_codes, k_norms, B, Hkv, "key")
+    _check_cache(cb_v, v_codes, v_norms, B, Hkv, "value")
+    if v_codes.shape[2] != T_ld:
+        raise ValueError("key and value caches must have the same capacity")
+    if workspace is None:
+        nbytes = fq_attend_workspace_size(cb_k, B, Hq * M, Hkv, T)
+        workspace = torch.empty((max(nbytes, 256),), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, M, 64), dtype=torch.float16, device=q.device)
+    _check(library().fq_attend_queries(cb_k.handle, cb_v.handle, _ptr(q), _ptr(k_codes),
+                                       _ptr(k_norms), _ptr(v_codes), _ptr(v_norms), B, Hq, Hkv, T,
+                                       T_ld, M, float(scale), _ptr(workspace), workspace.numel(),
+                                       _ptr(out), _stream(stream, q.device)), "fq_attend_queries")
+    return out
+
+
+def fq_decode_step(cb_k, cb_v, q, k_new, v_new, k_codes, k_norms, v_codes, v_norms, pos, scale,
+                   workspace=None, out=None, stream=None):
+    """Encode k_new / v_new [B, Hkv, M, 64] fp16 into cache slots pos .. pos + M - 1,
+    then causal attention of q [B, Hq, M, 64] over the pos + M cached tokens."""
+    import torch
+    B, Hq, M, d = q.shape
+    Hkv, T_ld = k_codes.shape[1], k_codes.shape[2]
+    for t in (q, k_new, v_new):
+        if not t.is_contiguous() or t.dtype != torch.float16:
+            raise ValueError("q, k_new and v_new must be contiguous binary16")
+    if k_new.shape != (B, Hkv, M, 64) or v_new.shape != (B, Hkv, M, 64):
+        raise ValueError("k_new and v_new must be [B, Hkv, M, 64]")
+    _check_cache(cb_k, k_codes, k_norms, B, Hkv, "key")
+    _check_cache(cb_v, v_codes, v_norms, B, Hkv, "value")
+    if v_codes.shape[2] != T_ld:
+        raise ValueError("key and value caches must have the same capacity")
+    if workspace is None:
+        nbytes = fq_attend_workspace_size(cb_k, B, Hq * M, Hkv, pos + M)
+        workspace = torch.empty((max(nbytes, 256),), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, M, 64), dtype=torch.float16, device=q.device)
+    _check(library().fq_decode_step(cb_k.handle, cb_v.handle, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                    _ptr(k_codes), _ptr(k_norms), _ptr(v_codes), _ptr(v_norms), B,
+                                    Hq, Hkv, T_ld, pos, M, float(scale), _ptr(workspace),
+                                    workspace.numel(), _ptr(out), _stream(stream, q.device)),
+           "fq_decode_step")
     return out

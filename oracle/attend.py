@@ -62,6 +62,41 @@ def attend(q, k_words, k_norms, v_words, v_norms, Pi, Ck, Cv, scale, rows=None):
     return o
 
 
+def attend_queries(q, k_words, k_norms, v_words, v_norms, Pi, Ck, Cv, scale, T, rows=None):
+    """Several queries per head over the first T cached tokens, causal.
+
+    The pages fix no multi-query variant (a prefill chunk, speculative draft
+    tokens); the reading: the M queries of a head are the last M positions, so
+    query m sees tokens 0 .. T - M + m, each with the single-query softmax of
+    ``attend``.  q: [B, Hq, M, d]; caches [B, Hkv, >= T, W*] / [B, Hkv, >= T].
+    ``rows`` optionally limits the output to (b, h, m) triples (returns a dict);
+    else an array [B, Hq, M, d].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, M, d = q.shape
+    Hkv = k_words.shape[1]
+    group = Hq // Hkv
+    trips = rows if rows is not None else [(b, h, m) for b in range(B) for h in range(Hq)
+                                            for m in range(M)]
+    cache = {}
+    out = {}
+    for b, h, m in trips:
+        g = h // group
+        if (b, g) not in cache:
+            Kh = codec.decode_records(k_words[b, g, :T], k_norms[b, g, :T], Pi, Ck)
+            Vh = codec.decode_records(v_words[b, g, :T], v_norms[b, g, :T], Pi, Cv)
+            cache = {(b, g): (Kh, Vh)}
+        Kh, Vh = cache[(b, g)]
+        n = T - M + m + 1
+        out[(b, h, m)] = softmax_attend(q[b, h, m], Kh[:n], Vh[:n], scale)[0]
+    if rows is not None:
+        return out
+    o = np.empty((B, Hq, M, d))
+    for (b, h, m), v in out.items():
+        o[b, h, m] = v
+    return o
+
+
 def attend_rotated(q, k_words, k_norms, v_words, v_norms, Pi, Ck, Cv, scale, b, h):
     """The rotated-domain form of ``attend`` for one (b, h) row (pin only)."""
     q = np.asarray(q, dtype=np.float64)

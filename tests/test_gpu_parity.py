@@ -283,6 +283,100 @@ def test_attention(dev, case):
     assert np.max(rel) <= 2e-3
 
 
+QUERY_CASES = [
+    # (B, Hq, Hkv, T, T_ld, M, codebook): M causal queries per head over the
+    # first T of T_ld cached tokens (slots past T hold other records)
+    (2, 4, 4, 300, 320, 4, (2, 16)),
+    (2, 8, 4, 512, 520, 4, (4, 256)),     # transposed-quarter kernel, 8 columns
+    (1, 8, 1, 1000, 1000, 1, (4, 256)),
+    (3, 2, 2, 77, 100, 8, (8, 256)),      # T not a multiple of 8: staged kernel
+    (2, 4, 2, 2048, 4096, 3, (3, 512)),
+    (1, 4, 1, 8, 64, 2, (8, 16)),
+    (4, 16, 4, 2000, 2048, 2, (4, 256)),
+]
+
+
+@pytest.mark.parametrize("case", QUERY_CASES,
+                         ids=lambda c: f"B{c[0]}Hq{c[1]}Hkv{c[2]}T{c[3]}ld{c[4]}M{c[5]}k{c[6][0]}N{c[6][1]}")
+def test_attend_queries(dev, case):
+    B, Hq, Hkv, T, T_ld, M, kb = case
+    art, cb = book(*kb)
+    seed = B * 1000 + T + M
+    bits = cb.nb * cb.info["idx_bits"]
+    kw = synth.random_records((B, Hkv, T_ld), cb.W, bits, seed)
+    vw = synth.random_records((B, Hkv, T_ld), cb.W, bits, seed + 1)
+    kn = synth.random_norms((B, Hkv, T_ld), seed + 2)
+    vn = synth.random_norms((B, Hkv, T_ld), seed + 3)
+    q = np.stack([synth.query(B, Hq, seed=seed + 4 + m) for m in range(M)], axis=2)
+    o = fq.fq_attend_queries(cb, cb, to_dev(q, dev), to_dev(kw, dev, np.int32),
+                             to_dev(kn, dev, np.int16), to_dev(vw, dev, np.int32),
+                             to_dev(vn, dev, np.int16), T, 0.125)
+    torch.cuda.synchronize()
+    got = o.float().cpu().numpy().astype(np.float64)
+    ref = attend.attend_queries(q, kw, kn, vw, vn, art["Pi"], art["C"], art["C"], 0.125, T)
+    rel = np.linalg.norm(got - ref, axis=-1) / np.linalg.norm(ref, axis=-1)
+    print(f"{case}: max rel {np.max(rel):.2e}")
+    assert np.max(rel) <= 2e-3
+
+
+@pytest.mark.parametrize("kb,M", [((4, 256), 1), ((4, 256), 3), ((2, 16), 1), ((2, 64), 4)])
+def test_decode_step_appends_and_attends(dev, kb, M):
+    """Encode-on-append: the M new keys and values land in slots pos .. pos + M - 1
+    as the oracle encodes them, no other slot changes, and the output is the
+    oracle's causal attention over the pos + M cached tokens."""
+    art, cb = book(*kb)
+    B, Hq, Hkv, T_ld, pos = 2, 8, 4, 264, 101
+    Hq = min(Hq, Hkv * (8 // M))
+    bits = cb.nb * cb.info["idx_bits"]
+    kw = synth.random_records((B, Hkv, T_ld), cb.W, bits, 71)
+    vw = synth.random_records((B, Hkv, T_ld), cb.W, bits, 72)
+    kn = synth.random_norms((B, Hkv, T_ld), 73)
+    vn = synth.random_norms((B, Hkv, T_ld), 74)
+    k_new = synth.kv_slab(3, 5, 0, B, Hkv, M)          # [B, Hkv, M, 64]
+    v_new = synth.kv_slab(3, 5, 1, B, Hkv, M)
+    q = np.stack([synth.query(B, Hq, seed=80 + m) for m in range(M)], axis=2)
+    tk = [to_dev(kw, dev, np.int32), to_dev(kn, dev, np.int16), to_dev(vw, dev, np.int32),
+          to_dev(vn, dev, np.int16)]
+    o = fq.fq_decode_step(cb, cb, to_dev(q, dev), to_dev(k_new, dev), to_dev(v_new, dev), *tk,
+                          pos, 0.125)
+    torch.cuda.synchronize()
+    kw2, kn2, vw2, vn2 = [t.cpu().numpy() for t in tk]
+    kw2, vw2 = kw2.view(np.uint32), vw2.view(np.uint32)
+    kn2, vn2 = kn2.view(np.uint16), vn2.view(np.uint16)
+    new = slice(pos, pos + M)
+    for old, got in ((kw, kw2), (kn, kn2), (vw, vw2), (vn, vn2)):
+        keep = np.ones(T_ld, dtype=bool)
+        keep[new] = False
+        assert np.array_equal(old[:, :, keep], got[:, :, keep])
+    for x, c, nn in ((k_new, kw2, kn2), (v_new, vw2, vn2)):
+        check_encode(art, x.reshape(-1, 64), c[:, :, new].reshape(-1, cb.W),
+                     nn[:, :, new].reshape(-1))
+    got = o.float().cpu().numpy().astype(np.float64)
+    ref = attend.attend_queries(q, kw2, kn2, vw2, vn2, art["Pi"], art["C"], art["C"], 0.125,
+                                pos + M)
+    rel = np.linalg.norm(got - ref, axis=-1) / np.linalg.norm(ref, axis=-1)
+    print(f"k{kb[0]}N{kb[1]} M{M}: max rel {np.max(rel):.2e}")
+    assert np.max(rel) <= 2e-3
+
+
+def test_queries_and_step_reject_bad_shapes(dev):
+    _, c4 = book(4, 256)
+    kw = torch.zeros((1, 2, 64, c4.W), dtype=torch.int32, device=dev)
+    nn = torch.zeros((1, 2, 64), dtype=torch.int16, device=dev)
+    q = torch.zeros((1, 8, 3, 64), dtype=torch.float16, device=dev)    # 4 heads x 3 queries per KV head
+    with pytest.raises(fq.FQError) as e:
+        fq.fq_attend_queries(c4, c4, q, kw, nn, kw, nn, 32, 0.125)
+    assert e.value.status == fq.FQ_ERR_UNSUPPORTED
+    q2 = torch.zeros((1, 2, 2, 64), dtype=torch.float16, device=dev)
+    with pytest.raises(fq.FQError) as e:                                  # T > T_ld
+        fq.fq_attend_queries(c4, c4, q2, kw, nn, kw, nn, 65, 0.125)
+    assert e.value.status == fq.FQ_ERR_INVALID_ARG
+    kn = torch.zeros((1, 2, 2, 64), dtype=torch.float16, device=dev)
+    with pytest.raises(fq.FQError) as e:                                  # pos + M > T_ld
+        fq.fq_decode_step(c4, c4, q2, kn, kn, kw, nn, kw, nn, 63, 0.125)
+    assert e.value.status == fq.FQ_ERR_INVALID_ARG
+
+
 def test_attention_rejects_unsupported(dev):
     _, c4 = book(4, 256)
     _, c2 = book(2, 16)

@@ -229,3 +229,25 @@ def test_attend_gqa_grouping_and_softmax():
     V = codec.decode_records(vw[0, 0], vn[0, 0], PI, C)
     out, p = attend.softmax_attend(q[0, 0].astype(np.float64), K, V, 0.125)
     assert abs(p.sum() - 1) < 1e-14 and np.all(p > 0)
+
+
+def test_attend_queries_causal_limits():
+    # query m of M sees the first T - M + m + 1 tokens: with M = 1 it is the
+    # single-query form over T tokens; the zero query averages exactly its
+    # visible values; a cache longer than T is ignored past T
+    q, kw, kn, vw, vn, C = attn_case(T=50)
+    T, M = 40, 4
+    qm = np.stack([synth.query(2, 4, seed=40 + m) for m in range(M)], axis=2)
+    o = attend.attend_queries(qm, kw, kn, vw, vn, PI, C, C, 0.125, T)
+    for m in range(M):
+        n = T - M + m + 1
+        ref = attend.attend(qm[:, :, m], kw[:, :, :n], kn[:, :, :n], vw[:, :, :n], vn[:, :, :n],
+                            PI, C, C, 0.125)
+        assert np.array_equal(o[:, :, m], ref)
+    one = attend.attend_queries(q[:, :, None], kw, kn, vw, vn, PI, C, C, 0.125, 50)
+    assert np.array_equal(one[:, :, 0], attend.attend(q, kw, kn, vw, vn, PI, C, C, 0.125))
+    qz = np.zeros((2, 4, M, 64), dtype=np.float16)
+    oz = attend.attend_queries(qz, kw, kn, vw, vn, PI, C, C, 0.125, T)
+    V = codec.decode_records(vw[1, 1], vn[1, 1], PI, C)
+    for m in range(M):
+        assert np.allclose(oz[1, 3, m], V[:T - M + m + 1].mean(axis=0), rtol=1e-12, atol=1e-12)
