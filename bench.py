@@ -474,11 +474,29 @@ def bench_attend(torch, fq, synth, dev, layers, steps, warmup):
     import numpy as np
     ms = float(np.mean(timer.ms["attend"]))
     bytes_layer = per * 2 * (cb.W * 4 + 2) + 2 * Bq * Hq * 64 * 2
+
+    # the same step with encode-on-append: the new token's key and value are
+    # encoded into the last slot, then attention reads all 32768 tokens
+    k_new = synth.kv_slab_device(3, 0, 0, Bq, Hkv, 1, dev)
+    v_new = synth.kv_slab_device(3, 0, 1, Bq, Hkv, 1, dev)
+    q4 = q.view(Bq, Hq, 1, 64)
+    out4 = out.view(Bq, Hq, 1, 64)
+    timer.reset()
+    for i in range(warmup + steps):
+        if i == warmup:
+            timer.reset()
+        for layer in range(layers):
+            timer.run("step", lambda layer=layer: fq.fq_decode_step(
+                cb, cb, q4, k_new, v_new, kc[layer], kn[layer], vc[layer], vn[layer], Tq - 1, 0.125,
+                workspace=ws, out=out4))
+    timer.collect()
+    ms_step = float(np.mean(timer.ms["step"]))
     return {"workload": "tinyllama decode step: batch 16, 32 q / 4 kv heads, seq 32768, d=64, "
                         f"k4N256 K and V, {layers} layers",
             "ms_per_layer_event": ms, "ms_per_layer_wall": 1e3 * el / (steps * layers),
             "bytes_per_layer": bytes_layer, "gbs": bytes_layer / (ms * 1e-3) / 1e9,
-            "hbm_frac": bytes_layer / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            "hbm_frac": bytes_layer / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "decode_step_with_append_ms_per_layer": ms_step}
 
 
 if __name__ == "__main__":
