@@ -537,8 +537,18 @@ fq_status fq_decode_step(const fq_codebook* cb_k, const fq_codebook* cb_v, const
   rows.stride = T_ld;
   rows.pos = pos;
   const int64_t n = (int64_t)B * Hkv * M;
-  hipError_t e = fq::launch_encode(cb_k, k_new, FQ_F16, n, fq::D, k_codes, k_norms, s, rows);
-  if (e == hipSuccess) e = fq::launch_encode(cb_v, v_new, FQ_F16, n, fq::D, v_codes, v_norms, s, rows);
+  hipError_t e;
+  if (cb_v == cb_k) {   // one launch encodes the keys and then the values
+    fq::SecondInput vals;
+    vals.x = v_new;
+    vals.n = n;
+    vals.codes = v_codes;
+    vals.norms = v_norms;
+    e = fq::launch_encode(cb_k, k_new, FQ_F16, n, fq::D, k_codes, k_norms, s, rows, vals);
+  } else {
+    e = fq::launch_encode(cb_k, k_new, FQ_F16, n, fq::D, k_codes, k_norms, s, rows);
+    if (e == hipSuccess) e = fq::launch_encode(cb_v, v_new, FQ_F16, n, fq::D, v_codes, v_norms, s, rows);
+  }
   if (e == hipSuccess)
     e = fq::launch_attend(cb_k, cb_v, q, k_codes, k_norms, v_codes, v_norms, B, Hq * M, Hkv, T,
                           T_ld, M, scale, workspace, out, s);

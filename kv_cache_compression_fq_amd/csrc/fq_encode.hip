@@ -85,6 +85,12 @@ struct EncArgs {
   int G, G1;               // cells per dimension
   float gscale, g1scale;   // cells per unit length
   OutRows rows;            // record of each encoded row
+  // rows n1 .. n - 1: a second input and its outputs (same codebook);
+  // n1 = n when there is none
+  const void* x2;
+  uint32_t* codes2;
+  uint16_t* norms2;
+  int64_t n1;
 };
 
 __host__ __device__ inline size_t enc_table_bytes(int N, int S) {   // N rows + sentinel
@@ -256,10 +262,15 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
   const int j = lane & 15, g = lane >> 4;
 
   // the lane's row of a chunk (rows past the end repeat the last one)
+  // row r of the input: rows >= a.n1 come from the second input (keys and
+  // values of one decode step in one launch)
+  auto xrow = [&](int64_t r) {
+    return r < a.n1 ? x + r * a.ld : static_cast<const TX*>(a.x2) + (r - a.n1) * a.ld;
+  };
   auto row_of = [&](int64_t chunk) {
     const int64_t base = chunk * EV;
     const int64_t last = a.n - 1 - base;
-    return x + (base + (j < last ? j : last)) * a.ld;
+    return xrow(base + (j < last ? j : last));
   };
   int64_t ch = (int64_t)blockIdx.x * WAVES + wave;
   XRaw<TX> xraw;
@@ -401,7 +412,7 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
       const bool last = c >= NCF;
       const int v = last ? c - NCF : c / NBF, b = last ? NB - 1 : c - (c / NBF) * NBF;
       const int rj = last ? Sh::LAST : K;
-      const TX* xr = x + (base + v) * a.ld + 4 * l16;
+      const TX* xr = xrow(base + v) + 4 * l16;
       double xq[4];
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) xq[qq] = (double)xr[qq];
@@ -495,12 +506,16 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
       }
       if (g == 0 && j < nv) a.norms[base + j] = nbits;
     } else {
-      auto rec_of = [&](int64_t r) { return (r / a.rows.inner) * a.rows.stride + a.rows.pos + r % a.rows.inner; };
+      auto rec_of = [&](int64_t r) {
+        if (r >= a.n1) r -= a.n1;
+        return (r / a.rows.inner) * a.rows.stride + a.rows.pos + r % a.rows.inner;
+      };
       for (int t = lane; t < nv * Sh::W; t += 64) {
         const int v = t / Sh::W, w = t - v * Sh::W;
-        a.codes[rec_of(base + v) * Sh::W + w] = pack_word<BITS, NB>(sIdx + v * IP, w);
+        uint32_t* codes = base + v < a.n1 ? a.codes : a.codes2;
+        codes[rec_of(base + v) * Sh::W + w] = pack_word<BITS, NB>(sIdx + v * IP, w);
       }
-      if (g == 0 && j < nv) a.norms[rec_of(base + j)] = nbits;
+      if (g == 0 && j < nv) (base + j < a.n1 ? a.norms : a.norms2)[rec_of(base + j)] = nbits;
     }
     wave_lds_sync();
   }
@@ -508,7 +523,7 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
 
 template <int K, int BITS, typename TX>
 hipError_t launch_k(const fq_codebook* cb, const TX* x, int64_t n, int64_t ld, uint32_t* codes,
-                    uint16_t* norms, hipStream_t s, OutRows rows) {
+                    uint16_t* norms, hipStream_t s, OutRows rows, SecondInput second) {
   using Sh = EncShape<K, BITS>;
   constexpr int WAVES = enc_waves<BITS>();
   const size_t shm =
@@ -522,7 +537,7 @@ hipError_t launch_k(const fq_codebook* cb, const TX* x, int64_t n, int64_t ld, u
   if (e != hipSuccess) return e;
   static int64_t cap = 0;
   if (cap == 0) cap = resident_blocks(reinterpret_cast<const void*>(kern), WAVES * 64, shm);
-  const int64_t chunks = (n + EV - 1) / EV;
+  const int64_t chunks = (n + (second.x ? second.n : 0) + EV - 1) / EV;
   int64_t blocks = (chunks + WAVES - 1) / WAVES;
   if (cap > 0 && blocks > cap) blocks = cap;
   EncArgs a;
@@ -544,6 +559,18 @@ hipError_t launch_k(const fq_codebook* cb, const TX* x, int64_t n, int64_t ld, u
   a.gscale = (float)(cb->grid_G / (2.0 * GRID_R));
   a.g1scale = (float)(a.G1 / (2.0 * GRID_R));
   a.rows = rows;
+  a.n1 = n;
+  a.x2 = nullptr;
+  a.codes2 = nullptr;
+  a.norms2 = nullptr;
+  if (second.x && rows.inner == 0) return hipErrorInvalidValue;   // needs a record map
+  if (second.x) {   // the second input's rows follow the first's
+    a.n1 = n;
+    a.n = n + second.n;
+    a.x2 = second.x;
+    a.codes2 = second.codes;
+    a.norms2 = second.norms;
+  }
   if (GRID && (cb->t.grid == nullptr || cb->grid_G <= 0)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(WAVES * 64), shm, s, a);
   return hipGetLastError();
@@ -551,9 +578,10 @@ hipError_t launch_k(const fq_codebook* cb, const TX* x, int64_t n, int64_t ld, u
 
 template <typename TX>
 hipError_t dispatch(const fq_codebook* cb, const TX* x, int64_t n, int64_t ld, uint32_t* codes,
-                    uint16_t* norms, hipStream_t s, OutRows rows) {
+                    uint16_t* norms, hipStream_t s, OutRows rows, SecondInput second) {
 #define FQ_ENC_CASE(KK, BB) \
-  if (cb->k == KK && cb->bits == BB) return launch_k<KK, BB, TX>(cb, x, n, ld, codes, norms, s, rows);
+  if (cb->k == KK && cb->bits == BB)                                                        \
+    return launch_k<KK, BB, TX>(cb, x, n, ld, codes, norms, s, rows, second);
   FQ_VARIANTS(FQ_ENC_CASE)
 #undef FQ_ENC_CASE
   return hipErrorInvalidValue;
@@ -562,10 +590,12 @@ hipError_t dispatch(const fq_codebook* cb, const TX* x, int64_t n, int64_t ld, u
 }  // namespace
 
 hipError_t launch_encode(const fq_codebook* cb, const void* x, fq_dtype xt, int64_t n, int64_t ld,
-                         uint32_t* codes, uint16_t* norms, hipStream_t s, OutRows rows) {
+                         uint32_t* codes, uint16_t* norms, hipStream_t s, OutRows rows,
+                         SecondInput second) {
   if (xt == FQ_F16)
-    return dispatch<_Float16>(cb, static_cast<const _Float16*>(x), n, ld, codes, norms, s, rows);
-  return dispatch<float>(cb, static_cast<const float*>(x), n, ld, codes, norms, s, rows);
+    return dispatch<_Float16>(cb, static_cast<const _Float16*>(x), n, ld, codes, norms, s, rows,
+                              second);
+  return dispatch<float>(cb, static_cast<const float*>(x), n, ld, codes, norms, s, rows, second);
 }
 
 }  // namespace fq

@@ -109,9 +109,17 @@ namespace fq {
 struct OutRows {
   int64_t inner = 0, stride = 0, pos = 0;
 };
+// A second input encoded by the same launch (same codebook, dtype, row stride
+// and OutRows map), its rows following the first input's.
+struct SecondInput {
+  const void* x = nullptr;
+  int64_t n = 0;
+  uint32_t* codes = nullptr;
+  uint16_t* norms = nullptr;
+};
 hipError_t launch_encode(const fq_codebook* cb, const void* x, fq_dtype xt, int64_t n,
                          int64_t ld, uint32_t* codes, uint16_t* norms, hipStream_t s,
-                         OutRows rows = OutRows());
+                         OutRows rows = OutRows(), SecondInput second = SecondInput());
 hipError_t launch_encode_large(const fq_codebook* cb, const void* x, fq_dtype xt, int64_t n,
                                int64_t ld, uint32_t* codes, uint16_t* norms, hipStream_t s);
 hipError_t launch_decode(const fq_codebook* cb, const uint32_t* codes, const uint16_t* norms,
