@@ -194,9 +194,10 @@ fq_status fq_attend_queries(const fq_codebook* cb_k, const fq_codebook* cb_v, co
 /*
  * One decode step with encode-on-append [FQ 1, 2.3, 5]: encode the M new keys
  * and values of every (batch, KV head) into cache slots pos .. pos + M - 1
- * (exactly as fq_encode would), then attend as fq_attend_queries over the
+ * (the float64 nearest codewords and binary16 norms fq_encode computes, with
+ * its near-tie allowance), then attend as fq_attend_queries over the
  * T = pos + M tokens now in the cache.  Kernels queued on `stream` (one
- * encode launch for keys and values when cb_k == cb_v, then attention), no
+ * append launch for keys and values when cb_k == cb_v, then attention), no
  * host synchronisation and no intermediate buffers.
  *
  *   k_new, v_new  [B, Hkv, M, 64] binary16

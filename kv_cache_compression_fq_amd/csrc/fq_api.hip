@@ -472,6 +472,9 @@ fq_status fq_attend_decode(const fq_codebook* cb_k, const fq_codebook* cb_v, con
   return e == hipSuccess ? FQ_OK : FQ_ERR_DEVICE;
 }
 
+// appends of up to this many vectors per cache take the float64 append kernel
+constexpr int64_t APPEND_DIRECT_MAX = 8192;
+
 static fq_status check_queries(const fq_codebook* cb_k, const fq_codebook* cb_v, int B, int Hq,
                                int Hkv, int64_t T, int64_t T_ld, int M) {
   if (M < 1 || M > fq::MAX_QUERIES || T < M || T_ld < T) return FQ_ERR_INVALID_ARG;
@@ -538,7 +541,16 @@ fq_status fq_decode_step(const fq_codebook* cb_k, const fq_codebook* cb_v, const
   rows.pos = pos;
   const int64_t n = (int64_t)B * Hkv * M;
   hipError_t e;
-  if (cb_v == cb_k) {   // one launch encodes the keys and then the values
+  if (n <= APPEND_DIRECT_MAX) {
+    // a few vectors: one wave each, the float64 definition directly
+    if (cb_v == cb_k) {
+      e = fq::launch_append(cb_k, k_new, v_new, n, 2 * n, k_codes, k_norms, v_codes, v_norms, rows, s);
+    } else {
+      e = fq::launch_append(cb_k, k_new, nullptr, n, n, k_codes, k_norms, nullptr, nullptr, rows, s);
+      if (e == hipSuccess)
+        e = fq::launch_append(cb_v, v_new, nullptr, n, n, v_codes, v_norms, nullptr, nullptr, rows, s);
+    }
+  } else if (cb_v == cb_k) {   // one launch encodes the keys and then the values
     fq::SecondInput vals;
     vals.x = v_new;
     vals.n = n;

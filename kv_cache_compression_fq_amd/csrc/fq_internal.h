@@ -120,6 +120,12 @@ struct SecondInput {
 hipError_t launch_encode(const fq_codebook* cb, const void* x, fq_dtype xt, int64_t n,
                          int64_t ld, uint32_t* codes, uint16_t* norms, hipStream_t s,
                          OutRows rows = OutRows(), SecondInput second = SecondInput());
+// Exact float64 encode of a few binary16 rows into cache slots (decode-step
+// appends): rows < n1 from x1 into codes1 / norms1, the rest from x2 into
+// codes2 / norms2, each mapped by `rows` (inner > 0).
+hipError_t launch_append(const fq_codebook* cb, const uint16_t* x1, const uint16_t* x2,
+                         int64_t n1, int64_t n, uint32_t* codes1, uint16_t* norms1,
+                         uint32_t* codes2, uint16_t* norms2, OutRows rows, hipStream_t s);
 hipError_t launch_encode_large(const fq_codebook* cb, const void* x, fq_dtype xt, int64_t n,
                                int64_t ld, uint32_t* codes, uint16_t* norms, hipStream_t s);
 hipError_t launch_decode(const fq_codebook* cb, const uint32_t* codes, const uint16_t* norms,

@@ -359,6 +359,33 @@ def test_decode_step_appends_and_attends(dev, kb, M):
     assert np.max(rel) <= 2e-3
 
 
+def test_decode_step_large_append(dev):
+    """A prefill-sized append (64 x 32 heads x 8 tokens per cache, past the
+    small-append kernel's range) into an empty cache, then causal attention."""
+    art, cb = book(2, 64)
+    B, Hkv, M, T_ld = 64, 32, 8, 16
+    Hq = Hkv
+    kw = np.zeros((B, Hkv, T_ld, cb.W), dtype=np.uint32)
+    kn = np.zeros((B, Hkv, T_ld), dtype=np.uint16)
+    k_new = synth.kv_slab(3, 6, 0, B, Hkv, M)
+    v_new = synth.kv_slab(3, 6, 1, B, Hkv, M)
+    q = np.stack([synth.query(B, Hq, seed=90 + m) for m in range(M)], axis=2)
+    tk = [to_dev(kw, dev, np.int32), to_dev(kn, dev, np.int16), to_dev(kw, dev, np.int32),
+          to_dev(kn, dev, np.int16)]
+    o = fq.fq_decode_step(cb, cb, to_dev(q, dev), to_dev(k_new, dev), to_dev(v_new, dev), *tk, 0,
+                          0.125)
+    torch.cuda.synchronize()
+    kw2, kn2, vw2, vn2 = [t.cpu().numpy() for t in tk]
+    kw2, vw2, kn2, vn2 = kw2.view(np.uint32), vw2.view(np.uint32), kn2.view(np.uint16), vn2.view(np.uint16)
+    assert np.all(kw2[:, :, M:] == 0) and np.all(vn2[:, :, M:] == 0)
+    for x, c, nn in ((k_new, kw2, kn2), (v_new, vw2, vn2)):
+        check_encode(art, x.reshape(-1, 64), c[:, :, :M].reshape(-1, cb.W), nn[:, :, :M].reshape(-1))
+    got = o.float().cpu().numpy().astype(np.float64)
+    ref = attend.attend_queries(q, kw2, kn2, vw2, vn2, art["Pi"], art["C"], art["C"], 0.125, M)
+    rel = np.linalg.norm(got - ref, axis=-1) / np.linalg.norm(ref, axis=-1)
+    assert np.max(rel) <= 2e-3
+
+
 def test_queries_and_step_reject_bad_shapes(dev):
     _, c4 = book(4, 256)
     kw = torch.zeros((1, 2, 64, c4.W), dtype=torch.int32, device=dev)
