@@ -540,17 +540,24 @@ fq_status fq_decode_step(const fq_codebook* cb_k, const fq_codebook* cb_v, const
   rows.stride = T_ld;
   rows.pos = pos;
   const int64_t n = (int64_t)B * Hkv * M;
-  hipError_t e;
   if (n <= APPEND_DIRECT_MAX) {
-    // a few vectors: one wave each, the float64 definition directly
-    if (cb_v == cb_k) {
-      e = fq::launch_append(cb_k, k_new, v_new, n, 2 * n, k_codes, k_norms, v_codes, v_norms, rows, s);
-    } else {
-      e = fq::launch_append(cb_k, k_new, nullptr, n, n, k_codes, k_norms, nullptr, nullptr, rows, s);
-      if (e == hipSuccess)
-        e = fq::launch_append(cb_v, v_new, nullptr, n, n, v_codes, v_norms, nullptr, nullptr, rows, s);
-    }
-  } else if (cb_v == cb_k) {   // one launch encodes the keys and then the values
+    // a few vectors: encoded from the float64 definition, inside the
+    // attention kernel where it can (see launch_attend)
+    fq::AppendIn app;
+    app.k_new = k_new;
+    app.v_new = v_new;
+    app.M = M;
+    app.pi64t = cb_k->t.pi64t;
+    app.kc = k_codes;
+    app.kn = k_norms;
+    app.vc = v_codes;
+    app.vn = v_norms;
+    hipError_t e = fq::launch_attend(cb_k, cb_v, q, k_codes, k_norms, v_codes, v_norms, B, Hq * M,
+                                     Hkv, T, T_ld, M, scale, workspace, out, s, app);
+    return e == hipSuccess ? FQ_OK : FQ_ERR_DEVICE;
+  }
+  hipError_t e;
+  if (cb_v == cb_k) {   // one launch encodes the keys and then the values
     fq::SecondInput vals;
     vals.x = v_new;
     vals.n = n;

@@ -862,6 +862,88 @@ __device__ inline float half_at(const u32x4& v, int i) {   // binary16 number i 
   return f16_bits_to_f32((uint16_t)((i & 1) ? (w >> 16) : (w & 0xFFFFu)));
 }
 
+// One appended vector, encoded by one wave from the float64 definition: the
+// norm, z = Pi x / |x| (lane t forms z_t from coalesced rows of Pi^T), then
+// for every block the nearest codeword of the binary16 table in LDS (exact:
+// the table holds binary16 values) by float64 squared distance, ties to the
+// lowest index; the record (LSB-first fields) and the binary16 norm, rounded
+// once from the float64 norm.  scratch: 2 * 64 doubles + 64 words per wave.
+template <int K, int BITS>
+__device__ void append_one(const uint16_t* x, const _Float16* sTab, int N, const double* pi64t,
+                           uint32_t* rec, uint16_t* nrm, double* scratch, int lane) {
+  constexpr int NB = D / K, P = D / NB, W = Shape<K, BITS>::W;
+  double* sX = scratch;
+  double* sZ = scratch + D;
+  uint32_t* sI = reinterpret_cast<uint32_t*>(scratch + 2 * D);
+  const double xv = (double)f16_bits_to_f32(x[lane]);
+  double ss = xv * xv;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    int2 v = __builtin_bit_cast(int2, ss);
+    v.x = __shfl_xor(v.x, m, 64);
+    v.y = __shfl_xor(v.y, m, 64);
+    ss += __builtin_bit_cast(double, v);
+  }
+  const double nu = sqrt(ss);
+  sX[lane] = xv;
+  wave_lds_sync();
+  double acc = 0.0;
+#pragma unroll 1
+  for (int h = 0; h < D / 8; ++h) {   // 8 rows of Pi^T in flight at a time
+    double pv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pv[i] = pi64t[(8 * h + i) * D + lane];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = fma(pv[i], sX[8 * h + i], acc);
+  }
+  sZ[lane] = acc / nu;   // a zero vector gives NaN: every distance is NaN, index 0
+  wave_lds_sync();
+  const int b = lane / P, p = lane % P;
+  double zb[K];
+#pragma unroll
+  for (int t = 0; t < K; ++t) zb[t] = sZ[b * K + t];
+  double best = INFINITY;
+  int bi = 0;
+  for (int cn = p; cn < N; cn += P) {
+    double dd = 0.0;
+#pragma unroll
+    for (int t = 0; t < K; ++t) {
+      const double df = zb[t] - (double)(float)sTab[cn * K + t];
+      dd = fma(df, df, dd);
+    }
+    if (dd < best) {
+      best = dd;
+      bi = cn;
+    }
+  }
+#pragma unroll
+  for (int m = P >> 1; m >= 1; m >>= 1) {
+    int2 v = __builtin_bit_cast(int2, best);
+    v.x = __shfl_xor(v.x, m, 64);
+    v.y = __shfl_xor(v.y, m, 64);
+    const double ob = __builtin_bit_cast(double, v);
+    const int oi = __shfl_xor(bi, m, 64);
+    if (ob < best || (ob == best && oi < bi)) {
+      best = ob;
+      bi = oi;
+    }
+  }
+  if (p == 0) sI[b] = (uint32_t)bi;
+  wave_lds_sync();
+  if (lane < W) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int p0 = j * BITS - 32 * lane;
+      if (p0 >= 32 || p0 + BITS <= 0) continue;
+      word |= p0 >= 0 ? (sI[j] << p0) : (sI[j] >> (-p0));
+    }
+    rec[lane] = word;
+  }
+  if (lane == 0) *nrm = f64_to_f16_bits(nu);
+  wave_lds_sync();
+}
+
 template <int K, int BITS>
 __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(3))) void attend_direct_kernel(
     const uint16_t* __restrict__ q, const uint32_t* __restrict__ kc,
@@ -870,7 +952,8 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(3))
     int64_t chunk, int S,
     float scale, const _Float16* __restrict__ pih_g, const _Float16* __restrict__ pil_g,
     const _Float16* __restrict__ kh_g, const _Float16* __restrict__ vh_g, int N,
-    float* __restrict__ ws, const float* __restrict__ pi32t, uint16_t* __restrict__ out) {
+    float* __restrict__ ws, const float* __restrict__ pi32t, uint16_t* __restrict__ out,
+    AppendIn app) {
   using C = DirectCfg<K, BITS>;
   using L = DirectLds<K, BITS>;
   constexpr int W = C::W;
@@ -957,8 +1040,14 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(3))
   constexpr uint32_t WSTEP = ATT_WAVES * TILE;
   uint32_t rel = (uint32_t)wave * TILE;
   DTile<W> rr[DEPTH];
+  // a workgroup holding appended tokens encodes them first (below), so its
+  // tile loads wait until then
+  const int64_t ap0 = T - app.M > t0 ? T - app.M : t0;
+  const bool appends = app.M > 0 && ap0 < t1;
+  if (!appends) {
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d) load(rr[d], rel + d * WSTEP);
+    for (int d = 0; d < DEPTH; ++d) load(rr[d], rel + d * WSTEP);
+  }
 
   // tables (zeros past the end: out-of-range loads)
   *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(sK) + threadIdx.x * 16) = kt4;
@@ -983,6 +1072,25 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(3))
     }
   }
   __syncthreads();
+  if (appends) {
+    // keys then values of tokens ap0 .. t1 - 1, one vector per wave at a time,
+    // from the binary16 tables now in LDS; the merge area is free until the end
+    const int nv = 2 * (int)(t1 - ap0);
+    const int64_t stream = (int64_t)b * Hkv + g;
+    for (int v = wave; v < nv; v += ATT_WAVES) {
+      const int64_t t = ap0 + v / 2;
+      const bool isv = v & 1;
+      const uint16_t* x = (isv ? app.v_new : app.k_new) + (stream * app.M + (t - (T - app.M))) * D;
+      const int64_t r = stream * Tld + t;
+      append_one<K, BITS>(x, isv ? sV : sK, N, app.pi64t, (isv ? app.vc : app.kc) + r * W,
+                          (isv ? app.vn : app.kn) + r,
+                          reinterpret_cast<double*>(sMerge) + wave * (2 * D + D / 2), lane);
+    }
+    __threadfence_block();   // the new records are stored before any wave reads them
+    __syncthreads();
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) load(rr[d], rel + d * WSTEP);
+  }
   // B operands of the scores, K-step s2: coordinates 16 grp + 8 s2 + 0..7
   half8 qb[2];
 #pragma unroll
@@ -1144,7 +1252,8 @@ template <int K, int BITS>
 hipError_t launch_v(const fq_codebook* ck, const fq_codebook* cv, const uint16_t* q,
                     const uint32_t* kc, const uint16_t* kn, const uint32_t* vc,
                     const uint16_t* vn, int B, int Hq, int Hkv, int64_t T, int64_t Tld, int Mq,
-                    float scale, void* workspace, uint16_t* out, hipStream_t s) {
+                    float scale, void* workspace, uint16_t* out, hipStream_t s,
+                    const AppendIn& app) {
   float* ws = static_cast<float*>(workspace);
   hipError_t e;
   if constexpr (K == 4 || K == 8) {
@@ -1153,13 +1262,28 @@ hipError_t launch_v(const fq_codebook* ck, const fq_codebook* cv, const uint16_t
       auto kern = attend_direct_kernel<K, BITS>;
       hipLaunchKernelGGL(kern, dim3((unsigned)p.S, Hkv, B), dim3(ATT_THREADS), 0, s, q, kc, kn, vc,
                          vn, Hq, Hkv, T, Tld, Mq, p.chunk, p.S, scale, ck->t.pi16hi, ck->t.pi16lo,
-                         ck->t.cb16hi, cv->t.cb16hi, ck->N, ws, ck->t.pi32t, out);
+                         ck->t.cb16hi, cv->t.cb16hi, ck->N, ws, ck->t.pi32t, out, app);
       e = hipGetLastError();
       if (e != hipSuccess || p.S == 1) return e;
       hipLaunchKernelGGL(attend_merge_kernel, dim3(Hq * B), dim3(256), 0, s, ws, p.S, ck->t.pi32t,
                          out);
       return hipGetLastError();
     }
+  }
+  if (app.M > 0) {   // appended tokens first, by their own launch
+    OutRows rows;
+    rows.inner = app.M;
+    rows.stride = Tld;
+    rows.pos = T - app.M;
+    const int64_t n = (int64_t)B * Hkv * app.M;
+    if (ck == cv) {
+      e = launch_append(ck, app.k_new, app.v_new, n, 2 * n, app.kc, app.kn, app.vc, app.vn, rows, s);
+    } else {
+      e = launch_append(ck, app.k_new, nullptr, n, n, app.kc, app.kn, nullptr, nullptr, rows, s);
+      if (e == hipSuccess)
+        e = launch_append(cv, app.v_new, nullptr, n, n, app.vc, app.vn, nullptr, nullptr, rows, s);
+    }
+    if (e != hipSuccess) return e;
   }
   const SplitPlan p = plan_splits(B, Hkv, T, SPLIT_TARGET);
   const size_t shm = attend_lds_bytes<K, BITS>(ck->N);
@@ -1197,10 +1321,12 @@ size_t attend_workspace_bytes(const fq_codebook* /*cb_k*/, int B, int Hq, int Hk
 hipError_t launch_attend(const fq_codebook* ck, const fq_codebook* cv, const uint16_t* q,
                          const uint32_t* kc, const uint16_t* kn, const uint32_t* vc,
                          const uint16_t* vn, int B, int Hq, int Hkv, int64_t T, int64_t Tld,
-                         int Mq, float scale, void* ws, uint16_t* out, hipStream_t s) {
+                         int Mq, float scale, void* ws, uint16_t* out, hipStream_t s,
+                         const AppendIn& app) {
 #define FQ_ATT(KK, BB)                                                                           \
   if (ck->k == KK && ck->bits == BB)                                                             \
-    return launch_v<KK, BB>(ck, cv, q, kc, kn, vc, vn, B, Hq, Hkv, T, Tld, Mq, scale, ws, out, s);
+    return launch_v<KK, BB>(ck, cv, q, kc, kn, vc, vn, B, Hq, Hkv, T, Tld, Mq, scale, ws, out, s, \
+                            app);
   FQ_VARIANTS(FQ_ATT)
 #undef FQ_ATT
   return hipErrorInvalidValue;

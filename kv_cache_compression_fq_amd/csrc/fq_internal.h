@@ -133,13 +133,30 @@ hipError_t launch_decode(const fq_codebook* cb, const uint32_t* codes, const uin
                          fq_dtype yt, int64_t ld, hipStream_t s);
 bool attend_supported(const fq_codebook* cb);  // the codebooks fit the kernel's LDS
 size_t attend_workspace_bytes(const fq_codebook* cb_k, int B, int Hq, int Hkv, int64_t T);
+// Tokens a decode step appends (the last M of the T attended tokens), to be
+// encoded into the caches before they are read.
+struct AppendIn {
+  const uint16_t* k_new = nullptr;   // [B, Hkv, M, 64] binary16
+  const uint16_t* v_new = nullptr;
+  int M = 0;                         // 0: nothing to append
+  const double* pi64t = nullptr;     // Pi^T, float64 (the key codebook's)
+  uint32_t* kc = nullptr;            // the caches, written
+  uint16_t* kn = nullptr;
+  uint32_t* vc = nullptr;
+  uint16_t* vn = nullptr;
+};
+
 // Attention over T tokens of caches whose per-(b, KV head) rows are Tld
 // records apart; with Mq > 1 every Mq consecutive query heads are the Mq
-// queries of one head, query m seeing tokens 0 .. T - Mq + m (causal).
+// queries of one head, query m seeing tokens 0 .. T - Mq + m (causal).  With
+// app.M > 0 the appended tokens are encoded first: inside the attention
+// kernel, by the workgroups whose split holds them, where that kernel runs;
+// else by launch_append ahead of it.
 hipError_t launch_attend(const fq_codebook* ck, const fq_codebook* cv, const uint16_t* q,
                          const uint32_t* kc, const uint16_t* kn, const uint32_t* vc,
                          const uint16_t* vn, int B, int Hq, int Hkv, int64_t T, int64_t Tld,
-                         int Mq, float scale, void* ws, uint16_t* out, hipStream_t s);
+                         int Mq, float scale, void* ws, uint16_t* out, hipStream_t s,
+                         const AppendIn& app = AppendIn());
 
 // Workgroups of `kern` that fit on the current device at once (CUs x blocks per CU),
 // or 0 if the runtime cannot say.
