@@ -319,13 +319,24 @@ def test_attend_queries(dev, case):
     assert np.max(rel) <= 2e-3
 
 
-@pytest.mark.parametrize("kb,M", [((4, 256), 1), ((4, 256), 3), ((2, 16), 1), ((2, 64), 4)])
-def test_decode_step_appends_and_attends(dev, kb, M):
+STEP_CASES = [
+    # (codebook, M, pos, separate K and V handles); pos + M a multiple of 8
+    # with k = 4, 8 takes the attention kernel that encodes the appended
+    # tokens itself, the rest an append launch ahead of the attention
+    ((4, 256), 1, 101, False), ((4, 256), 3, 101, False), ((2, 16), 1, 101, False),
+    ((2, 64), 4, 101, False), ((4, 256), 1, 103, False), ((8, 256), 8, 96, False),
+    ((4, 256), 2, 62, True), ((2, 16), 2, 5, True), ((8, 16), 1, 0, False),
+]
+
+
+@pytest.mark.parametrize("kb,M,pos,two", STEP_CASES)
+def test_decode_step_appends_and_attends(dev, kb, M, pos, two):
     """Encode-on-append: the M new keys and values land in slots pos .. pos + M - 1
     as the oracle encodes them, no other slot changes, and the output is the
     oracle's causal attention over the pos + M cached tokens."""
     art, cb = book(*kb)
-    B, Hq, Hkv, T_ld, pos = 2, 8, 4, 264, 101
+    cbv = fq.fq_codebook_load(open(artifact_path(*kb), "rb").read(), 0) if two else cb
+    B, Hq, Hkv, T_ld = 2, 8, 4, 264
     Hq = min(Hq, Hkv * (8 // M))
     bits = cb.nb * cb.info["idx_bits"]
     kw = synth.random_records((B, Hkv, T_ld), cb.W, bits, 71)
@@ -337,7 +348,7 @@ def test_decode_step_appends_and_attends(dev, kb, M):
     q = np.stack([synth.query(B, Hq, seed=80 + m) for m in range(M)], axis=2)
     tk = [to_dev(kw, dev, np.int32), to_dev(kn, dev, np.int16), to_dev(vw, dev, np.int32),
           to_dev(vn, dev, np.int16)]
-    o = fq.fq_decode_step(cb, cb, to_dev(q, dev), to_dev(k_new, dev), to_dev(v_new, dev), *tk,
+    o = fq.fq_decode_step(cb, cbv, to_dev(q, dev), to_dev(k_new, dev), to_dev(v_new, dev), *tk,
                           pos, 0.125)
     torch.cuda.synchronize()
     kw2, kn2, vw2, vn2 = [t.cpu().numpy() for t in tk]
