@@ -1040,6 +1040,13 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(3))
   constexpr uint32_t WSTEP = ATT_WAVES * TILE;
   uint32_t rel = (uint32_t)wave * TILE;
   DTile<W> rr[DEPTH];
+  // masks: tiles from mstart on (relative to the split) reach past its end or
+  // past T - Mq, where the queries of a head see different token counts;
+  // lim_lane = the last token (relative) this lane's query sees, clamped
+  const int64_t vis = T - Mq + 1 - t0 < (int64_t)ntok ? T - Mq + 1 - t0 : (int64_t)ntok;
+  const uint32_t mstart = vis < 0 ? 0u : (uint32_t)vis;
+  const int64_t ll = T - Mq + (col % MAX_G) % Mq - t0;
+  const int lim_lane = ll < -1 ? -1 : (ll > (int64_t)ntok ? (int)ntok : (int)ll);
   // a workgroup holding appended tokens encodes them first (below), so its
   // tile loads wait until then
   const int64_t ap0 = T - app.M > t0 ? T - app.M : t0;
@@ -1142,15 +1149,15 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(3))
       const _Float16 nu = __builtin_bit_cast(_Float16, (uint16_t)((i & 1) ? (nw >> 16) : (nw & 0xFFFFu)));
       sc[i] = __builtin_fmaf(own + rot8(give), (float)nu, 0.f);
     }
-    const uint32_t valid = ntok - tr;
-    if (valid < (uint32_t)TILE || t0 + (int64_t)tr + TILE > T - Mq + 1) {
+    if (tr + (uint32_t)TILE > mstart) {
       // past the split's end, or past this query's causal limit (several
       // queries per head: query m of Mq sees tokens up to T - Mq + m)
-      const int64_t lim = T - Mq + (col % MAX_G) % Mq - t0 - (int64_t)tr;
-      const uint32_t vq = lim + 1 < (int64_t)valid ? (uint32_t)(lim + 1) : valid;
+      const int valid = (int)(ntok - tr);
+      const int lq = lim_lane - (int)tr + 1;
+      const int vq = lq < valid ? lq : valid;
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        if (tok_n + (uint32_t)i >= vq) sc[i] = NEG_BIG;
+        if ((int)tok_n + i >= vq) sc[i] = NEG_BIG;
     }
     // ---- online softmax over the row's 16 tokens x 4 rows (lane pair col,
     //      col + 8 shares head col % 8)
