@@ -204,8 +204,9 @@ def test_decode_variants(dev, k, N, ydt):
     print(f"k{k}N{N} {ydt}: max err/nu {np.max(err / np.maximum(nu16, 1e-30)):.2e}")
 
 
-def test_random_access_decode(dev):
-    art, cb = book(4, 256)
+@pytest.mark.parametrize("kb", [(4, 256), (64, 4096), (3, 512)])
+def test_random_access_decode(dev, kb):
+    art, cb = book(*kb)
     x = synth.kv_slab(3, 0, 0, 4, 1, 500).reshape(-1, 64)
     idx, nbits = codec.encode(x, art["Pi"], art["C"])
     words = codec.pack(idx, art["bits"])
