@@ -196,10 +196,10 @@ fq_status fq_attend_queries(const fq_codebook* cb_k, const fq_codebook* cb_v, co
  * and values of every (batch, KV head) into cache slots pos .. pos + M - 1
  * (the float64 nearest codewords and binary16 norms fq_encode computes, with
  * its near-tie allowance), then attend as fq_attend_queries over the
- * T = pos + M tokens now in the cache.  Kernels queued on `stream`: where
- * the transposed-quarter attention kernel runs (k = 4, 8; T and T_ld
- * multiples of 8) the workgroups holding the new tokens encode them inside
- * it, otherwise an append launch precedes the attention; no host
+ * T = pos + M tokens now in the cache.  Kernels queued on `stream`: the
+ * attention workgroups holding the new tokens encode them before reading
+ * their tiles (codebooks whose tables hold binary16 values, as the shipped
+ * ones do), otherwise an append launch precedes the attention; no host
  * synchronisation and no intermediate buffers.  Keys and values share the
  * rotation of cb_k (the one shared rotation).
  *

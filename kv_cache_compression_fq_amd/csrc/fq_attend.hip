@@ -236,6 +236,95 @@ __device__ inline void finish_heads(const float* sMerge, int G, int Hq, int b, i
   }
 }
 
+// One appended vector, encoded by one wave from the float64 definition: the
+// norm, z = Pi x / |x| (lane t forms z_t from coalesced rows of Pi^T), then
+// for every block the nearest codeword of the binary16 table in LDS (exact:
+// the table holds binary16 values) by float64 squared distance, ties to the
+// lowest index; the record (LSB-first fields) and the binary16 norm, rounded
+// once from the float64 norm.  scratch: 2 * 64 doubles + 64 words per wave.
+template <int K, int BITS>
+__device__ void append_one(const uint16_t* x, const _Float16* sTab, int tstride, int N,
+                           const double* pi64t, uint32_t* rec, uint16_t* nrm, double* scratch,
+                           int lane) {
+  // P lanes per block (a power of two, P * NB <= 64); the last block of k = 3
+  // has one real coordinate
+  constexpr int NB = (D + K - 1) / K, W = Shape<K, BITS>::W;
+  constexpr int P = NB <= 8 ? 8 : (NB <= 16 ? 4 : 2);
+  double* sX = scratch;
+  double* sZ = scratch + D;
+  uint32_t* sI = reinterpret_cast<uint32_t*>(scratch + 2 * D);
+  const double xv = (double)f16_bits_to_f32(x[lane]);
+  double ss = xv * xv;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    int2 v = __builtin_bit_cast(int2, ss);
+    v.x = __shfl_xor(v.x, m, 64);
+    v.y = __shfl_xor(v.y, m, 64);
+    ss += __builtin_bit_cast(double, v);
+  }
+  const double nu = sqrt(ss);
+  sX[lane] = xv;
+  wave_lds_sync();
+  double acc = 0.0;
+#pragma unroll 1
+  for (int h = 0; h < D / 8; ++h) {   // 8 rows of Pi^T in flight at a time
+    double pv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pv[i] = pi64t[(8 * h + i) * D + lane];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = fma(pv[i], sX[8 * h + i], acc);
+  }
+  sZ[lane] = acc / nu;   // a zero vector gives NaN: every distance is NaN, index 0
+  wave_lds_sync();
+  const int b = lane / P, p = lane % P;
+  const int rd = b < NB ? (D - b * K < K ? D - b * K : K) : 0;   // real coordinates
+  double zb[K];
+#pragma unroll
+  for (int t = 0; t < K; ++t) zb[t] = t < rd ? sZ[b * K + t] : 0.0;
+  double best = INFINITY;
+  int bi = 0;
+  if (b < NB) {
+    for (int cn = p; cn < N; cn += P) {
+      double dd = 0.0;
+#pragma unroll
+      for (int t = 0; t < K; ++t) {
+        const double df = t < rd ? zb[t] - (double)(float)sTab[cn * tstride + t] : 0.0;
+        dd = fma(df, df, dd);
+      }
+      if (dd < best) {
+        best = dd;
+        bi = cn;
+      }
+    }
+  }
+#pragma unroll
+  for (int m = P >> 1; m >= 1; m >>= 1) {
+    int2 v = __builtin_bit_cast(int2, best);
+    v.x = __shfl_xor(v.x, m, 64);
+    v.y = __shfl_xor(v.y, m, 64);
+    const double ob = __builtin_bit_cast(double, v);
+    const int oi = __shfl_xor(bi, m, 64);
+    if (ob < best || (ob == best && oi < bi)) {
+      best = ob;
+      bi = oi;
+    }
+  }
+  if (b < NB && p == 0) sI[b] = (uint32_t)bi;
+  wave_lds_sync();
+  if (lane < W) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int p0 = j * BITS - 32 * lane;
+      if (p0 >= 32 || p0 + BITS <= 0) continue;
+      word |= p0 >= 0 ? (sI[j] << p0) : (sI[j] >> (-p0));
+    }
+    rec[lane] = word;
+  }
+  if (lane == 0) *nrm = f64_to_f16_bits(nu);
+  wave_lds_sync();
+}
+
 template <int K, int BITS>
 __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void attend_split_kernel(
     const uint16_t* __restrict__ q, const uint32_t* __restrict__ kc,
@@ -245,7 +334,7 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2))
     float scale, const float* __restrict__ pi32, const _Float16* __restrict__ kh_g,
     const _Float16* __restrict__ kl_g, const _Float16* __restrict__ vh_g,
     const _Float16* __restrict__ vl_g, int N, float* __restrict__ ws,
-    const float* __restrict__ pi32t, uint16_t* __restrict__ out) {
+    const float* __restrict__ pi32t, uint16_t* __restrict__ out, AppendIn app) {
   using Sh = Shape<K, BITS>;
   using AS = AttShape<K, BITS>;
   using L = AttLds<K, BITS>;
@@ -331,6 +420,30 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2))
   const int64_t t1 = t0 + chunk < T ? t0 + chunk : T;
   const int64_t stream = (int64_t)b * Hkv + g;
   constexpr int64_t WSTEP = (int64_t)ATT_WAVES * TILE;
+
+  // appended tokens in this split: encoded before any tile is read, from the
+  // binary16 tables in LDS (hi parts; the launcher sends codebooks whose
+  // tables are binary16 values), the merge area as scratch
+  {
+    const int64_t ap0 = T - app.M > t0 ? T - app.M : t0;
+    if (app.M > 0 && ap0 < t1) {
+      const int nv = 2 * (int)(t1 - ap0);
+      constexpr int KST = KeyTable<K>::INTERLEAVED ? 2 * K : K;   // key table row
+      constexpr int VST = AS::EXPAND ? K : 2 * K;                  // value table row
+      for (int v = wave; v < nv; v += ATT_WAVES) {
+        const int64_t t = ap0 + v / 2;
+        const bool isv = v & 1;
+        const uint16_t* x =
+            (isv ? app.v_new : app.k_new) + (stream * app.M + (t - (T - app.M))) * D;
+        const int64_t r = stream * Tld + t;
+        append_one<K, BITS>(x, isv ? sVh : sK, isv ? VST : KST, N, app.pi64t,
+                            (isv ? app.vc : app.kc) + r * W, (isv ? app.vn : app.kn) + r,
+                            reinterpret_cast<double*>(sMerge) + wave * (2 * D + D / 2), lane);
+      }
+      __threadfence_block();   // the new records are stored before any wave reads them
+      __syncthreads();
+    }
+  }
 
   // B operands of the score product, K-steps 0..5: part s / 2, coordinates
   // 32 (s % 2) + 8 grp + e, column (head) col
@@ -862,88 +975,6 @@ __device__ inline float half_at(const u32x4& v, int i) {   // binary16 number i 
   return f16_bits_to_f32((uint16_t)((i & 1) ? (w >> 16) : (w & 0xFFFFu)));
 }
 
-// One appended vector, encoded by one wave from the float64 definition: the
-// norm, z = Pi x / |x| (lane t forms z_t from coalesced rows of Pi^T), then
-// for every block the nearest codeword of the binary16 table in LDS (exact:
-// the table holds binary16 values) by float64 squared distance, ties to the
-// lowest index; the record (LSB-first fields) and the binary16 norm, rounded
-// once from the float64 norm.  scratch: 2 * 64 doubles + 64 words per wave.
-template <int K, int BITS>
-__device__ void append_one(const uint16_t* x, const _Float16* sTab, int N, const double* pi64t,
-                           uint32_t* rec, uint16_t* nrm, double* scratch, int lane) {
-  constexpr int NB = D / K, P = D / NB, W = Shape<K, BITS>::W;
-  double* sX = scratch;
-  double* sZ = scratch + D;
-  uint32_t* sI = reinterpret_cast<uint32_t*>(scratch + 2 * D);
-  const double xv = (double)f16_bits_to_f32(x[lane]);
-  double ss = xv * xv;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    int2 v = __builtin_bit_cast(int2, ss);
-    v.x = __shfl_xor(v.x, m, 64);
-    v.y = __shfl_xor(v.y, m, 64);
-    ss += __builtin_bit_cast(double, v);
-  }
-  const double nu = sqrt(ss);
-  sX[lane] = xv;
-  wave_lds_sync();
-  double acc = 0.0;
-#pragma unroll 1
-  for (int h = 0; h < D / 8; ++h) {   // 8 rows of Pi^T in flight at a time
-    double pv[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) pv[i] = pi64t[(8 * h + i) * D + lane];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc = fma(pv[i], sX[8 * h + i], acc);
-  }
-  sZ[lane] = acc / nu;   // a zero vector gives NaN: every distance is NaN, index 0
-  wave_lds_sync();
-  const int b = lane / P, p = lane % P;
-  double zb[K];
-#pragma unroll
-  for (int t = 0; t < K; ++t) zb[t] = sZ[b * K + t];
-  double best = INFINITY;
-  int bi = 0;
-  for (int cn = p; cn < N; cn += P) {
-    double dd = 0.0;
-#pragma unroll
-    for (int t = 0; t < K; ++t) {
-      const double df = zb[t] - (double)(float)sTab[cn * K + t];
-      dd = fma(df, df, dd);
-    }
-    if (dd < best) {
-      best = dd;
-      bi = cn;
-    }
-  }
-#pragma unroll
-  for (int m = P >> 1; m >= 1; m >>= 1) {
-    int2 v = __builtin_bit_cast(int2, best);
-    v.x = __shfl_xor(v.x, m, 64);
-    v.y = __shfl_xor(v.y, m, 64);
-    const double ob = __builtin_bit_cast(double, v);
-    const int oi = __shfl_xor(bi, m, 64);
-    if (ob < best || (ob == best && oi < bi)) {
-      best = ob;
-      bi = oi;
-    }
-  }
-  if (p == 0) sI[b] = (uint32_t)bi;
-  wave_lds_sync();
-  if (lane < W) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int p0 = j * BITS - 32 * lane;
-      if (p0 >= 32 || p0 + BITS <= 0) continue;
-      word |= p0 >= 0 ? (sI[j] << p0) : (sI[j] >> (-p0));
-    }
-    rec[lane] = word;
-  }
-  if (lane == 0) *nrm = f64_to_f16_bits(nu);
-  wave_lds_sync();
-}
-
 template <int K, int BITS>
 __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(3))) void attend_direct_kernel(
     const uint16_t* __restrict__ q, const uint32_t* __restrict__ kc,
@@ -1089,7 +1120,7 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(3))
       const bool isv = v & 1;
       const uint16_t* x = (isv ? app.v_new : app.k_new) + (stream * app.M + (t - (T - app.M))) * D;
       const int64_t r = stream * Tld + t;
-      append_one<K, BITS>(x, isv ? sV : sK, N, app.pi64t, (isv ? app.vc : app.kc) + r * W,
+      append_one<K, BITS>(x, isv ? sV : sK, K, N, app.pi64t, (isv ? app.vc : app.kc) + r * W,
                           (isv ? app.vn : app.kn) + r,
                           reinterpret_cast<double*>(sMerge) + wave * (2 * D + D / 2), lane);
     }
@@ -1277,7 +1308,8 @@ hipError_t launch_v(const fq_codebook* ck, const fq_codebook* cv, const uint16_t
       return hipGetLastError();
     }
   }
-  if (app.M > 0) {   // appended tokens first, by their own launch
+  const bool fuse = app.M > 0 && ck->half_exact && cv->half_exact;
+  if (app.M > 0 && !fuse) {   // appended tokens first, by their own launch
     OutRows rows;
     rows.inner = app.M;
     rows.stride = Tld;
@@ -1300,7 +1332,8 @@ hipError_t launch_v(const fq_codebook* ck, const fq_codebook* cv, const uint16_t
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)p.S, Hkv, B), dim3(ATT_THREADS), shm, s, q, kc, kn, vc, vn, Hq,
                      Hkv, T, Tld, Mq, p.chunk, p.S, scale, ck->t.pi32, ck->t.cb16hi, ck->t.cb16lo,
-                     cv->t.cb16hi, cv->t.cb16lo, ck->N, ws, ck->t.pi32t, out);
+                     cv->t.cb16hi, cv->t.cb16lo, ck->N, ws, ck->t.pi32t, out,
+                     fuse ? app : AppendIn());
   e = hipGetLastError();
   if (e != hipSuccess || p.S == 1) return e;
   hipLaunchKernelGGL(attend_merge_kernel, dim3(Hq * B), dim3(256), 0, s, ws, p.S, ck->t.pi32t, out);
