@@ -371,6 +371,47 @@ def test_decode_step_appends_and_attends(dev, kb, M, pos, two):
     assert np.max(rel) <= 2e-3
 
 
+def test_decode_step_off_grid_codebook(dev):
+    """A codebook whose table is not on the binary16 grid (the shipped ones
+    are): the appended tokens go through the separate float64 append launch
+    and the attention through the hi / lo table path."""
+    art = artifact.read_artifact(open(artifact_path(2, 16), "rb").read())
+    C = art["C"].astype(np.float64)
+    C = (C * (1.0 + 1e-4 * np.sin(np.arange(C.size)).reshape(C.shape))).astype(np.float32)
+    assert not np.array_equal(C.astype(np.float16).astype(np.float32), C)
+    art2 = dict(art)
+    art2["C"] = C
+    art2["d"] = 64
+    blob = artifact.write_artifact(art["Pi"], art2)
+    ref_art = artifact.read_artifact(blob)
+    cb = fq.fq_codebook_load(blob, 0)
+    B, Hq, Hkv, T_ld, M, pos = 2, 8, 4, 128, 2, 40
+    bits = cb.nb * cb.info["idx_bits"]
+    kw = synth.random_records((B, Hkv, T_ld), cb.W, bits, 61)
+    vw = synth.random_records((B, Hkv, T_ld), cb.W, bits, 62)
+    kn = synth.random_norms((B, Hkv, T_ld), 63)
+    vn = synth.random_norms((B, Hkv, T_ld), 64)
+    k_new = synth.kv_slab(3, 7, 0, B, Hkv, M)
+    v_new = synth.kv_slab(3, 7, 1, B, Hkv, M)
+    q = np.stack([synth.query(B, Hq, seed=66 + m) for m in range(M)], axis=2)
+    tk = [to_dev(kw, dev, np.int32), to_dev(kn, dev, np.int16), to_dev(vw, dev, np.int32),
+          to_dev(vn, dev, np.int16)]
+    o = fq.fq_decode_step(cb, cb, to_dev(q, dev), to_dev(k_new, dev), to_dev(v_new, dev), *tk,
+                          pos, 0.125)
+    torch.cuda.synchronize()
+    kw2, kn2, vw2, vn2 = [t.cpu().numpy() for t in tk]
+    kw2, vw2, kn2, vn2 = kw2.view(np.uint32), vw2.view(np.uint32), kn2.view(np.uint16), vn2.view(np.uint16)
+    new = slice(pos, pos + M)
+    for x, c, nn in ((k_new, kw2, kn2), (v_new, vw2, vn2)):
+        check_encode(ref_art, x.reshape(-1, 64), c[:, :, new].reshape(-1, cb.W),
+                     nn[:, :, new].reshape(-1))
+    got = o.float().cpu().numpy().astype(np.float64)
+    ref = attend.attend_queries(q, kw2, kn2, vw2, vn2, ref_art["Pi"], ref_art["C"], ref_art["C"],
+                                0.125, pos + M)
+    rel = np.linalg.norm(got - ref, axis=-1) / np.linalg.norm(ref, axis=-1)
+    assert np.max(rel) <= 2e-3
+
+
 def test_decode_step_large_append(dev):
     """A prefill-sized append (64 x 32 heads x 8 tokens per cache, past the
     small-append kernel's range) into an empty cache, then causal attention."""
