@@ -172,6 +172,8 @@ def main():
                          "counter run can scale FETCH_SIZE / WRITE_SIZE by a known size")
     ap.add_argument("--no-fidelity", action="store_true",
                     help="skip the attention-fidelity sweep over the rates")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the timing of the tiny, TinyLlama-cache and 2^24-vector sets")
     ap.add_argument("--no-large", action="store_true",
                     help="skip the large-block (k = 32, 64; N = 4096) encode / decode timing")
     ap.add_argument("--attend-layers", type=int, default=22)
@@ -308,6 +310,8 @@ def main():
 
     fid = None if a.no_fidelity else fidelity(torch, fq, synth, dev)
 
+    cfgs = None if a.no_configs else bench_configs(torch, fq, synth, dev)
+
     cpu = None if a.no_cpu_baseline else cpu_baseline(a.cpu_sample)
 
     out = {
@@ -325,6 +329,7 @@ def main():
         "ops": ops,
         "attend_tinyllama": attend,
         "large_k": large,
+        "configs": cfgs,
         "fidelity": fid,
     }
     print(json.dumps(out))
@@ -430,6 +435,82 @@ def bench_large(torch, fq, x, y, steps, warmup):
     log("large-block timing done")
     return {"workload": f"gpt2-small-kv-cache, {n} vectors, fp16; median of {steps} launches",
             "peak_mfma_f16_tflops": MFMA_F16_PEAK_TFLOPS, "codes": out}
+
+
+def bench_configs(torch, fq, synth, dev, reps=5):
+    """The other configurations' throughput, each op timed with HIP events (median).
+
+    tiny: 4096 float32 vectors, k2N16 encode + decode (a latency figure);
+    tinyllama cache: 22 layers x {K,V} x batch 8 x 4 heads x 2048 tokens,
+      full encode at k4N256 and k8N256, then 2^20 uniformly drawn addresses
+      decoded by address;
+    stress set: 2^24 vectors (256 streams x 65536 tokens) at k8N16, k4N4
+      (0.5 bit per coordinate) and k3N4096, encode and decode.
+    Algorithmic bytes: encode 128 B read + record + norm written; decode the
+    reverse; random access adds the 8-byte address.
+    """
+    import numpy as np
+
+    def timed(fn, n_rep):
+        ts = []
+        for i in range(n_rep + 1):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            if i:
+                ts.append(a.elapsed_time(b) * 1e-3)
+        return float(np.median(ts))
+
+    def codec_rows(cb, x, n, with_decode=True, rows=None):
+        codes = torch.empty((n, cb.W), dtype=torch.int32, device=dev)
+        norms = torch.empty((n,), dtype=torch.int16, device=dev)
+        rb = record_bytes(cb.k, cb.N) + 2
+        te = timed(lambda: fq.fq_encode(cb, x, codes, norms), reps)
+        r = {"encode_ms": te * 1e3, "encode_vectors_per_s": n / te,
+             "encode_gbs": n * (128 + rb) / te / 1e9}
+        if with_decode:
+            y = torch.empty((n, 64), dtype=torch.float16, device=dev)
+            td = timed(lambda: fq.fq_decode(cb, codes, norms, y=y), reps)
+            r.update({"decode_ms": td * 1e3, "decode_vectors_per_s": n / td,
+                      "decode_gbs": n * (128 + rb) / td / 1e9,
+                      "decode_hbm_frac": n * (128 + rb) / td / 1e9 / HBM_PEAK_GBS})
+            del y
+        if rows is not None:
+            m = rows.shape[0]
+            y = torch.empty((m, 64), dtype=torch.float16, device=dev)
+            tr = timed(lambda: fq.fq_decode(cb, codes, norms, rows=rows, y=y), reps)
+            r.update({"random_decode_ms": tr * 1e3, "random_decodes_per_s": m / tr,
+                      "random_decode_gbs": m * (8 + 128 + rb) / tr / 1e9})
+            del y
+        return r
+
+    out = {}
+    cb = fq.load_codebook(2, 16)
+    xt = torch.from_numpy(synth.tiny_vectors(4096)).to(dev)
+    out["tiny_4096_fp32_k2N16"] = codec_rows(cb, xt, 4096)
+
+    L3, B3, H3, T3 = 22, 8, 4, 2048
+    x3 = torch.cat([synth.kv_slab_device(3, l, kv, B3, H3, T3, dev).reshape(-1, 64)
+                    for l in range(L3) for kv in range(2)])
+    n3 = x3.shape[0]
+    rows = torch.from_numpy(synth.random_rows(n3, 1 << 20, seed=33)).to(dev)
+    for k, N in ((4, 256), (8, 256)):
+        out[f"tinyllama_cache_{n3}_k{k}N{N}"] = codec_rows(fq.load_codebook(k, N), x3, n3,
+                                                            with_decode=False, rows=rows)
+    del x3, rows
+    torch.cuda.empty_cache()
+
+    x4 = synth.kv_slab_device(4, 0, 0, 1, 256, 65536, dev).reshape(-1, 64)
+    n4 = x4.shape[0]
+    for k, N in ((8, 16), (4, 4), (3, 4096)):
+        out[f"stress_{n4}_k{k}N{N}"] = codec_rows(fq.load_codebook(k, N), x4, n4)
+    del x4
+    torch.cuda.empty_cache()
+    log("configuration timing done")
+    return out
 
 
 def bench_attend(torch, fq, synth, dev, layers, steps, warmup):
