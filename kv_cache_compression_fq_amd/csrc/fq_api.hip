@@ -199,7 +199,24 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
   }
   cb->half_exact = true;
   cb->cmax = 0.0;
-  std::vector<float> hnorm(fq::large_block(k) ? N : 0);
+  // The matrix-core searches keep -|c|^2 / 2 per codeword in float32.  At
+  // k = 8 a constant K0 = r + r^2 / 2 (r the smallest codeword norm) is added
+  // to every score: it cancels in every comparison, and it lifts the score of
+  // the smallest codeword, and so the best score, above zero for any block of
+  // norm <= 1, which the certificate needs (its integer keys order only
+  // non-negative scores); the bounds charge its rounding.
+  const bool k8mma = k == 8 && N == 256;
+  std::vector<float> hnorm(fq::large_block(k) || k8mma ? N : 0);
+  cb->hshift = 0.0;
+  if (k8mma) {
+    double rmin = INFINITY;
+    for (int n = 0; n < N; ++n) {
+      double cc = 0;
+      for (int t = 0; t < k; ++t) cc += cb->c[(size_t)n * k + t] * cb->c[(size_t)n * k + t];
+      rmin = fmin(rmin, sqrt(cc));
+    }
+    cb->hshift = rmin + 0.5 * rmin * rmin;
+  }
   for (int n = 0; n < N; ++n) {
     double cc = 0;
     for (int t = 0; t < k; ++t) {
@@ -212,7 +229,7 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
     }
     enc[(size_t)n * S + k] = (float)cc;
     cb->cmax = fmax(cb->cmax, sqrt(cc));
-    if (!hnorm.empty()) hnorm[n] = (float)(-0.5 * cc);
+    if (!hnorm.empty()) hnorm[n] = (float)(cb->hshift - 0.5 * cc);
   }
   // k >= 32: the codebook as A fragments of v_mfma_f32_16x16x32_f16 (binary16;
   // the large-block kernels need a table on the binary16 grid)
@@ -398,11 +415,10 @@ fq_status fq_encode(const fq_codebook* cb, const void* x, fq_dtype x_dtype, int6
   DeviceGuard g(cb->device);
   if (g.err != hipSuccess) return FQ_ERR_DEVICE;
   (void)hipGetLastError();
-  hipError_t e = fq::large_block(cb->k)
-                     ? fq::launch_encode_large(cb, x, x_dtype, n, x_ld, codes, norms,
-                                               static_cast<hipStream_t>(stream))
-                     : fq::launch_encode(cb, x, x_dtype, n, x_ld, codes, norms,
-                                         static_cast<hipStream_t>(stream));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = fq::large_block(cb->k)        ? fq::launch_encode_large(cb, x, x_dtype, n, x_ld, codes, norms, st)
+                 : fq::encode_k8_applies(cb) ? fq::launch_encode_k8(cb, x, x_dtype, n, x_ld, codes, norms, st)
+                                             : fq::launch_encode(cb, x, x_dtype, n, x_ld, codes, norms, st);
   return e == hipSuccess ? FQ_OK : FQ_ERR_DEVICE;
 }
 

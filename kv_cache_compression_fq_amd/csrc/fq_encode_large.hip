@@ -107,10 +107,10 @@ __device__ inline float key_value(int key) { return __int_as_float(key); }
 // The exact nearest codeword of one listed block (the whole wave): z's block
 // in float64 from x and Pi (lane t < k holds z_t), then float64 distances to
 // the listed candidates, to every codeword 16 t + s of each hidden slot s,
-// or to all N codewords; ties to the lowest index.
-template <int K, typename TX>
-__device__ int settle_block(const LArgs& a, const TX* x, const uint32_t* ent, double* sX,
-                            double* sZd, int lane) {
+// or to all N codewords (binary16 table `cbt`, exact); ties to the lowest index.
+template <int K, typename TX, int NCW = LN>
+__device__ int settle_block(const LArgs& a, const TX* x, const _Float16* cbt, const uint32_t* ent,
+                            double* sX, double* sZd, int lane) {
   const int64_t row = (int64_t)((uint64_t)ent[0] | ((uint64_t)ent[1] << 32));
   const uint32_t info = ent[2], hm = ent[3];
   const int b = (int)(info & 0xFFu), nc = (int)((info >> 8) & 0xFFu);
@@ -127,7 +127,7 @@ __device__ int settle_block(const LArgs& a, const TX* x, const uint32_t* ent, do
   float cv[FL_CAND];
 #pragma unroll
   for (int e = 0; e < FL_CAND; ++e)
-    cv[e] = (!full && e < nc && lane < K) ? a.enc[(size_t)ce[e] * a.S + lane] : 0.f;
+    cv[e] = (!full && e < nc && lane < K) ? (float)cbt[(size_t)ce[e] * K + lane] : 0.f;
   const double nu = sqrt(wave_sum_f64(xv * xv));
   sX[lane] = xv;
   wave_lds_sync();
@@ -144,7 +144,7 @@ __device__ int settle_block(const LArgs& a, const TX* x, const uint32_t* ent, do
   double best = INFINITY;
   int bi = 0;
   auto dist = [&](int cn) {   // this lane's codeword, all k coordinates (binary16, exact)
-    const half8* cr = reinterpret_cast<const half8*>(a.cbh + (size_t)cn * K);
+    const half8* cr = reinterpret_cast<const half8*>(cbt + (size_t)cn * K);
     half8 hv[K / 8];
 #pragma unroll
     for (int q = 0; q < K / 8; ++q) hv[q] = cr[q];
@@ -163,7 +163,7 @@ __device__ int settle_block(const LArgs& a, const TX* x, const uint32_t* ent, do
     for (int e = 0; e < FL_CAND; ++e) {
       if (e < nc) {
         const int cn = ce[e];
-        const double df = lane < K ? zd + 0.5 * (double)cv[e] : 0.0;   // c = -enc / 2, exact
+        const double df = lane < K ? zd - (double)cv[e] : 0.0;
         const double dd = wave_sum_f64(df * df);
         if (dd < best || (dd == best && cn < bi)) {
           best = dd;
@@ -176,7 +176,8 @@ __device__ int settle_block(const LArgs& a, const TX* x, const uint32_t* ent, do
       const int slot = __builtin_ctz(h);
       h &= h - 1;
 #pragma unroll 1
-      for (int m = 0; m < LN / 16 / 64; ++m) {
+      for (int m = 0; m < (NCW / 16 + 63) / 64; ++m) {
+        if (lane + 64 * m >= NCW / 16) continue;
         const int cn = 16 * (lane + 64 * m) + slot;
         const double dd = dist(cn);
         if (dd < best || (dd == best && cn < bi)) {
@@ -187,7 +188,7 @@ __device__ int settle_block(const LArgs& a, const TX* x, const uint32_t* ent, do
     }
   } else {
 #pragma unroll 1
-    for (int cn = lane; cn < LN; cn += 64) {
+    for (int cn = lane; cn < NCW; cn += 64) {
       const double dd = dist(cn);
       if (dd < best) {
         best = dd;
@@ -257,7 +258,7 @@ __global__ __launch_bounds__(LW * 64) void encode_large_kernel(LArgs a) {
 
   // settle one listed block and replace its field of the record
   auto settle_fix = [&](const uint32_t* ent) {
-    const int bi = settle_block<K, TX>(a, x, ent, sX, sZd, lane);
+    const int bi = settle_block<K, TX>(a, x, a.cbh, ent, sX, sZd, lane);
     if (lane == 0) {
       const int64_t row = (int64_t)((uint64_t)ent[0] | ((uint64_t)ent[1] << 32));
       const int sh = LBITS * (int)(ent[2] & 0xFFu);
@@ -522,6 +523,8 @@ __global__ __launch_bounds__(LW * 64) void encode_large_kernel(LArgs a) {
   }
 }
 
+void set_bounds(LArgs& a, const fq_codebook* cb, int k, size_t xsize);
+
 template <int K, typename TX>
 hipError_t launch_large_k(const fq_codebook* cb, const TX* x, int64_t n, int64_t ld,
                           uint32_t* codes, uint16_t* norms, hipStream_t s) {
@@ -550,14 +553,332 @@ hipError_t launch_large_k(const fq_codebook* cb, const TX* x, int64_t n, int64_t
   a.enc = cb->t.enc;
   a.S = cb->enc_stride;
   a.pi64t = cb->t.pi64t;
-  // certification constants (bounds in the header), from the largest codeword norm
-  const double cm = cb->cmax, kk = K;
+  set_bounds(a, cb, K, sizeof(TX));
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(LW * 64), shm, s, a);
+  return hipGetLastError();
+}
+
+// ---- k = 8, N = 256 (one bit per coordinate) ---------------------------------
+//
+// The same search with the whole codebook (4 KB of binary16) resident in LDS:
+// a block of 8 coordinates is one column, and v_mfma_f32_16x16x16_f16
+// contracts [z_hi | z_lo] (16 values) against [c | c], so one instruction
+// scores 16 codewords against 16 columns with both halves of the split.  A
+// wave rotates 16 vectors and then takes their 128 columns in two sub-passes
+// of 4 blocks (4 column groups), each a sweep over the 16 tiles with the same
+// keys, slot tracking, certificate and exact settle of listed blocks; a
+// sub-pass stores one record word (4 byte-wide fields) per vector.  The
+// accumulator starts at K0 - |c|^2 / 2 (K0 = r + r^2 / 2, r the smallest
+// codeword norm): K0 cancels in every comparison and makes the best score of
+// any block of norm <= 1 non-negative, so blocks near the origin need no
+// full scan.
+constexpr int EW = 4;          // waves per workgroup
+constexpr int E8CG = 4;        // blocks (column groups) per sub-pass
+constexpr int E8N = 256;
+constexpr int E8NT = E8N / 16; // tiles
+constexpr size_t E8_WAVE_BYTES = (size_t)EV * ZP * 4 + 2 * 64 * 8 + FL_MAX * FL_WORDS * 4;
+constexpr size_t E8_TAB = (size_t)E8N * 8 * 2 + E8N * 4;   // codebook + -|c|^2 / 2
+constexpr size_t E8_LDS = E8_TAB + ROT_BYTES + EW * E8_WAVE_BYTES + EW * 4;
+
+template <typename TX>
+// (at least 3 waves per SIMD: at most 168 registers, no AGPR copies of the scores)
+__global__ __launch_bounds__(EW * 64, 3) void encode_k8_kernel(LArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const _Float16* sCb = reinterpret_cast<const _Float16*>(smem);        // [N][8]
+  float* sHn = reinterpret_cast<float*>(smem + E8N * 16);                // [N]
+  _Float16* sRot = reinterpret_cast<_Float16*>(smem + E8_TAB);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  unsigned char* wb = smem + E8_TAB + ROT_BYTES + wave * E8_WAVE_BYTES;
+  float* sZ = reinterpret_cast<float*>(wb);                               // [EV][ZP]
+  double* sX = reinterpret_cast<double*>(wb + EV * ZP * 4);              // exact path: x
+  double* sZd = sX + 64;                                                  // exact path: z block
+  uint32_t* sList = reinterpret_cast<uint32_t*>(sZd + 64);                // uncertain blocks
+  int* sCount = reinterpret_cast<int*>(smem + E8_TAB + ROT_BYTES + EW * E8_WAVE_BYTES);
+  int nfl = 0;
+  const int j = lane & 15, grp = lane >> 4;
+
+  for (int i = threadIdx.x; i < ROT_BYTES / 16; i += blockDim.x)
+    reinterpret_cast<u32x4*>(sRot)[i] = reinterpret_cast<const u32x4*>(a.rotfrag)[i];
+  for (int i = threadIdx.x; i < E8N; i += blockDim.x)
+    reinterpret_cast<u32x4*>(smem)[i] = reinterpret_cast<const u32x4*>(a.cbh)[i];
+  for (int i = threadIdx.x; i < E8N / 4; i += blockDim.x)
+    reinterpret_cast<floatx4*>(sHn)[i] = reinterpret_cast<const floatx4*>(a.hn)[i];
+  __syncthreads();
+
+  const TX* __restrict__ x = static_cast<const TX*>(a.x);
+  const int64_t n = a.n;
+  const int64_t wg_vecs = (int64_t)EW * EV;
+  const int64_t passes = (n + wg_vecs - 1) / wg_vecs;
+  // the lane's x row of pass gp (rows past the end repeat the last one)
+  auto xrow = [&](int64_t gp) {
+    const int64_t row0 = gp * wg_vecs + (int64_t)wave * EV;
+    const int64_t last = n - 1 - row0;
+    return x + (last < 0 ? n - 1 : row0 + (j < last ? j : last)) * a.ld;
+  };
+  XRaw<TX> xnext;
+  if (blockIdx.x < passes) load_raw<TX>(xrow(blockIdx.x), grp, xnext);
+
+  // settle one listed block and replace its byte of the record
+  auto settle_fix = [&](const uint32_t* ent) {
+    const int bi = settle_block<8, TX, E8N>(a, x, sCb, ent, sX, sZd, lane);
+    if (lane == 0) {
+      const int64_t row = (int64_t)((uint64_t)ent[0] | ((uint64_t)ent[1] << 32));
+      const int b = (int)(ent[2] & 0xFFu);
+      uint32_t* rp = a.codes + 2 * row + (b >> 2);
+      const int sh = 8 * (b & 3);
+      atomicAnd(rp, ~(0xFFu << sh));
+      atomicOr(rp, (uint32_t)bi << sh);
+    }
+  };
+
+  for (int64_t gp = blockIdx.x; gp < passes; gp += gridDim.x) {
+    const int64_t vbase = gp * wg_vecs + (int64_t)wave * EV;
+    const int64_t last = n - 1 - vbase;
+    {   // norm and rotation of the wave's 16 vectors; the next pass's x in flight
+      const XRaw<TX> xraw = xnext;
+      if (gp + gridDim.x < passes) load_raw<TX>(xrow(gp + gridDim.x), grp, xnext);
+      XFrag<TX> xf;
+      finish_x<TX>(xraw, xf);
+      const float nus = __builtin_amdgcn_sqrtf(xf.ss);
+      if (grp == 0 && j <= last) a.norms[vbase + j] = f32_to_f16_rne(nus * xf.escale);
+      rotate_to_lds<TX>(xf, sRot, __builtin_amdgcn_rcpf(nus), sZ, lane);
+      wave_lds_sync();
+    }
+
+#pragma unroll 1
+    for (int half = 0; half < 2; ++half) {
+      if (nfl > FL_MAX - 16 * E8CG) {   // room for this sub-pass's blocks
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's record stores have completed
+        for (int e = 0; e < nfl; ++e) settle_fix(sList + e * FL_WORDS);
+        nfl = 0;
+      }
+      // B operands: lanes of groups 0, 1 hold z_hi of coordinates 0-3, 4-7 of
+      // block 4 half + c, groups 2, 3 the lo parts of the same coordinates
+      half4 bz[E8CG];
+      float zz[E8CG];
+#pragma unroll
+      for (int c = 0; c < E8CG; ++c) {
+        const floatx4 z4 = *reinterpret_cast<const floatx4*>(sZ + j * ZP + 8 * (E8CG * half + c) + 4 * (grp & 1));
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const _Float16 hi = (_Float16)z4[e];
+          const _Float16 lo = (_Float16)(z4[e] - (float)hi);
+          bz[c][e] = grp < 2 ? hi : lo;
+          ss = fmaf(z4[e], z4[e], ss);
+        }
+        const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(ss), __float_as_uint(ss), false, false);
+        zz[c] = __uint_as_float(q[0]) + __uint_as_float(q[1]);   // coordinates 0-3 and 4-7
+      }
+      wave_lds_sync();
+
+      int m1[E8CG][4], m2[E8CG][4];
+#pragma unroll
+      for (int c = 0; c < E8CG; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) m1[c][r] = m2[c][r] = INT32_MIN;
+      // tile operands, read one tile ahead
+      const _Float16* ap = sCb + j * 8 + 4 * (grp & 1);
+      const float* hp = sHn + 4 * grp;
+      half4 avn = *reinterpret_cast<const half4*>(ap);
+      floatx4 c0n = *reinterpret_cast<const floatx4*>(hp);
+      auto scores = [&](int i, floatx4 (&acc)[E8CG]) {
+        const half4 av = avn;
+        const floatx4 c0 = c0n;
+        const int in = i + 1 < E8NT ? i + 1 : i;
+        avn = *reinterpret_cast<const half4*>(ap + 128 * in);
+        c0n = *reinterpret_cast<const floatx4*>(hp + 16 * in);
+#pragma unroll
+        for (int c = 0; c < E8CG; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, bz[c], c0, 0, 0, 0);
+      };
+      auto track = [&](const floatx4 (&acc)[E8CG], int i) {
+#pragma unroll
+        for (int c = 0; c < E8CG; ++c)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = (int)__builtin_amdgcn_perm(__float_as_uint(acc[c][r]), (uint32_t)i, 0x07060500u);
+            m2[c][r] = max(min(m1[c][r], m2[c][r]), min(max(m1[c][r], m2[c][r]), key));
+            m1[c][r] = max(m1[c][r], key);
+          }
+      };
+      // a loop (not unrolled): the running keys are carried tile to tile, so
+      // only two tiles' scores are live at a time
+      floatx4 accA[E8CG], accB[E8CG];
+      scores(0, accA);
+#pragma unroll 1
+      for (int i = 1; i < E8NT - 1; i += 2) {
+        scores(i, accB);
+        track(accA, i - 1);
+        scores(i + 1, accA);
+        track(accB, i);
+      }
+      scores(E8NT - 1, accB);
+      track(accA, E8NT - 2);
+      track(accB, E8NT - 1);
+
+      // merge the slots (in the lane, then over the four 16-lane rows on
+      // permlane swaps), certify (as for the large blocks); all four column
+      // groups first, so their latencies overlap, then the listing
+      int res[E8CG];
+      float lims[E8CG];
+      bool fulls[E8CG];
+      uint64_t unc[E8CG];
+#pragma unroll
+      for (int c = 0; c < E8CG; ++c) {
+        int b1 = m1[c][0], b2 = m2[c][0];
+        int r1 = 0;
+#pragma unroll
+        for (int r = 1; r < 4; ++r) {
+          const int o1 = m1[c][r], o2 = m2[c][r];
+          b2 = max(max(b2, o2), min(b1, o1));
+          const bool tk = o1 > b1;
+          b1 = tk ? o1 : b1;
+          r1 = tk ? r : r1;
+        }
+        int n1 = 16 * (int)key_tile(b1) + 4 * grp + r1;
+        // a swap hands each lane its partner's triple beside its own (in
+        // either order); the merge is symmetric, so both lanes agree
+        auto merge = [&](auto q1, auto q2, auto qn) {
+          const int u1 = (int)q1[0], v1 = (int)q1[1], u2 = (int)q2[0], v2 = (int)q2[1];
+          const int un = (int)qn[0], vn = (int)qn[1];
+          b2 = max(max(u2, v2), min(u1, v1));
+          const bool tk = v1 > u1 || (v1 == u1 && vn < un);
+          b1 = tk ? v1 : u1;
+          n1 = tk ? vn : un;
+        };
+        merge(__builtin_amdgcn_permlane16_swap((uint32_t)b1, (uint32_t)b1, false, false),
+              __builtin_amdgcn_permlane16_swap((uint32_t)b2, (uint32_t)b2, false, false),
+              __builtin_amdgcn_permlane16_swap((uint32_t)n1, (uint32_t)n1, false, false));
+        merge(__builtin_amdgcn_permlane32_swap((uint32_t)b1, (uint32_t)b1, false, false),
+              __builtin_amdgcn_permlane32_swap((uint32_t)b2, (uint32_t)b2, false, false),
+              __builtin_amdgcn_permlane32_swap((uint32_t)n1, (uint32_t)n1, false, false));
+        const float bv = key_value(b1);
+        const float zn = __builtin_amdgcn_sqrtf(zz[c]);
+        const float E = fmaf(a.EA, zn, a.EB);
+        const float M = fmaf(2.f, E, fmaf(0x1p-14f, fabsf(bv), a.ZT)) * 1.0001f + 1e-12f;
+        const float lim = bv - M;
+        // candidates (slot leaders within the margin) in the low byte, hidden
+        // slots (second keys within it) above
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          cnt += (key_value(m1[c][r]) >= lim ? 1u : 0u) + (key_value(m2[c][r]) >= lim ? 0x100u : 0u);
+        const auto c16 = __builtin_amdgcn_permlane16_swap(cnt, cnt, false, false);
+        cnt = c16[0] + c16[1];
+        const auto c32 = __builtin_amdgcn_permlane32_swap(cnt, cnt, false, false);
+        cnt = c32[0] + c32[1];
+        const bool finite = __builtin_isfinite(bv) && __builtin_isfinite(zz[c]) &&
+                            __builtin_isfinite(lim) && lim > 0.f;
+        const bool hid = (cnt >> 8) != 0;
+        const bool certain = finite && !hid && (cnt & 0xFFu) == 1;
+        res[c] = n1;
+        lims[c] = lim;
+        fulls[c] = !finite || hid;
+        unc[c] = __builtin_amdgcn_ballot_w64(lane < 16 && !certain);
+      }
+#pragma unroll
+      for (int c = 0; c < E8CG; ++c) {
+        uint64_t need = unc[c];
+        while (need) {
+          const int jj = __builtin_ctzll(need);
+          need &= need - 1;
+          const int64_t row = vbase + jj;
+          if (row >= n) continue;
+          const bool col_full = __builtin_amdgcn_readlane((int)fulls[c], jj) != 0;
+          const float col_lim = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(lims[c]), jj));
+          uint32_t* ent = sList + nfl * FL_WORDS;
+          uint16_t* ce = reinterpret_cast<uint16_t*>(ent + 4);
+          int nc = 0;
+          uint32_t hm = 0;
+          if (!col_full) {
+#pragma unroll
+            for (int lg = 0; lg < 4; ++lg)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int key = __builtin_amdgcn_readlane(m1[c][r], 16 * lg + jj);
+                const int key2 = __builtin_amdgcn_readlane(m2[c][r], 16 * lg + jj);
+                if (key_value(key) >= col_lim) {
+                  if (lane == 0 && nc < FL_CAND) ce[nc] = (uint16_t)(16 * (int)key_tile(key) + 4 * lg + r);
+                  ++nc;
+                }
+                if (key_value(key2) >= col_lim) hm |= 1u << (4 * lg + r);
+              }
+          }
+          if (lane == 0) {
+            ent[0] = (uint32_t)row;
+            ent[1] = (uint32_t)(row >> 32);
+            ent[2] = (uint32_t)(E8CG * half + c) | ((uint32_t)(nc < FL_CAND ? nc : FL_CAND) << 8) |
+                     ((col_full || nc > FL_CAND ? 1u : 0u) << 16);
+            ent[3] = hm;
+          }
+          wave_lds_sync();
+          ++nfl;
+        }
+      }
+      // word `half` of the record of vector j
+      if (grp == 0 && j <= last)
+        a.codes[2 * (vbase + j) + half] = (uint32_t)res[0] | ((uint32_t)res[1] << 8) |
+                                          ((uint32_t)res[2] << 16) | ((uint32_t)res[3] << 24);
+    }
+  }
+
+  // the workgroup's uncertain blocks, settled exactly and shared out over its waves
+  __builtin_amdgcn_s_waitcnt(0);
+  if (lane == 0) sCount[wave] = nfl;
+  __syncthreads();
+  int tot = 0;
+  for (int w = 0; w < EW; ++w) tot += sCount[w];
+  for (int g = wave; g < tot; g += EW) {
+    int w = 0, e = g;
+    while (e >= sCount[w]) e -= sCount[w++];
+    const uint32_t* ent = reinterpret_cast<const uint32_t*>(
+        reinterpret_cast<const unsigned char*>(sList) + (ptrdiff_t)(w - wave) * (ptrdiff_t)E8_WAVE_BYTES) +
+        e * FL_WORDS;
+    settle_fix(ent);
+  }
+}
+
+// certification constants for block length k (bounds in the header), from
+// the largest codeword norm
+void set_bounds(LArgs& a, const fq_codebook* cb, int k, size_t xsize) {
+  const double cm = cb->cmax, kk = k;
   const double acc = (2.0 * kk + 2.0) * 0x1p-23;
   a.EA = (float)(cm * (0x1p-22 + acc * 1.001) * 1.01);
-  a.EB = (float)((0x1p-25 * sqrt(kk) * cm + (acc + 0x1p-24) * cm * cm * 0.5) * 1.01);
-  const double ez = sizeof(TX) == 2 ? cb->enc_ez16 : cb->enc_ez32;
+  a.EB = (float)((0x1p-25 * sqrt(kk) * cm + (acc + 0x1p-24) * (cm * cm * 0.5 + cb->hshift)) * 1.01);
+  const double ez = xsize == 2 ? cb->enc_ez16 : cb->enc_ez32;
   a.ZT = (float)(2.0 * ez * sqrt(kk) * cm * 1.01);
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(LW * 64), shm, s, a);
+}
+
+template <typename TX>
+hipError_t launch_k8(const fq_codebook* cb, const TX* x, int64_t n, int64_t ld, uint32_t* codes,
+                     uint16_t* norms, hipStream_t s) {
+  if (cb->k != 8 || cb->N != E8N || cb->W != 2 || !cb->half_exact || cb->t.hnorm == nullptr)
+    return hipErrorInvalidValue;
+  auto kern = encode_k8_kernel<TX>;
+  const size_t shm = E8_LDS;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  if (e != hipSuccess) return e;
+  static const int64_t cap = resident_blocks(reinterpret_cast<const void*>(kern), EW * 64, shm);
+  if (cap <= 0) return hipErrorInvalidConfiguration;
+  const int64_t wg_vecs = (int64_t)EW * EV;
+  int64_t blocks = (n + wg_vecs - 1) / wg_vecs;
+  if (blocks > cap) blocks = cap;
+  LArgs a;
+  a.x = x;
+  a.n = n;
+  a.ld = ld;
+  a.codes = codes;
+  a.norms = norms;
+  a.rotfrag = cb->t.encfrag;
+  a.lfrag = nullptr;
+  a.hn = cb->t.hnorm;
+  a.cbh = cb->t.cb16hi;
+  a.enc = cb->t.enc;
+  a.S = cb->enc_stride;
+  a.pi64t = cb->t.pi64t;
+  set_bounds(a, cb, 8, sizeof(TX));
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(EW * 64), shm, s, a);
   return hipGetLastError();
 }
 
@@ -575,6 +896,16 @@ hipError_t launch_encode_large(const fq_codebook* cb, const void* x, fq_dtype xt
     if (cb->k == 64) return launch_large_k<64, float>(cb, xx, n, ld, codes, norms, s);
   }
   return hipErrorInvalidValue;
+}
+
+bool encode_k8_applies(const fq_codebook* cb) {
+  return cb->k == 8 && cb->N == E8N && cb->W == 2 && cb->half_exact && cb->t.hnorm != nullptr;
+}
+
+hipError_t launch_encode_k8(const fq_codebook* cb, const void* x, fq_dtype xt, int64_t n,
+                            int64_t ld, uint32_t* codes, uint16_t* norms, hipStream_t s) {
+  if (xt == FQ_F16) return launch_k8<_Float16>(cb, static_cast<const _Float16*>(x), n, ld, codes, norms, s);
+  return launch_k8<float>(cb, static_cast<const float*>(x), n, ld, codes, norms, s);
 }
 
 }  // namespace fq

@@ -92,6 +92,7 @@ struct fq_codebook {
   int grid1_G;      // cells of the last-block grid (k = 3)
   bool half_exact;  // every codeword coordinate is a binary16 number
   double cmax;      // largest codeword norm
+  double hshift;    // constant added to every score of the matrix-core k = 8 search
   std::vector<double> pi;  // host copy of Pi
   std::vector<float> c;    // host copy of C
   void* dev_block;         // the single device allocation
@@ -128,6 +129,11 @@ hipError_t launch_append(const fq_codebook* cb, const uint16_t* x1, const uint16
                          uint32_t* codes2, uint16_t* norms2, OutRows rows, hipStream_t s);
 hipError_t launch_encode_large(const fq_codebook* cb, const void* x, fq_dtype xt, int64_t n,
                                int64_t ld, uint32_t* codes, uint16_t* norms, hipStream_t s);
+// k = 8, N = 256 on the matrix cores (binary16-exact codebooks; plain row-major
+// records of two words)
+bool encode_k8_applies(const fq_codebook* cb);
+hipError_t launch_encode_k8(const fq_codebook* cb, const void* x, fq_dtype xt, int64_t n,
+                            int64_t ld, uint32_t* codes, uint16_t* norms, hipStream_t s);
 hipError_t launch_decode(const fq_codebook* cb, const uint32_t* codes, const uint16_t* norms,
                          const int64_t* rows, int64_t n_records, int64_t n, void* y,
                          fq_dtype yt, int64_t ld, hipStream_t s);

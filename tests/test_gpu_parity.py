@@ -100,12 +100,12 @@ def test_encode_variants_fp16(dev, k, N):
     print(f"k{k}N{N}: {ex} exact, {win} in window")
 
 
-@pytest.mark.parametrize("k", [32, 64])
-def test_encode_large_blocks_fp32_and_tiny(dev, k):
-    """k = 32 / 64, N = 4096 (matrix-core search): float32 input with the
-    special vectors, then inputs shorter than one wave's share (5 rows) and one
-    row past a workgroup's share (513 rows)."""
-    art, cb = book(k, 4096)
+@pytest.mark.parametrize("k,N", [(8, 256), (32, 4096), (64, 4096)])
+def test_encode_large_blocks_fp32_and_tiny(dev, k, N):
+    """The matrix-core searches (k = 8 with N = 256; k = 32 / 64 with N = 4096):
+    float32 input with the special vectors, then inputs shorter than one wave's
+    share (5 rows) and one row past a workgroup's share (513 rows)."""
+    art, cb = book(k, N)
     x = np.concatenate([synth.tiny_vectors(700, seed=3), synth.special_vectors(dtype=np.float32)])
     codes, norms = gpu_encode(cb, x, dev)
     ex, win = check_encode(art, x, codes, norms)
@@ -113,22 +113,22 @@ def test_encode_large_blocks_fp32_and_tiny(dev, k):
         xs = synth.kv_slab(2, 1, 0, 1, 1, m).reshape(-1, 64)
         c, nn = gpu_encode(cb, xs, dev)
         check_encode(art, xs, c, nn)
-    print(f"k{k}N4096 fp32: {ex} exact, {win} in window")
+    print(f"k{k}N{N} fp32: {ex} exact, {win} in window")
 
 
-@pytest.mark.parametrize("k", [32, 64])
-def test_encode_large_blocks_many_uncertain(dev, k):
+@pytest.mark.parametrize("k,N", [(8, 256), (32, 4096), (64, 4096)])
+def test_encode_large_blocks_many_uncertain(dev, k, N):
     """Runs of zero vectors (every block uncertain: all codewords scanned,
     index 0) between ordinary rows, more than one pass's worth per wave, so
     the list of uncertain blocks is settled early as well as at the end."""
-    art, cb = book(k, 4096)
+    art, cb = book(k, N)
     xs = synth.kv_slab(2, 3, 1, 1, 1, 9000).reshape(-1, 64).copy()
     xs[100:700] = 0.0
     xs[5000:5100] = 0.0
     codes, norms = gpu_encode(cb, xs, dev)
     ex, win = check_encode(art, xs, codes, norms)
     assert np.all(codes[100:700] == 0) and np.all(norms[100:700] == 0)
-    print(f"k{k}N4096 with zero runs: {ex} exact, {win} in window")
+    print(f"k{k}N{N} with zero runs: {ex} exact, {win} in window")
 
 
 @pytest.mark.parametrize("k", [32, 64])
