@@ -160,8 +160,12 @@ def test_large_blocks_gpt2_cache_full_size(dev, k):
           f"decode max err/nu {np.max(err / np.maximum(nu16, 1e-30)):.2e}")
 
 
-def test_encode_strided_rows_and_empty(dev):
-    art, cb = book(3, 512)
+@pytest.mark.parametrize("k,N", [(3, 512), (8, 256), (64, 4096)])
+def test_encode_strided_rows_and_empty(dev, k, N):
+    """Rows read with a stride (x_ld = 72, the extra columns ignored) give the
+    records of the packed rows; n = 0 is a no-op (grid, matrix-core k = 8 and
+    large-block kernels)."""
+    art, cb = book(k, N)
     x = synth.kv_slab(2, 1, 1, 1, 2, 300).reshape(-1, 64)
     wide = np.zeros((len(x), 72), dtype=np.float16)
     wide[:, :64] = x
@@ -170,6 +174,7 @@ def test_encode_strided_rows_and_empty(dev):
     codes, norms = fq.fq_encode(cb, xt[:, :64])
     torch.cuda.synchronize()
     c2, n2 = gpu_encode(cb, x, dev)
+    check_encode(art, x, c2, n2)
     assert np.array_equal(codes.cpu().numpy().view(np.uint32), c2)
     assert np.array_equal(norms.cpu().numpy().view(np.uint16), n2)
     e = torch.empty((0, 64), dtype=torch.float16, device=dev)
