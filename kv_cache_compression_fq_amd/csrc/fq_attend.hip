@@ -242,7 +242,7 @@ __device__ inline void finish_heads(const float* sMerge, int G, int Hq, int b, i
 // the table holds binary16 values) by float64 squared distance, ties to the
 // lowest index; the record (LSB-first fields) and the binary16 norm, rounded
 // once from the float64 norm.  scratch: 2 * 64 doubles + 64 words per wave.
-template <int K, int BITS>
+template <int K, int BITS, int RB>
 __device__ void append_one(const uint16_t* x, const _Float16* sTab, int tstride, int N,
                            const double* pi64t, uint32_t* rec, uint16_t* nrm, double* scratch,
                            int lane) {
@@ -253,7 +253,14 @@ __device__ void append_one(const uint16_t* x, const _Float16* sTab, int tstride,
   double* sX = scratch;
   double* sZ = scratch + D;
   uint32_t* sI = reinterpret_cast<uint32_t*>(scratch + 2 * D);
+  // the encode is latency-bound: x and the first RB rows of Pi^T are loaded
+  // before the norm's reduction, each further batch of RB rows once the
+  // previous one is used (D / RB round trips to memory; RB is what the
+  // calling kernel's register budget allows)
   const double xv = (double)f16_bits_to_f32(x[lane]);
+  double pv[RB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i) pv[i] = pi64t[i * D + lane];
   double ss = xv * xv;
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) {
@@ -267,12 +274,13 @@ __device__ void append_one(const uint16_t* x, const _Float16* sTab, int tstride,
   wave_lds_sync();
   double acc = 0.0;
 #pragma unroll 1
-  for (int h = 0; h < D / 8; ++h) {   // 8 rows of Pi^T in flight at a time
-    double pv[8];
+  for (int h = 0; h < D / RB; ++h) {
+    if (h > 0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pv[i] = pi64t[(8 * h + i) * D + lane];
+      for (int i = 0; i < RB; ++i) pv[i] = pi64t[(RB * h + i) * D + lane];
+    }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc = fma(pv[i], sX[8 * h + i], acc);
+    for (int i = 0; i < RB; ++i) acc = fma(pv[i], sX[RB * h + i], acc);
   }
   sZ[lane] = acc / nu;   // a zero vector gives NaN: every distance is NaN, index 0
   wave_lds_sync();
@@ -436,7 +444,7 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2))
         const uint16_t* x =
             (isv ? app.v_new : app.k_new) + (stream * app.M + (t - (T - app.M))) * D;
         const int64_t r = stream * Tld + t;
-        append_one<K, BITS>(x, isv ? sVh : sK, isv ? VST : KST, N, app.pi64t,
+        append_one<K, BITS, 8>(x, isv ? sVh : sK, isv ? VST : KST, N, app.pi64t,
                             (isv ? app.vc : app.kc) + r * W, (isv ? app.vn : app.kn) + r,
                             reinterpret_cast<double*>(sMerge) + wave * (2 * D + D / 2), lane);
       }
@@ -1120,7 +1128,7 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(3))
       const bool isv = v & 1;
       const uint16_t* x = (isv ? app.v_new : app.k_new) + (stream * app.M + (t - (T - app.M))) * D;
       const int64_t r = stream * Tld + t;
-      append_one<K, BITS>(x, isv ? sV : sK, K, N, app.pi64t, (isv ? app.vc : app.kc) + r * W,
+      append_one<K, BITS, 16>(x, isv ? sV : sK, K, N, app.pi64t, (isv ? app.vc : app.kc) + r * W,
                           (isv ? app.vn : app.kn) + r,
                           reinterpret_cast<double*>(sMerge) + wave * (2 * D + D / 2), lane);
     }
