@@ -333,6 +333,117 @@ __device__ void append_one(const uint16_t* x, const _Float16* sTab, int tstride,
   wave_lds_sync();
 }
 
+// The appended tokens of one (batch, KV head) that fall in a workgroup's
+// split, key and value of a token at a time with all four waves (k = 4 or 8,
+// binary16 tables in LDS): wave w forms the partial rotation of both vectors
+// over coordinates 16 w .. 16 w + 15 (its 16 rows of Pi^T, loaded once for
+// all tokens) and its share of both sums of squares; after a barrier, waves
+// 0 and 1 search half of the key's blocks each, waves 2 and 3 the value's;
+// after a second barrier waves 0 and 2 pack the records and store the norms.
+// The definition is append_one's (float64 norm, rotation and distances, ties
+// to the lowest index); only the order of the float64 sums differs.
+// scratch: 12 * 64 + 8 doubles and 2 * d / k words.
+template <int K, int BITS>
+__device__ void append_pairs(const AppendIn& app, int64_t stream, int64_t T, int64_t Tld, int64_t ap0,
+                             int64_t t1, const _Float16* sK, const _Float16* sV, int N, double* scr,
+                             int wave, int lane) {
+  constexpr int NB = D / K, W = Shape<K, BITS>::W;
+  constexpr int HB = NB / 2;    // blocks per searching wave
+  constexpr int P = 64 / HB;    // lanes per block: 8 (k = 4) or 16 (k = 8)
+  static_assert(K == 4 || K == 8, "k = 4 or 8");
+  double* sP = scr;                              // [wave][vector][64] partial rotations
+  double* sS = scr + 8 * D;                      // [wave][vector] partial sums of squares
+  double* sZ = scr + 8 * D + 8 + wave * D;       // this wave's z
+  uint32_t* sI = reinterpret_cast<uint32_t*>(scr + 12 * D + 8);   // [vector][NB] indices
+  double pv[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) pv[i] = app.pi64t[(16 * wave + i) * D + lane];
+  const int v = wave >> 1, hb = wave & 1;
+  const _Float16* tab = v ? sV : sK;
+  // x of token t (key and value; lane = coordinate), one token ahead
+  auto xload = [&](int64_t t, int& xk, int& xv) {
+    const int64_t row = stream * app.M + (t - (T - app.M));
+    xk = app.k_new[row * D + lane];
+    xv = app.v_new[row * D + lane];
+  };
+  int nk = 0, nv = 0;
+  if (ap0 < t1) xload(ap0, nk, nv);
+  for (int64_t t = ap0; t < t1; ++t) {
+    const int xk = nk, xv = nv;
+    if (t + 1 < t1) xload(t + 1, nk, nv);
+    double ak = 0.0, av = 0.0, sk = 0.0, sv = 0.0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const double a = (double)f16_bits_to_f32((uint16_t)__builtin_amdgcn_readlane(xk, 16 * wave + i));
+      const double c = (double)f16_bits_to_f32((uint16_t)__builtin_amdgcn_readlane(xv, 16 * wave + i));
+      ak = fma(pv[i], a, ak);
+      av = fma(pv[i], c, av);
+      sk = fma(a, a, sk);
+      sv = fma(c, c, sv);
+    }
+    sP[(2 * wave) * D + lane] = ak;
+    sP[(2 * wave + 1) * D + lane] = av;
+    if (lane == 0) {
+      sS[2 * wave] = sk;
+      sS[2 * wave + 1] = sv;
+    }
+    __syncthreads();
+    const double nu = sqrt(((sS[v] + sS[2 + v]) + sS[4 + v]) + sS[6 + v]);
+    // a zero vector gives NaN: every distance is NaN, index 0
+    sZ[lane] = (((sP[v * D + lane] + sP[(2 + v) * D + lane]) + sP[(4 + v) * D + lane]) +
+                sP[(6 + v) * D + lane]) / nu;
+    wave_lds_sync();
+    const int b = hb * HB + lane / P, p = lane % P;
+    double zb[K];
+#pragma unroll
+    for (int e = 0; e < K; ++e) zb[e] = sZ[b * K + e];
+    double best = INFINITY;
+    int bi = 0;
+    for (int cn = p; cn < N; cn += P) {
+      const _Float16* cr = tab + cn * K;
+      double dd = 0.0;
+#pragma unroll
+      for (int e = 0; e < K; ++e) {
+        const double df = zb[e] - (double)(float)cr[e];
+        dd = fma(df, df, dd);
+      }
+      if (dd < best) {
+        best = dd;
+        bi = cn;
+      }
+    }
+#pragma unroll
+    for (int m = P >> 1; m >= 1; m >>= 1) {
+      int2 q = __builtin_bit_cast(int2, best);
+      q.x = __shfl_xor(q.x, m, 64);
+      q.y = __shfl_xor(q.y, m, 64);
+      const double ob = __builtin_bit_cast(double, q);
+      const int oi = __shfl_xor(bi, m, 64);
+      if (ob < best || (ob == best && oi < bi)) {
+        best = ob;
+        bi = oi;
+      }
+    }
+    if (p == 0) sI[v * NB + b] = (uint32_t)bi;
+    __syncthreads();
+    if (hb == 0) {
+      const int64_t r = stream * Tld + t;
+      if (lane < W) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const int p0 = j * BITS - 32 * lane;
+          if (p0 >= 32 || p0 + BITS <= 0) continue;
+          const uint32_t f = sI[v * NB + j];
+          word |= p0 >= 0 ? (f << p0) : (f >> (-p0));
+        }
+        (v ? app.vc : app.kc)[r * W + lane] = word;
+      }
+      if (lane == 0) (v ? app.vn : app.kn)[r] = f64_to_f16_bits(nu);
+    }
+  }
+}
+
 template <int K, int BITS>
 __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void attend_split_kernel(
     const uint16_t* __restrict__ q, const uint32_t* __restrict__ kc,
@@ -1119,19 +1230,10 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(3))
   }
   __syncthreads();
   if (appends) {
-    // keys then values of tokens ap0 .. t1 - 1, one vector per wave at a time,
-    // from the binary16 tables now in LDS; the merge area is free until the end
-    const int nv = 2 * (int)(t1 - ap0);
-    const int64_t stream = (int64_t)b * Hkv + g;
-    for (int v = wave; v < nv; v += ATT_WAVES) {
-      const int64_t t = ap0 + v / 2;
-      const bool isv = v & 1;
-      const uint16_t* x = (isv ? app.v_new : app.k_new) + (stream * app.M + (t - (T - app.M))) * D;
-      const int64_t r = stream * Tld + t;
-      append_one<K, BITS, 16>(x, isv ? sV : sK, K, N, app.pi64t, (isv ? app.vc : app.kc) + r * W,
-                          (isv ? app.vn : app.kn) + r,
-                          reinterpret_cast<double*>(sMerge) + wave * (2 * D + D / 2), lane);
-    }
+    // tokens ap0 .. t1 - 1, key and value together on all four waves, from the
+    // binary16 tables now in LDS; the merge area is free until the end
+    append_pairs<K, BITS>(app, (int64_t)b * Hkv + g, T, Tld, ap0, t1, sK, sV, N,
+                          reinterpret_cast<double*>(sMerge), wave, lane);
     __threadfence_block();   // the new records are stored before any wave reads them
     __syncthreads();
 #pragma unroll
