@@ -248,6 +248,19 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
             lfrag[(((size_t)tile * kcs + kc) * 64 + lane) * 8 + e] =
                 cbh[(size_t)(16 * tile + lane % 16) * k + 32 * kc + 8 * (lane / 16) + e];
   }
+  // k = 2, N = 16 on the binary16 grid: the table of codeword pairs (byte j of
+  // a record holds the fields of blocks 2 j and 2 j + 1, LSB first, so it is
+  // the index of the pair (c_i0, c_i1) in this table)
+  std::vector<_Float16> pair16;
+  if (k == 2 && N == 16 && cb->half_exact) {
+    pair16.resize(256 * 4);
+    for (int i1 = 0; i1 < 16; ++i1)
+      for (int i0 = 0; i0 < 16; ++i0)
+        for (int t = 0; t < 2; ++t) {
+          pair16[(size_t)(i0 + 16 * i1) * 4 + t] = cbh[(size_t)i0 * 2 + t];
+          pair16[(size_t)(i0 + 16 * i1) * 4 + 2 + t] = cbh[(size_t)i1 * 2 + t];
+        }
+  }
   // Encode rotation error bound per coordinate of a unit vector.  Each output
   // is a float32 sum of four 16-product groups (each accumulated from zero,
   // at most 15 roundings) for the hi part and four for the lo part (scaled by
@@ -316,7 +329,7 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
                o_grid = take(2ull * grid.rec.size() + 64), o_grid1 = take(2ull * grid1.rec.size() + 64),
                o_pih = take(2ull * d * d), o_pil = take(2ull * d * d), o_pit = take(4ull * d * d),
                o_lfrag = take(2ull * lfrag.size()), o_hn = take(4ull * hnorm.size()),
-               o_pi64t = take(8ull * d * d);
+               o_pi64t = take(8ull * d * d), o_pair = take(2ull * pair16.size());
   cb->dev_bytes = off;
   {
     DeviceGuard g(device);
@@ -345,6 +358,7 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
     cb->t.grid1 = grid1.rec.empty() ? nullptr : reinterpret_cast<uint16_t*>(base + o_grid1);
     cb->t.lfrag = lfrag.empty() ? nullptr : reinterpret_cast<_Float16*>(base + o_lfrag);
     cb->t.hnorm = hnorm.empty() ? nullptr : reinterpret_cast<float*>(base + o_hn);
+    cb->t.pair16 = pair16.empty() ? nullptr : reinterpret_cast<_Float16*>(base + o_pair);
     std::vector<char> staging(off, 0);
     memcpy(staging.data() + o_pi64, cb->pi.data(), 8ull * d * d);
     memcpy(staging.data() + o_pi32, pi32.data(), 4ull * d * d);
@@ -362,6 +376,7 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
       }
     if (!lfrag.empty()) memcpy(staging.data() + o_lfrag, lfrag.data(), 2ull * lfrag.size());
     if (!hnorm.empty()) memcpy(staging.data() + o_hn, hnorm.data(), 4ull * hnorm.size());
+    if (!pair16.empty()) memcpy(staging.data() + o_pair, pair16.data(), 2ull * pair16.size());
     if (!grid.rec.empty()) memcpy(staging.data() + o_grid, grid.rec.data(), 2ull * grid.rec.size());
     if (!grid1.rec.empty())
       memcpy(staging.data() + o_grid1, grid1.rec.data(), 2ull * grid1.rec.size());

@@ -1404,19 +1404,27 @@ hipError_t launch_v(const fq_codebook* ck, const fq_codebook* cv, const uint16_t
                     const AppendIn& app) {
   float* ws = static_cast<float*>(workspace);
   hipError_t e;
+  // kernel A' over binary16 tables kt, vt of Nt entries of KD coordinates
+  auto direct = [&](auto kern, const _Float16* kt, const _Float16* vt, int Nt) {
+    const SplitPlan p = plan_splits(B, Hkv, T, SPLIT_TARGET_DIRECT);
+    hipLaunchKernelGGL(kern, dim3((unsigned)p.S, Hkv, B), dim3(ATT_THREADS), 0, s, q, kc, kn, vc, vn,
+                       Hq, Hkv, T, Tld, Mq, p.chunk, p.S, scale, ck->t.pi16hi, ck->t.pi16lo, kt, vt,
+                       Nt, ws, ck->t.pi32t, out, app);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || p.S == 1) return err;
+    hipLaunchKernelGGL(attend_merge_kernel, dim3(Hq * B), dim3(256), 0, s, ws, p.S, ck->t.pi32t, out);
+    return hipGetLastError();
+  };
   if constexpr (K == 4 || K == 8) {
-    if (ck->half_exact && cv->half_exact && T % 8 == 0 && Tld % 8 == 0) {
-      const SplitPlan p = plan_splits(B, Hkv, T, SPLIT_TARGET_DIRECT);
-      auto kern = attend_direct_kernel<K, BITS>;
-      hipLaunchKernelGGL(kern, dim3((unsigned)p.S, Hkv, B), dim3(ATT_THREADS), 0, s, q, kc, kn, vc,
-                         vn, Hq, Hkv, T, Tld, Mq, p.chunk, p.S, scale, ck->t.pi16hi, ck->t.pi16lo,
-                         ck->t.cb16hi, cv->t.cb16hi, ck->N, ws, ck->t.pi32t, out, app);
-      e = hipGetLastError();
-      if (e != hipSuccess || p.S == 1) return e;
-      hipLaunchKernelGGL(attend_merge_kernel, dim3(Hq * B), dim3(256), 0, s, ws, p.S, ck->t.pi32t,
-                         out);
-      return hipGetLastError();
-    }
+    if (ck->half_exact && cv->half_exact && T % 8 == 0 && Tld % 8 == 0)
+      return direct(attend_direct_kernel<K, BITS>, ck->t.cb16hi, cv->t.cb16hi, ck->N);
+  }
+  if constexpr (K == 2 && BITS == 4) {
+    // k = 2, N = 16: a record's bytes index codeword pairs, so it is read as a
+    // k = 4, N = 256 record over the pair tables (the appended tokens are then
+    // searched over pairs: the nearest pair is the pair of nearest codewords)
+    if (ck->t.pair16 && cv->t.pair16 && T % 8 == 0 && Tld % 8 == 0)
+      return direct(attend_direct_kernel<4, 8>, ck->t.pair16, cv->t.pair16, 256);
   }
   const bool fuse = app.M > 0 && ck->half_exact && cv->half_exact;
   if (app.M > 0 && !fuse) {   // appended tokens first, by their own launch

@@ -55,6 +55,8 @@ struct DeviceTables {
   _Float16* lfrag;    // k >= 32: codebook as v_mfma_f32_16x16x32_f16 A fragments,
                       // [tile][kc][lane][8] = C[16 tile + lane % 16][32 kc + 8 (lane / 16) + e]
   float* hnorm;       // k >= 32: -|c_n|^2 / 2 in float32
+  _Float16* pair16;   // k = 2, N = 16, binary16-exact: [256][4] codeword pairs, entry
+                      // i0 + 16 i1 = (c_i0, c_i1), so a record reads as k = 4, N = 256
 };
 
 // Candidate-list grids for the block search (fq_grid.cpp).

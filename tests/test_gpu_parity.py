@@ -260,6 +260,10 @@ ATT_CASES = [
     (8, 16, 2, 200, (2, 16)),
     (128, 8, 8, 130, (2, 64)),
     (1, 4, 4, 130, (2, 128)),
+    # k = 2, N = 16 read as k = 4, N = 256 over codeword pairs: the GPT-2
+    # shape (one query head per KV head) and grouped heads
+    (4, 12, 12, 1024, (2, 16)),
+    (2, 16, 2, 2056, (2, 16)),
 ]
 
 
@@ -327,11 +331,13 @@ def test_attend_queries(dev, case):
 
 STEP_CASES = [
     # (codebook, M, pos, separate K and V handles); pos + M a multiple of 8
-    # with k = 4, 8 takes the attention kernel that encodes the appended
-    # tokens itself, the rest an append launch ahead of the attention
+    # with k = 4, 8 (and k = 2, N = 16 over codeword pairs) takes the direct
+    # kernel, which encodes the appended tokens on all four waves; the rest
+    # encode them one wave per vector inside the staged kernel
     ((4, 256), 1, 101, False), ((4, 256), 3, 101, False), ((2, 16), 1, 101, False),
     ((2, 64), 4, 101, False), ((4, 256), 1, 103, False), ((8, 256), 8, 96, False),
     ((4, 256), 2, 62, True), ((2, 16), 2, 5, True), ((8, 16), 1, 0, False),
+    ((2, 16), 1, 103, False), ((2, 16), 3, 61, True),
 ]
 
 
