@@ -1,6 +1,8 @@
-// FibQuant encode for large blocks: k = 32 and k = 64 (one or two blocks per
-// vector) with N = 4096 codewords (FibQuant technical summary, sections 2.2
-// and 2.3; the extreme rates below one bit per coordinate of section 4).
+// FibQuant encode on the matrix cores (FibQuant technical summary, sections
+// 2.2 and 2.3): large blocks, k = 32 and k = 64 (one or two blocks per vector)
+// with N = 4096 codewords (the extreme rates below one bit per coordinate of
+// section 4), and k = 8 with N = 256 (one bit per coordinate; at the end of
+// the file).
 //
 // The nearest-codeword search is a dense contraction here: every block is
 // compared with all 4096 codewords of k coordinates, 4096 k multiply-adds per
