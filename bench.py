@@ -160,6 +160,31 @@ def measured_traffic(op):
     return None if best is None else best[1]
 
 
+def measured_utilisation(op):
+    """VALU and MFMA utilisation of `op`'s kernel from the committed counter summary
+    (rocprofv3 VALUBusy, VALUUtilization, MfmaUtil; the largest grid, which is the
+    step's launch), or None when there is none or the library sources changed."""
+    path = os.path.join(ROOT, "profiles", "fq_search_utilisation_valu_mfma_bench.txt")
+    label = _KERNEL_LABEL.get(op)
+    if label is None or not os.path.exists(path):
+        return None
+    text = open(path).read().splitlines()
+    if f"source-sha256: {source_digest()}" not in text:
+        return None
+    best = None
+    for line in text:
+        f = line.split()
+        if len(f) != 8 or f[0] != label:
+            continue
+        try:
+            wg, busy, lanes, mfma = int(f[1]), float(f[3]), float(f[4]), float(f[5])
+        except ValueError:
+            continue
+        if best is None or wg > best[0]:
+            best = (wg, {"valu_busy_pct": busy, "valu_lanes_pct": lanes, "mfma_busy_pct": mfma})
+    return None if best is None else best[1]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -268,6 +293,7 @@ def main():
         e["ops_per_vector"] = enc_ops_per_vector(k, N)
         e["alu_tops"] = e["vectors_per_s"] * e["ops_per_vector"] / 1e12
         e["alu_frac"] = e["alu_tops"] / VALU_PEAK_TOPS
+        e["utilisation"] = measured_utilisation(f"encode_k{k}N{N}")
         d = ops[f"decode_k{k}N{N}"]
         d["vectors_per_s"] = n / (d["ms_avg"] * 1e-3)
         d["bytes_per_vector"] = record_bytes(k, N) + 2 + 128
