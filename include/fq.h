@@ -104,12 +104,13 @@ void fq_codebook_free(fq_codebook* cb);
  * indices at fixed rate and store the norm [FQ 1].
  *
  *   x      [n rows, stride x_ld elements] of x_dtype (FQ_F16 or FQ_F32), row r at
- *          x + r * x_ld; x_ld >= 64; rows 16-byte aligned when x_ld is a
- *          multiple of 8 (F16) / 4 (F32), else 4-byte aligned.
+ *          x + r * x_ld; x_ld >= 64 and x_ld * element size a multiple of 16 bytes
+ *          (x_ld a multiple of 8 for F16, of 4 for F32); x 16-byte aligned.
+ *          Other strides or alignments return FQ_ERR_INVALID_ARG.
  *   codes  [n, record_words] uint32 out, 4-byte aligned: field j (idx_bits bits)
  *          at bits [j*idx_bits, (j+1)*idx_bits) of the record, counted from the
  *          least significant bit of little-endian words; unused bits are 0.
- *   norms  [n] binary16 out (bit patterns), nu rounded to nearest-even.
+ *   norms  [n] binary16 out (bit patterns), 2-byte aligned, nu rounded to nearest-even.
  *   A zero vector gets all-zero indices and norm 0.  n == 0 is a no-op.
  *   Indices agree with a float64 evaluation of the same distances except
  *   where two distances lie within a relative 1e-6 of each other.
@@ -125,11 +126,14 @@ fq_status fq_encode(const fq_codebook* cb, const void* x, fq_dtype x_dtype, int6
  * out-of-range address decodes to a zero row); when NULL, row i decodes
  * record i and n_records is ignored.
  *
- *   codes [n_records, record_words] uint32, norms [n_records] binary16 (layout of fq_encode)
+ *   codes [n_records, record_words] uint32 (4-byte aligned), norms [n_records] binary16
+ *         (2-byte aligned), the layout of fq_encode
  *   rows  [n] int64 or NULL, 8-byte aligned; with rows, the record array may span at
  *         most 2^31 - 1 bytes (n_records * record_words * 4), else FQ_ERR_UNSUPPORTED
  *   y     [n rows, stride y_ld elements] of y_dtype out (F16 rounded to
- *         nearest-even, or F32); y_ld >= 64
+ *         nearest-even, or F32); y 16-byte aligned, y_ld >= 64 and y_ld * element
+ *         size a multiple of 16 bytes (else FQ_ERR_INVALID_ARG), y_ld <= 2^22
+ *         (else FQ_ERR_UNSUPPORTED)
  */
 fq_status fq_decode(const fq_codebook* cb, const uint32_t* codes, const uint16_t* norms,
                     const int64_t* rows, int64_t n_records, int64_t n, void* y,
@@ -157,10 +161,12 @@ fq_status fq_attend_workspace_size(const fq_codebook* cb_k, int B, int Hq, int H
  *   Hq % Hkv == 0, Hq / Hkv <= 8, T >= 1; workspace of at least
  *   fq_attend_workspace_size bytes, 256-byte aligned, contents need not be
  *   initialised.  cb_k and cb_v may be the same handle; they must be on the
- *   same device and hold the same (k, N) variant (one shared codebook serves
- *   keys and values [FQ 2.1]); the k = 3, N = 4096 tables and the k = 32, 64
- *   tables exceed the kernel's LDS budget (FQ_ERR_UNSUPPORTED).  All pointers
- *   16-byte aligned.
+ *   same device (else FQ_ERR_INVALID_ARG) and hold the same (k, N) variant and
+ *   the same rotation Pi (one shared codebook and one shared rotation serve
+ *   keys and values [FQ 1, 2.1, 2.3]; else FQ_ERR_UNSUPPORTED, since scores
+ *   and values are formed in one rotated domain); the k = 3, N = 4096 tables
+ *   and the k = 32, 64 tables exceed the kernel's LDS budget
+ *   (FQ_ERR_UNSUPPORTED).  All pointers 16-byte aligned.
  */
 fq_status fq_attend_decode(const fq_codebook* cb_k, const fq_codebook* cb_v, const uint16_t* q,
                            const uint32_t* k_codes, const uint16_t* k_norms,
@@ -201,7 +207,7 @@ fq_status fq_attend_queries(const fq_codebook* cb_k, const fq_codebook* cb_v, co
  * their tiles (codebooks whose tables hold binary16 values, as the shipped
  * ones do), otherwise an append launch precedes the attention; no host
  * synchronisation and no intermediate buffers.  Keys and values share the
- * rotation of cb_k (the one shared rotation).
+ * rotation of cb_k, which must equal cb_v's (the one shared rotation).
  *
  *   k_new, v_new  [B, Hkv, M, 64] binary16
  *   caches        as fq_attend_queries, capacity T_ld tokens; slots >= pos + M

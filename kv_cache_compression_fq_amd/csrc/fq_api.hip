@@ -12,84 +12,7 @@
 
 namespace {
 
-constexpr uint32_t HEADER_BYTES = 256;
-constexpr uint32_t VERSION = 1;
-
-struct Header {
-  char magic[4];
-  uint32_t version, header_bytes, d, k, N, nb, bits, W, last, restarts, max_iter, iters, best;
-  uint64_t seed_rot, samples;
-  double tol, d_train, d_test, rate_nom, rate_act, law_a, law_b;
-};
-static_assert(sizeof(Header) == 128, "header layout");
-
-uint64_t fnv1a64(const unsigned char* p, size_t n) {
-  uint64_t h = 0xCBF29CE484222325ull;
-  for (size_t i = 0; i < n; ++i) {
-    h ^= p[i];
-    h *= 0x100000001B3ull;
-  }
-  return h;
-}
-
-bool is_pow2(uint32_t v) { return v && !(v & (v - 1)); }
-
-// Parse + validate.  On success fills hdr and returns pointers into the blob.
-fq_status parse(const void* blob, size_t nbytes, Header* hdr, const double** pi,
-                const float** cw) {
-  if (!blob) return FQ_ERR_INVALID_ARG;
-  if (nbytes < HEADER_BYTES + 8) return FQ_ERR_BAD_ARTIFACT;
-  const unsigned char* b = static_cast<const unsigned char*>(blob);
-  memcpy(hdr, b, sizeof(Header));
-  if (memcmp(hdr->magic, "FQCB", 4) != 0 || hdr->version != VERSION ||
-      hdr->header_bytes != HEADER_BYTES)
-    return FQ_ERR_BAD_ARTIFACT;
-  for (size_t i = sizeof(Header); i < HEADER_BYTES; ++i)
-    if (b[i] != 0) return FQ_ERR_BAD_ARTIFACT;
-  const uint32_t d = hdr->d, k = hdr->k, N = hdr->N;
-  if (d < 1 || d > 4096 || k < 1 || k > d || !is_pow2(N) || N < 2 || N > (1u << 20))
-    return FQ_ERR_BAD_ARTIFACT;
-  const uint64_t want = HEADER_BYTES + 8ull * d * d + 4ull * N * k + 8;
-  if (nbytes != want) return FQ_ERR_BAD_ARTIFACT;
-  uint32_t bits = 0;
-  while ((1u << bits) < N) ++bits;
-  const uint32_t nb = (d + k - 1) / k;
-  if (hdr->nb != nb || hdr->bits != bits || hdr->W != (nb * bits + 31) / 32 ||
-      hdr->last != d - (nb - 1) * k)
-    return FQ_ERR_BAD_ARTIFACT;
-  uint64_t h;
-  memcpy(&h, b + want - 8, 8);
-  if (h != fnv1a64(b, want - 8)) return FQ_ERR_BAD_ARTIFACT;
-  *pi = reinterpret_cast<const double*>(b + HEADER_BYTES);
-  *cw = reinterpret_cast<const float*>(b + HEADER_BYTES + 8ull * d * d);
-  // payload is not guaranteed aligned inside the caller's blob: check through memcpy
-  for (uint64_t i = 0; i < (uint64_t)d * d; ++i) {
-    double v;
-    memcpy(&v, b + HEADER_BYTES + 8 * i, 8);
-    if (!isfinite(v)) return FQ_ERR_BAD_ARTIFACT;
-  }
-  for (uint64_t i = 0; i < (uint64_t)N * k; ++i) {
-    float v;
-    memcpy(&v, b + HEADER_BYTES + 8ull * d * d + 4 * i, 4);
-    if (!isfinite(v)) return FQ_ERR_BAD_ARTIFACT;
-  }
-  // orthogonality of Pi
-  std::vector<double> P((size_t)d * d);
-  memcpy(P.data(), b + HEADER_BYTES, 8ull * d * d);
-  double worst = 0;
-  for (uint32_t i = 0; i < d; ++i)
-    for (uint32_t j = i; j < d; ++j) {
-      double s = 0;
-      for (uint32_t r = 0; r < d; ++r) s += P[(size_t)r * d + i] * P[(size_t)r * d + j];
-      worst = fmax(worst, fabs(s - (i == j ? 1.0 : 0.0)));
-    }
-  if (worst > 1e-9) return FQ_ERR_BAD_ARTIFACT;
-  if (d != (uint32_t)fq::D || N > (uint32_t)fq::MAX_N || !fq::variant_supported(k, bits))
-    return FQ_ERR_UNSUPPORTED;
-  return FQ_OK;
-}
-
-void fill_info(const Header& h, fq_info* o) {
+void fill_info(const fq::ArtifactHeader& h, fq_info* o) {
   o->d = h.d;
   o->k = h.k;
   o->N = h.N;
@@ -120,6 +43,14 @@ struct DeviceGuard {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Keys and values attended together: the same (k, N) variant and the same
+// rotation.  The kernels score and accumulate in one rotated domain and rotate
+// the output back once, which is exact only when both caches were coded with
+// the one shared rotation (FibQuant technical summary, sections 1 and 2.3).
+bool same_variant(const fq_codebook* a, const fq_codebook* b) {
+  return a->k == b->k && a->N == b->N && a->pi_digest == b->pi_digest;
+}
+
 }  // namespace
 
 extern "C" {
@@ -137,10 +68,8 @@ const char* fq_status_string(fq_status s) {
 }
 
 fq_status fq_artifact_check(const void* artifact, size_t nbytes, fq_info* out) {
-  Header h;
-  const double* pi;
-  const float* cw;
-  fq_status st = parse(artifact, nbytes, &h, &pi, &cw);
+  fq::ArtifactHeader h;
+  fq_status st = fq::parse_artifact(artifact, nbytes, &h, nullptr, nullptr);
   if ((st == FQ_OK || st == FQ_ERR_UNSUPPORTED) && out) {
     fill_info(h, out);
     uint64_t hh;
@@ -153,10 +82,9 @@ fq_status fq_artifact_check(const void* artifact, size_t nbytes, fq_info* out) {
 fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_codebook** out) {
   if (!out) return FQ_ERR_INVALID_ARG;
   *out = nullptr;
-  Header h;
-  const double* pi_p;
-  const float* cw_p;
-  fq_status st = parse(artifact, nbytes, &h, &pi_p, &cw_p);
+  fq::ArtifactHeader h;
+  const unsigned char *pi_p = nullptr, *cw_p = nullptr;
+  fq_status st = fq::parse_artifact(artifact, nbytes, &h, &pi_p, &cw_p);
   if (st != FQ_OK) return st;
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) return FQ_ERR_DEVICE;
@@ -181,6 +109,7 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
   cb->pi.resize((size_t)d * d);
   cb->c.resize((size_t)N * k);
   memcpy(cb->pi.data(), pi_p, 8ull * d * d);
+  cb->pi_digest = fq::fnv1a64(pi_p, 8ull * d * d);
   memcpy(cb->c.data(), cw_p, 4ull * N * k);
 
   // host-side tables
@@ -305,13 +234,17 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
   fq::GridTable grid, grid1;
   cb->grid_G = 0;
   cb->grid1_G = 0;
-  if (k == 2 || k == 3 || (k == 4 && N >= 64)) {
-    const int G = (k == 2) ? (N <= 64 ? 32 : 64) : (k == 3 ? (N <= 512 ? 32 : 64) : 14);
-    fq::build_grid(cb->c.data(), N, k, k, G, fq::GRID_R, fq::grid_record_entries(k), (uint16_t)N, &grid);
-    cb->grid_G = G;
-    if (cb->last < k) {
-      fq::build_grid(cb->c.data(), N, k, 1, 4 * N, fq::GRID_R, fq::grid_record_entries(k), (uint16_t)N, &grid1);
-      cb->grid1_G = 4 * N;
+  {
+    int G = 0, G1 = 0;
+    if (fq::grid_plan(k, N, cb->last, &G, &G1)) {
+      fq::build_grid(cb->c.data(), N, k, k, G, fq::GRID_R, fq::grid_record_entries(k), (uint16_t)N,
+                     &grid);
+      cb->grid_G = G;
+      if (G1 > 0) {
+        fq::build_grid(cb->c.data(), N, k, 1, G1, fq::GRID_R, fq::grid_record_entries(k),
+                       (uint16_t)N, &grid1);
+        cb->grid1_G = G1;
+      }
     }
   }
 
@@ -486,7 +419,7 @@ fq_status fq_attend_decode(const fq_codebook* cb_k, const fq_codebook* cb_v, con
   fq_status st = check_attend_shape(cb_k, B, Hq, Hkv, T);
   if (st != FQ_OK) return st;
   if (!cb_v || cb_v->device != cb_k->device) return FQ_ERR_INVALID_ARG;
-  if (cb_v->k != cb_k->k || cb_v->N != cb_k->N) return FQ_ERR_UNSUPPORTED;
+  if (!same_variant(cb_k, cb_v)) return FQ_ERR_UNSUPPORTED;
   if (!q || !k_codes || !k_norms || !v_codes || !v_norms || !workspace || !out)
     return FQ_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) ||
@@ -513,7 +446,7 @@ static fq_status check_queries(const fq_codebook* cb_k, const fq_codebook* cb_v,
   fq_status st = check_attend_shape(cb_k, B, Hq * M, Hkv, T);
   if (st != FQ_OK) return st;
   if (!cb_v || cb_v->device != cb_k->device) return FQ_ERR_INVALID_ARG;
-  if (cb_v->k != cb_k->k || cb_v->N != cb_k->N) return FQ_ERR_UNSUPPORTED;
+  if (!same_variant(cb_k, cb_v)) return FQ_ERR_UNSUPPORTED;
   if (T_ld > (int64_t(1) << 31)) return FQ_ERR_UNSUPPORTED;
   return FQ_OK;
 }

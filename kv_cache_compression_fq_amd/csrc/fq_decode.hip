@@ -272,7 +272,8 @@ hipError_t launch_k(const fq_codebook* cb, const uint32_t* codes, const uint16_t
   if (e != hipSuccess) return e;
   // persistent grid: as many workgroups as fit at once (queried on first use;
   // one (k, bits) pair fixes the LDS need)
-  static const int64_t cap = resident_blocks(reinterpret_cast<const void*>(kern), DEC_THREADS, shm);
+  static DeviceCache cap_cache;   // resident workgroups per device
+  const int64_t cap = cap_cache.get(reinterpret_cast<const void*>(kern), DEC_THREADS, shm);
   if (cap <= 0) return hipErrorInvalidConfiguration;
   const int64_t n_chunks = (n + CHUNK - 1) / CHUNK;
   int64_t blocks = (n_chunks + DEC_WAVES - 1) / DEC_WAVES;

@@ -158,10 +158,8 @@ __device__ inline void prepare_column(ColPrep<K, RW>& cp, const float* zrow, boo
     int cell = 0, mul = 1;
 #pragma unroll
     for (int t = 0; t < KR; ++t) {
-      cp.inside = cp.inside && cp.z[t] >= -(float)GRID_R && cp.z[t] < (float)GRID_R;
-      int u = (int)((cp.z[t] + (float)GRID_R) * gscale);
-      u = u < 0 ? 0 : (u >= G ? G - 1 : u);
-      cell += u * mul;
+      cp.inside = cp.inside && grid_inside(cp.z[t]);
+      cell += grid_axis(cp.z[t], G, gscale) * mul;
       mul *= G;
     }
     const uint32_t* rp = reinterpret_cast<const uint32_t*>(grid + (size_t)cell * (2 * RW));
@@ -375,9 +373,8 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
       const int v = lane < EV ? lane : 0;
       const double z0 = sZL[v];
       const float zf = (float)z0;
-      const bool inside = live && zf >= -(float)GRID_R && zf < (float)GRID_R;
-      int u = (int)((zf + (float)GRID_R) * a.g1scale);
-      u = u < 0 ? 0 : (u >= a.G1 ? a.G1 - 1 : u);
+      const bool inside = live && grid_inside(zf);
+      const int u = grid_axis(zf, a.G1, a.g1scale);
       const uint32_t* rp = reinterpret_cast<const uint32_t*>(a.grid1 + (size_t)u * (2 * RW));
       uint32_t rec[RW];
 #pragma unroll
@@ -473,10 +470,8 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
         for (int t = 0; t < K; ++t)
           if (t < dims) {
             const float zf = (float)zd[t];
-            inside = inside && zf >= -(float)GRID_R && zf < (float)GRID_R;
-            int u = (int)((zf + (float)GRID_R) * sc);
-            u = u < 0 ? 0 : (u >= G ? G - 1 : u);
-            cell += u * mul;
+            inside = inside && grid_inside(zf);
+            cell += grid_axis(zf, G, sc) * mul;
             mul *= G;
           }
         rec = (last ? a.grid1 : a.grid) + (size_t)cell * (2 * RW);
@@ -539,8 +534,10 @@ hipError_t launch_k(const fq_codebook* cb, const TX* x, int64_t n, int64_t ld, u
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
-  static int64_t cap = 0;
-  if (cap == 0) cap = resident_blocks(reinterpret_cast<const void*>(kern), WAVES * 64, shm);
+  // resident workgroups per device, computed on first use (the dynamic LDS
+  // size depends only on the variant, like the kernel)
+  static DeviceCache cap_cache;
+  const int64_t cap = cap_cache.get(reinterpret_cast<const void*>(kern), WAVES * 64, shm);
   const int64_t chunks = (n + (second.x ? second.n : 0) + EV - 1) / EV;
   int64_t blocks = (chunks + WAVES - 1) / WAVES;
   if (cap > 0 && blocks > cap) blocks = cap;
@@ -560,8 +557,8 @@ hipError_t launch_k(const fq_codebook* cb, const TX* x, int64_t n, int64_t ld, u
   a.grid1 = cb->t.grid1 ? cb->t.grid1 : cb->t.grid;
   a.G = cb->grid_G;
   a.G1 = cb->grid1_G > 0 ? cb->grid1_G : 1;
-  a.gscale = (float)(cb->grid_G / (2.0 * GRID_R));
-  a.g1scale = (float)(a.G1 / (2.0 * GRID_R));
+  a.gscale = grid_scale(cb->grid_G);
+  a.g1scale = grid_scale(a.G1);
   a.rows = rows;
   a.n1 = n;
   a.x2 = nullptr;

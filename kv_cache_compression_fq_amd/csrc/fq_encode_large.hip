@@ -537,7 +537,8 @@ hipError_t launch_large_k(const fq_codebook* cb, const TX* x, int64_t n, int64_t
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
-  static const int64_t cap = resident_blocks(reinterpret_cast<const void*>(kern), LW * 64, shm);
+  static DeviceCache cap_cache;   // resident workgroups per device
+  const int64_t cap = cap_cache.get(reinterpret_cast<const void*>(kern), LW * 64, shm);
   if (cap <= 0) return hipErrorInvalidConfiguration;
   const int64_t wg_vecs = (int64_t)LW * Sh::VPW;
   int64_t blocks = (n + wg_vecs - 1) / wg_vecs;
@@ -861,7 +862,8 @@ hipError_t launch_k8(const fq_codebook* cb, const TX* x, int64_t n, int64_t ld, 
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
-  static const int64_t cap = resident_blocks(reinterpret_cast<const void*>(kern), EW * 64, shm);
+  static DeviceCache cap_cache;   // resident workgroups per device
+  const int64_t cap = cap_cache.get(reinterpret_cast<const void*>(kern), EW * 64, shm);
   if (cap <= 0) return hipErrorInvalidConfiguration;
   const int64_t wg_vecs = (int64_t)EW * EV;
   int64_t blocks = (n + wg_vecs - 1) / wg_vecs;

@@ -27,9 +27,28 @@
 #include <utility>
 #include <vector>
 
-#include "fq_internal.h"
+#include "fq_host.h"
 
 namespace fq {
+
+// Grid sizes per codebook: cells of about a quarter (k = 2) or a third
+// (k = 3) of the codeword spacing keep lists short; the one-coordinate last
+// block of k = 3 gets 4N cells; k = 4 gets 14^4 cells, which holds the lists
+// of a 256-codeword table within 31 entries.  Other codebooks scan.
+bool grid_plan(int k, int N, int last, int* G, int* G1) {
+  *G = 0;
+  *G1 = 0;
+  if (k == 2)
+    *G = N <= 64 ? 32 : 64;
+  else if (k == 3)
+    *G = N <= 512 ? 32 : 64;
+  else if (k == 4 && N >= 64)
+    *G = 14;
+  else
+    return false;
+  if (last < k) *G1 = 4 * N;
+  return true;
+}
 
 void build_grid(const float* cw, int N, int k, int dims, int G, double R, int re, uint16_t pad,
                 GridTable* out) {

@@ -4,37 +4,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <vector>
 
 #include "fq.h"
+#include "fq_host.h"
 
 namespace fq {
-
-constexpr int D = 64;             // vector length handled by the kernels
-constexpr int MAX_N = 4096;       // largest codebook
-constexpr int MAX_WORDS = 12;     // record words for k >= 2, N <= 4096: ceil(32*12/32)
-constexpr int MAX_QUERIES = 8;    // queries per head in one attention call
-
-// (k, index bits) pairs the kernels are built for: the configurations' rates
-// (k=2: N 16 / 64 / 256, k=3: N 512 / 4096, k=4: N 4 / 256, k=8: N 16 / 256)
-// plus the fractional k=2 rates 2.5 and 3.5 (N 32 / 128).  X(k, bits).
-#define FQ_VARIANTS(X) \
-  X(2, 4) X(2, 5) X(2, 6) X(2, 7) X(2, 8) X(3, 9) X(3, 12) X(4, 2) X(4, 8) X(8, 4) X(8, 8)
-
-// Large blocks (k = d/2 and k = d, N = 4096): the table exceeds LDS, so they
-// have their own encode kernel (fq_encode_large.hip) and a decode that gathers
-// codewords from the L2-resident table.
-#define FQ_VARIANTS_LARGE(X) X(32, 12) X(64, 12)
-
-inline bool variant_supported(int k, int bits) {
-#define FQ_IS(KK, BB) if (k == KK && bits == BB) return true;
-  FQ_VARIANTS(FQ_IS)
-  FQ_VARIANTS_LARGE(FQ_IS)
-#undef FQ_IS
-  return false;
-}
-
-__host__ __device__ constexpr bool large_block(int k) { return k >= 32; }
 
 // Per-codebook device tables, all inside one allocation.
 struct DeviceTables {
@@ -59,27 +35,6 @@ struct DeviceTables {
                       // i0 + 16 i1 = (c_i0, c_i1), so a record reads as k = 4, N = 256
 };
 
-// Candidate-list grids for the block search (fq_grid.cpp).
-// uint16 entries per cell record: count + up to 7 (k = 2) or 15 (k = 3) candidates
-__host__ __device__ constexpr int grid_record_entries(int k) { return k == 2 ? 8 : (k == 3 ? 16 : 32); }
-constexpr uint16_t GRID_OVERFLOW = 0xFFFF;
-constexpr double GRID_MARGIN = 1e-4;     // box widening: rotation error + float32 cell arithmetic
-constexpr double GRID_R = 0.5;           // the grid covers [-R, R]^dims
-constexpr double GRID_REACH = 0.3;       // distance searched when building a cell's list
-
-struct GridTable {
-  int dims = 0, G = 0, re = 0;
-  double R = 0.0;
-  int max_len = 0, overflow = 0;
-  std::vector<uint16_t> rec;             // [G^dims][re]
-};
-
-// Candidate lists of the first `dims` coordinates of the N x k codebook `cw`
-// over a G^dims grid on [-R, R]^dims, records of `re` entries, unused slots
-// set to `pad`.
-void build_grid(const float* cw, int N, int k, int dims, int G, double R, int re, uint16_t pad,
-                GridTable* out);
-
 }  // namespace fq
 
 struct fq_codebook {
@@ -88,6 +43,7 @@ struct fq_codebook {
   int enc_stride;
   double rate_nominal, rate_actual, distortion;
   uint64_t hash;
+  uint64_t pi_digest;   // FNV-1a 64 of Pi's float64 bytes: keys and values must share Pi
   float enc_ez16;   // encode: bound on |z~ - z| per coordinate, binary16 input
   float enc_ez32;   // the same for float32 input
   int grid_G;       // cells per dimension of the block grid (0: no grid, full scan)
@@ -177,6 +133,25 @@ inline int64_t resident_blocks(const void* kern, int threads, size_t shm) {
     return 0;
   return (int64_t)cus * (per_cu < 1 ? 1 : per_cu);
 }
+
+// resident_blocks of one kernel per device, computed on first use.  Safe to
+// share between host threads: each slot is an atomic, and two threads that
+// race on an empty slot both store the same value.
+struct DeviceCache {
+  static constexpr int MAX_DEVICES = 64;
+  std::atomic<int64_t> slot[MAX_DEVICES] = {};
+  int64_t get(const void* kern, int threads, size_t shm) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES)
+      return resident_blocks(kern, threads, shm);
+    int64_t v = slot[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+      v = resident_blocks(kern, threads, shm);
+      slot[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+  }
+};
 
 // Binary16 helpers usable on host and device.
 __host__ __device__ inline uint16_t f32_to_f16_bits(float f) {

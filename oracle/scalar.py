@@ -52,9 +52,3 @@ def scalar_lloyd_max(d, bits, max_iter=2000, tol=1e-14):
         mse += m2 - 2.0 * c[i] * m1 + c[i] * c[i] * m0
     return c, d * mse
 
-
-def quantise_scalar(x, c):
-    """Nearest-centroid index per coordinate (the midpoint rule), lowest index on ties."""
-    x = np.asarray(x, dtype=np.float64)
-    d2 = (x[..., None] - c) ** 2
-    return np.argmin(d2, axis=-1)
