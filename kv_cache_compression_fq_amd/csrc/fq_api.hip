@@ -411,21 +411,33 @@ fq_status fq_attend_workspace_size(const fq_codebook* cb_k, int B, int Hq, int H
   return FQ_OK;
 }
 
+// Arguments shared by fq_attend_decode and fq_attend_decode_static.
+static fq_status check_attend_args(const fq_codebook* cb_k, const fq_codebook* cb_v,
+                                   const uint16_t* q, const uint32_t* k_codes,
+                                   const uint16_t* k_norms, const uint32_t* v_codes,
+                                   const uint16_t* v_norms, int B, int Hq, int Hkv, int64_t T,
+                                   float scale, const uint16_t* out) {
+  fq_status st = check_attend_shape(cb_k, B, Hq, Hkv, T);
+  if (st != FQ_OK) return st;
+  if (!cb_v || cb_v->device != cb_k->device) return FQ_ERR_INVALID_ARG;
+  if (!same_variant(cb_k, cb_v)) return FQ_ERR_UNSUPPORTED;
+  if (!q || !k_codes || !k_norms || !v_codes || !v_norms || !out) return FQ_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) ||
+      !aligned(k_norms, 16) || !aligned(v_norms, 16))
+    return FQ_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return FQ_ERR_INVALID_ARG;
+  return FQ_OK;
+}
+
 fq_status fq_attend_decode(const fq_codebook* cb_k, const fq_codebook* cb_v, const uint16_t* q,
                            const uint32_t* k_codes, const uint16_t* k_norms,
                            const uint32_t* v_codes, const uint16_t* v_norms, int B, int Hq,
                            int Hkv, int64_t T, float scale, void* workspace,
                            size_t workspace_bytes, uint16_t* out, void* stream) {
-  fq_status st = check_attend_shape(cb_k, B, Hq, Hkv, T);
+  fq_status st = check_attend_args(cb_k, cb_v, q, k_codes, k_norms, v_codes, v_norms, B, Hq, Hkv,
+                                   T, scale, out);
   if (st != FQ_OK) return st;
-  if (!cb_v || cb_v->device != cb_k->device) return FQ_ERR_INVALID_ARG;
-  if (!same_variant(cb_k, cb_v)) return FQ_ERR_UNSUPPORTED;
-  if (!q || !k_codes || !k_norms || !v_codes || !v_norms || !workspace || !out)
-    return FQ_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) ||
-      !aligned(k_norms, 16) || !aligned(v_norms, 16) || !aligned(workspace, 256))
-    return FQ_ERR_INVALID_ARG;
-  if (!isfinite(scale)) return FQ_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, 256)) return FQ_ERR_INVALID_ARG;
   if (workspace_bytes < fq::attend_workspace_bytes(cb_k, B, Hq, Hkv, T))
     return FQ_ERR_INVALID_ARG;
   DeviceGuard g(cb_k->device);
