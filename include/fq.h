@@ -20,7 +20,8 @@
  *     the caller's next synchronisation, not as a return code.
  *   - Only fq_codebook_load allocates device memory.  fq_encode, fq_decode
  *     and fq_attend_decode allocate nothing; attention scratch comes from a
- *     caller-provided workspace.
+ *     caller-provided workspace, or (fq_attend_decode_static) from a static
+ *     per-device array of the library.
  *   - A codebook handle is immutable after load and may be used from several
  *     host threads and streams at once.
  *   - Vectors have d = 64 coordinates.
@@ -45,8 +46,12 @@ typedef enum {
   FQ_ERR_BAD_ARTIFACT = 2, /* malformed, truncated or corrupt artifact */
   FQ_ERR_UNSUPPORTED = 3, /* well-formed but outside what the kernels handle */
   FQ_ERR_NO_MEMORY = 4,   /* device allocation failed (load only) */
-  FQ_ERR_DEVICE = 5       /* HIP runtime error, or no usable device */
+  FQ_ERR_DEVICE = 5,      /* HIP runtime error, or no usable device */
+  FQ_ERR_SCRATCH = 6      /* shape exceeds the static scratch of fq_attend_decode_static */
 } fq_status;
+
+/* Bytes of the per-device static attention scratch of fq_attend_decode_static. */
+#define FQ_STATIC_SCRATCH_BYTES (4u << 20)
 
 typedef struct {
   int32_t d;            /* vector length (64) */
@@ -173,6 +178,29 @@ fq_status fq_attend_decode(const fq_codebook* cb_k, const fq_codebook* cb_v, con
                            const uint32_t* v_codes, const uint16_t* v_norms, int B, int Hq,
                            int Hkv, int64_t T, float scale, void* workspace,
                            size_t workspace_bytes, uint16_t* out, void* stream);
+
+/*
+ * fq_attend_decode for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same computation and kernels; the split-K partials live in a library-owned
+ * static device array of FQ_STATIC_SCRATCH_BYTES per device instead of a
+ * caller workspace.  The array is part of the library's device code (each
+ * device holds its own copy until the process ends); its address is looked up
+ * when a codebook is first loaded on the device.  This call allocates nothing.
+ *
+ *   Arguments, requirements and errors as fq_attend_decode, without the
+ *   workspace.  A shape whose fq_attend_workspace_size exceeds
+ *   FQ_STATIC_SCRATCH_BYTES returns FQ_ERR_SCRATCH (use fq_attend_decode).
+ *   Every call on one device shares that device's array: calls that overlap
+ *   in time on one device (on different streams, or from host threads with no
+ *   ordering between them) race and give undefined outputs; calls ordered on
+ *   one stream are safe.  The array needs no clearing between calls.
+ */
+fq_status fq_attend_decode_static(const fq_codebook* cb_k, const fq_codebook* cb_v,
+                                  const uint16_t* q, const uint32_t* k_codes,
+                                  const uint16_t* k_norms, const uint32_t* v_codes,
+                                  const uint16_t* v_norms, int B, int Hq, int Hkv, int64_t T,
+                                  float scale, uint16_t* out, void* stream);
 
 /*
  * Attention of several queries per head over a compressed cache: the steps on

@@ -6,11 +6,45 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "fq_internal.h"
 
+// Attention scratch of fq_attend_decode_static: split-K partials for callers
+// that cannot allocate.  One copy per device, held until the process ends.
+// Host code never uses this name as an address: the device address of each
+// device's copy is looked up once (scratch_address) and kept per device.
+static __device__ __align__(256) unsigned char scratch[FQ_STATIC_SCRATCH_BYTES];
+
 namespace {
+
+// Device address of `scratch` on each device, looked up at set-up (the first
+// codebook load on that device, with the device current); null if the lookup
+// failed.
+constexpr int SCRATCH_DEVICES = fq::DeviceCache::MAX_DEVICES;
+std::mutex scratch_mu;
+void* scratch_dev[SCRATCH_DEVICES] = {};
+bool scratch_done[SCRATCH_DEVICES] = {};
+
+// Must run with `device` current.
+void scratch_setup(int device) {
+  if (device < 0 || device >= SCRATCH_DEVICES) return;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_done[device]) return;
+  scratch_done[device] = true;
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess && p != nullptr)
+    scratch_dev[device] = p;
+  else
+    (void)hipGetLastError();
+}
+
+void* scratch_address(int device) {
+  if (device < 0 || device >= SCRATCH_DEVICES) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  return scratch_dev[device];
+}
 
 void fill_info(const fq::ArtifactHeader& h, fq_info* o) {
   o->d = h.d;
@@ -63,6 +97,7 @@ const char* fq_status_string(fq_status s) {
     case FQ_ERR_UNSUPPORTED: return "unsupported codebook or shape";
     case FQ_ERR_NO_MEMORY: return "device allocation failed";
     case FQ_ERR_DEVICE: return "HIP device error";
+    case FQ_ERR_SCRATCH: return "shape needs more than the library's static attention scratch";
   }
   return "unknown status";
 }
@@ -270,6 +305,7 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
       delete cb;
       return FQ_ERR_DEVICE;
     }
+    scratch_setup(device);
     if (hipMalloc(&cb->dev_block, off) != hipSuccess) {
       (void)hipGetLastError();
       delete cb;
@@ -445,6 +481,26 @@ fq_status fq_attend_decode(const fq_codebook* cb_k, const fq_codebook* cb_v, con
   (void)hipGetLastError();
   hipError_t e = fq::launch_attend(cb_k, cb_v, q, k_codes, k_norms, v_codes, v_norms, B, Hq, Hkv,
                                    T, T, 1, scale, workspace, out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FQ_OK : FQ_ERR_DEVICE;
+}
+
+fq_status fq_attend_decode_static(const fq_codebook* cb_k, const fq_codebook* cb_v,
+                                  const uint16_t* q, const uint32_t* k_codes,
+                                  const uint16_t* k_norms, const uint32_t* v_codes,
+                                  const uint16_t* v_norms, int B, int Hq, int Hkv, int64_t T,
+                                  float scale, uint16_t* out, void* stream) {
+  fq_status st = check_attend_args(cb_k, cb_v, q, k_codes, k_norms, v_codes, v_norms, B, Hq, Hkv,
+                                   T, scale, out);
+  if (st != FQ_OK) return st;
+  if (fq::attend_workspace_bytes(cb_k, B, Hq, Hkv, T) > FQ_STATIC_SCRATCH_BYTES)
+    return FQ_ERR_SCRATCH;
+  void* ws = scratch_address(cb_k->device);   // set up when cb_k was loaded
+  if (!ws) return FQ_ERR_DEVICE;
+  DeviceGuard g(cb_k->device);
+  if (g.err != hipSuccess) return FQ_ERR_DEVICE;
+  (void)hipGetLastError();
+  hipError_t e = fq::launch_attend(cb_k, cb_v, q, k_codes, k_norms, v_codes, v_norms, B, Hq, Hkv,
+                                   T, T, 1, scale, ws, out, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FQ_OK : FQ_ERR_DEVICE;
 }
 

@@ -15,11 +15,13 @@ CODEBOOK_DIR = os.path.join(PKG, "codebooks")
 
 FQ_F16, FQ_F32 = 1, 2
 FQ_OK, FQ_ERR_INVALID_ARG, FQ_ERR_BAD_ARTIFACT, FQ_ERR_UNSUPPORTED, FQ_ERR_NO_MEMORY, \
-    FQ_ERR_DEVICE = range(6)
+    FQ_ERR_DEVICE, FQ_ERR_SCRATCH = range(7)
+FQ_STATIC_SCRATCH_BYTES = 4 << 20
 
 EXPORTS = ["fq_status_string", "fq_artifact_check", "fq_codebook_load", "fq_codebook_info",
            "fq_codebook_free", "fq_encode", "fq_decode", "fq_attend_workspace_size",
-           "fq_attend_decode", "fq_attend_queries", "fq_decode_step"]
+           "fq_attend_decode", "fq_attend_decode_static", "fq_attend_queries",
+           "fq_decode_step"]
 
 
 class FQError(RuntimeError):
@@ -68,6 +70,9 @@ def library(path=LIB_PATH):
     lib.fq_attend_decode.argtypes = [_P, _P, _P, _P, _P, _P, _P, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int, _I64, ctypes.c_float, _P, ctypes.c_size_t, _P,
                                      _P]
+    lib.fq_attend_decode_static.argtypes = [_P, _P, _P, _P, _P, _P, _P, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_int, _I64, ctypes.c_float,
+                                            _P, _P]
     lib.fq_attend_queries.argtypes = [_P, _P, _P, _P, _P, _P, _P, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_int, _I64, _I64, ctypes.c_int, ctypes.c_float, _P,
                                       ctypes.c_size_t, _P, _P]
@@ -248,6 +253,29 @@ def fq_attend_decode(cb_k, cb_v, q, k_codes, k_norms, v_codes, v_norms, scale, w
                                       _ptr(k_norms), _ptr(v_codes), _ptr(v_norms), B, Hq, Hkv, T,
                                       float(scale), _ptr(workspace), workspace.numel(), _ptr(out),
                                       _stream(stream, q.device)), "fq_attend_decode")
+    return out
+
+
+def fq_attend_decode_static(cb_k, cb_v, q, k_codes, k_norms, v_codes, v_norms, scale, out=None,
+                            stream=None):
+    """fq_attend_decode with the library's static per-device scratch (no workspace;
+    for callers that cannot allocate; calls overlapping on one device race)."""
+    import torch
+    B, Hq, d = q.shape
+    Hkv, T = k_codes.shape[1], k_codes.shape[2]
+    for t in (q, k_codes, k_norms, v_codes, v_norms):
+        if not t.is_contiguous():
+            raise ValueError("attention inputs must be contiguous")
+    if k_codes.shape != (B, Hkv, T, cb_k.W) or v_codes.shape != (B, Hkv, T, cb_v.W):
+        raise ValueError("cache code shapes do not match the codebooks")
+    if k_norms.shape != (B, Hkv, T) or v_norms.shape != (B, Hkv, T):
+        raise ValueError("norm shapes must be [B, Hkv, T]")
+    if out is None:
+        out = torch.empty((B, Hq, 64), dtype=torch.float16, device=q.device)
+    _check(library().fq_attend_decode_static(cb_k.handle, cb_v.handle, _ptr(q), _ptr(k_codes),
+                                             _ptr(k_norms), _ptr(v_codes), _ptr(v_norms), B, Hq,
+                                             Hkv, T, float(scale), _ptr(out),
+                                             _stream(stream, q.device)), "fq_attend_decode_static")
     return out
 
 

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for s in range(6):
+    for s in range(7):
         assert fq.fq_status_string(s)
     assert fq.fq_status_string(99) == "unknown status"
 
@@ -107,6 +107,8 @@ def test_null_arguments_rejected_without_device():
     assert lib.fq_attend_workspace_size(None, 1, 1, 1, 1, ctypes.byref(sz)) == INV
     assert lib.fq_attend_decode(None, None, None, None, None, None, None, 1, 1, 1, 1,
                                 ctypes.c_float(1.0), None, 0, None, None) == INV
+    assert lib.fq_attend_decode_static(None, None, None, None, None, None, None, 1, 1, 1, 1,
+                                       ctypes.c_float(1.0), None, None) == INV
 
 
 def test_load_without_device_reports_device_error():
