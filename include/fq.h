@@ -99,6 +99,20 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
 /* Describe a loaded codebook. */
 fq_status fq_codebook_info(const fq_codebook* cb, fq_info* out);
 
+/*
+ * Work model of the encoder's block search, for reporting its compute
+ * roofline (host only; reads host memory; no device work).  For n vectors of
+ * x (host memory, layout as fq_encode), counts the codewords the search
+ * compares each block with: the entries of the block's candidate list where
+ * the codebook has lists and the block's cell carries one, else all N (a
+ * full scan, as for codebooks without lists).  *entries_per_vector receives
+ * the mean over the vectors of the sum over their blocks; *full_scan_share
+ * (may be NULL) the share of blocks searched over all N.  Each entry costs
+ * about k + 2 vector operations (k fused multiply-adds, a compare, a select).
+ */
+fq_status fq_search_cost(const fq_codebook* cb, const void* x, fq_dtype x_dtype, int64_t n,
+                         int64_t x_ld, double* entries_per_vector, double* full_scan_share);
+
 /* Release a codebook.  The caller guarantees no queued work still uses it.  NULL is a no-op. */
 void fq_codebook_free(fq_codebook* cb);
 

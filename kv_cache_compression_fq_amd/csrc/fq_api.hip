@@ -349,6 +349,8 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
     if (!grid.rec.empty()) memcpy(staging.data() + o_grid, grid.rec.data(), 2ull * grid.rec.size());
     if (!grid1.rec.empty())
       memcpy(staging.data() + o_grid1, grid1.rec.data(), 2ull * grid1.rec.size());
+    cb->grid_host = std::move(grid.rec);
+    cb->grid1_host = std::move(grid1.rec);
     if (hipMemcpy(cb->dev_block, staging.data(), off, hipMemcpyHostToDevice) != hipSuccess) {
       (void)hipGetLastError();
       (void)hipFree(cb->dev_block);
@@ -374,6 +376,63 @@ fq_status fq_codebook_info(const fq_codebook* cb, fq_info* out) {
   out->rate_actual = cb->rate_actual;
   out->distortion = cb->distortion;
   out->artifact_hash = cb->hash;
+  return FQ_OK;
+}
+
+fq_status fq_search_cost(const fq_codebook* cb, const void* x, fq_dtype x_dtype, int64_t n,
+                         int64_t x_ld, double* entries_per_vector, double* full_scan_share) {
+  if (!cb || !x || n < 1 || x_ld < fq::D || !entries_per_vector) return FQ_ERR_INVALID_ARG;
+  if (x_dtype != FQ_F16 && x_dtype != FQ_F32) return FQ_ERR_INVALID_ARG;
+  const int k = cb->k, N = cb->N, nb = cb->nb, last = cb->last;
+  const bool grid = cb->grid_G > 0 && !cb->grid_host.empty();
+  const int re = fq::grid_record_entries(k);
+  const float sc = grid ? fq::grid_scale(cb->grid_G) : 0.f;
+  const float sc1 = cb->grid1_G > 0 ? fq::grid_scale(cb->grid1_G) : 0.f;
+  double entries = 0.0, scans = 0.0;
+  double xv[fq::D], z[fq::D];
+  for (int64_t r = 0; r < n; ++r) {
+    double ss = 0.0;
+    for (int i = 0; i < fq::D; ++i) {
+      if (x_dtype == FQ_F16) {
+        _Float16 h;
+        memcpy(&h, static_cast<const unsigned char*>(x) + 2 * (r * x_ld + i), 2);
+        xv[i] = (double)h;
+      } else {
+        float f;
+        memcpy(&f, static_cast<const unsigned char*>(x) + 4 * (r * x_ld + i), 4);
+        xv[i] = (double)f;
+      }
+      ss += xv[i] * xv[i];
+    }
+    const double nu = sqrt(ss);
+    for (int i = 0; i < fq::D; ++i) {
+      double t = 0.0;
+      for (int j = 0; j < fq::D; ++j) t += cb->pi[(size_t)i * fq::D + j] * xv[j];
+      z[i] = nu > 0.0 ? t / nu : NAN;
+    }
+    for (int j = 0; j < nb; ++j) {
+      const bool part = j == nb - 1 && last < k;
+      const int dims = part ? 1 : k;
+      int cnt = 0;
+      if (grid && (!part || cb->grid1_G > 0)) {
+        const int G = part ? cb->grid1_G : cb->grid_G;
+        bool inside = true;
+        int cell = 0, mul = 1;
+        for (int t = 0; t < dims; ++t) {
+          const float zf = (float)z[j * k + t];
+          inside = inside && fq::grid_inside(zf);
+          cell += fq::grid_axis(zf, G, part ? sc1 : sc) * mul;
+          mul *= G;
+        }
+        const uint16_t c0 = (part ? cb->grid1_host : cb->grid_host)[(size_t)cell * re];
+        if (inside && c0 != fq::GRID_OVERFLOW) cnt = c0;
+      }
+      entries += cnt > 0 ? cnt : N;
+      scans += cnt > 0 ? 0.0 : 1.0;
+    }
+  }
+  *entries_per_vector = entries / (double)n;
+  if (full_scan_share) *full_scan_share = scans / ((double)n * nb);
   return FQ_OK;
 }
 

@@ -51,6 +51,7 @@ struct fq_codebook {
   bool half_exact;  // every codeword coordinate is a binary16 number
   double cmax;      // largest codeword norm
   double hshift;    // constant added to every score of the matrix-core k = 8 search
+  std::vector<uint16_t> grid_host, grid1_host;   // host copies of the candidate grids
   std::vector<double> pi;  // host copy of Pi
   std::vector<float> c;    // host copy of C
   void* dev_block;         // the single device allocation

@@ -19,7 +19,7 @@ FQ_OK, FQ_ERR_INVALID_ARG, FQ_ERR_BAD_ARTIFACT, FQ_ERR_UNSUPPORTED, FQ_ERR_NO_ME
 FQ_STATIC_SCRATCH_BYTES = 4 << 20
 
 EXPORTS = ["fq_status_string", "fq_artifact_check", "fq_codebook_load", "fq_codebook_info",
-           "fq_codebook_free", "fq_encode", "fq_decode", "fq_attend_workspace_size",
+           "fq_search_cost", "fq_codebook_free", "fq_encode", "fq_decode", "fq_attend_workspace_size",
            "fq_attend_decode", "fq_attend_decode_static", "fq_attend_queries",
            "fq_decode_step"]
 
@@ -61,6 +61,8 @@ def library(path=LIB_PATH):
     lib.fq_artifact_check.argtypes = [_P, ctypes.c_size_t, ctypes.POINTER(fq_info)]
     lib.fq_codebook_load.argtypes = [_P, ctypes.c_size_t, ctypes.c_int, ctypes.POINTER(_P)]
     lib.fq_codebook_info.argtypes = [_P, ctypes.POINTER(fq_info)]
+    lib.fq_search_cost.argtypes = [_P, _P, ctypes.c_int, _I64, _I64,
+                                   ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
     lib.fq_codebook_free.argtypes = [_P]
     lib.fq_codebook_free.restype = None
     lib.fq_encode.argtypes = [_P, _P, ctypes.c_int, _I64, _I64, _P, _P, _P]
@@ -172,6 +174,21 @@ def fq_codebook_load(blob, device=0):
 
 def load_codebook(k, N, device=0):
     return fq_codebook_load(read_codebook_bytes(k, N), device)
+
+
+def fq_search_cost(cb, x_host):
+    """Search work model for host vectors x_host (numpy [n, >=64] float16 or
+    float32): (codewords compared per vector, share of blocks scanning all N)."""
+    import numpy as np
+    x_host = np.ascontiguousarray(x_host)
+    dt = FQ_F16 if x_host.dtype == np.float16 else FQ_F32
+    if x_host.dtype not in (np.float16, np.float32) or x_host.ndim != 2:
+        raise ValueError("x_host must be a 2-D float16 or float32 array")
+    e, f = ctypes.c_double(), ctypes.c_double()
+    _check(library().fq_search_cost(cb.handle, x_host.ctypes.data_as(_P), dt, x_host.shape[0],
+                                    x_host.shape[1], ctypes.byref(e), ctypes.byref(f)),
+           "fq_search_cost")
+    return e.value, f.value
 
 
 def fq_codebook_free(cb):

@@ -46,8 +46,15 @@ def library():
         lib.fqo_accept.argtypes = [P, I64, ctypes.c_int, P, P, ctypes.c_int, ctypes.c_int, P,
                                    ctypes.c_double, P, P]
         lib.fqo_accept.restype = ctypes.c_int
+        lib.fqo_threads.argtypes = [ctypes.c_int]
+        lib.fqo_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
+
+
+def threads(n=0):
+    """Set the OpenMP thread count of the searches (n >= 1); return the count in use."""
+    return int(library().fqo_threads(int(n)))
 
 
 def _p(a):

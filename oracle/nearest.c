@@ -23,8 +23,15 @@
  * evaluated.  Vectors are independent, so they are split over OpenMP threads.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
+
+/* Threads the searches below use (OpenMP); n < 1 leaves the setting alone. */
+int fqo_threads(int n) {
+  if (n >= 1) omp_set_num_threads(n);
+  return omp_get_max_threads();
+}
 
 /* z = Pi u with u = x / nu, of one vector (u is scratch of d doubles); returns nu. */
 static double rotate_unit(const double* x, int d, const double* Pi, double* u, double* z) {

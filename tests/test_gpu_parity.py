@@ -155,6 +155,23 @@ def test_encode_strided_rows_and_empty(dev, k, N):
     fq.fq_encode(cb, e)                        # n == 0: no-op
 
 
+def test_search_cost_model(dev):
+    """fq_search_cost: full scans count N per block, zero vectors scan every
+    block, and candidate lists count between 1 and the list capacity per block."""
+    x = synth.kv_slab(2, 0, 0, 1, 2, 500).reshape(-1, 64)
+    _, c4 = book(4, 4)
+    e, f = fq.fq_search_cost(c4, x)
+    assert e == 16 * 4 and f == 1.0
+    _, c2 = book(2, 16)
+    e, f = fq.fq_search_cost(c2, x)
+    assert 32 <= e < 32 * 8 and f < 0.05
+    e0, f0 = fq.fq_search_cost(c2, np.zeros((3, 64), dtype=np.float16))
+    assert e0 == 32 * 16 and f0 == 1.0
+    _, c3 = book(3, 4096)
+    e, f = fq.fq_search_cost(c3, x.astype(np.float32))
+    assert 22 <= e < 22 * 16
+
+
 def test_encode_rejects_misaligned(dev):
     art, cb = book(2, 16)
     x = torch.zeros((10, 72), dtype=torch.float16, device=dev)
