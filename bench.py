@@ -573,7 +573,8 @@ def fidelity(torch, fq, synth, dev, B=2, Hq=32, Hkv=4, T=4096, layers=(0, 11, 21
                 cos[name].append(torch.nn.functional.cosine_similarity(
                     o.float(), o_ref, dim=-1).flatten())
         row = {"variant": f"k{k}N{N}", "bits_per_coord": math.log2(N) / k,
-               "compression": 128.0 / (4 * cb.W + 2)}
+               "compression": 128.0 / (4 * cb.W + 2),
+               "compression_packed": 1024.0 / cb.packed_bits}
         for name, lst in cos.items():
             c = torch.cat(lst)
             row[f"{name}_cos_mean"] = float(c.mean())
@@ -614,6 +615,16 @@ def bench_large(torch, fq, synth, dev, steps, warmup):
         timer.collect()
         te = float(np.median(timer.ms["encode"])) * 1e-3
         td = float(np.median(timer.ms["decode"])) * 1e-3
+        packed = torch.empty((cb.packed_words(n),), dtype=torch.int32, device=x.device)
+        fq.fq_pack_records(cb, codes, norms, packed=packed)
+        tp = Timer(torch)
+        for i in range(warmup + steps):
+            if i == warmup:
+                tp.reset()
+            tp.run("decode_packed", lambda: fq.fq_decode_packed(cb, packed, n, y=y))
+        tp.collect()
+        tdp = float(np.median(tp.ms["decode_packed"])) * 1e-3
+        pk_bytes = n * (cb.packed_bits / 8 + 128)
         flops = 2.0 * 64 * N * n                  # one multiply-add per codeword coordinate
         dec_bytes = n * codec_bytes(k, N)
         out[f"k{k}N{N}"] = {
@@ -622,8 +633,11 @@ def bench_large(torch, fq, synth, dev, steps, warmup):
             "encode_mfma_tflops": flops / te / 1e12,
             "encode_mfma_frac": flops / te / 1e12 / MFMA_F16_PEAK_TFLOPS,
             "decode_ms": td * 1e3, "decode_gbs": dec_bytes / td / 1e9,
-            "decode_hbm_frac": dec_bytes / td / 1e9 / HBM_PEAK_GBS}
-        del codes, norms
+            "decode_hbm_frac": dec_bytes / td / 1e9 / HBM_PEAK_GBS,
+            "packed_bits_per_vector": cb.packed_bits, "packed_compression": 1024.0 / cb.packed_bits,
+            "decode_packed_ms": tdp * 1e3, "decode_packed_gbs": pk_bytes / tdp / 1e9,
+            "decode_packed_hbm_frac": pk_bytes / tdp / 1e9 / HBM_PEAK_GBS}
+        del codes, norms, packed
     log("large-block timing done")
     return {"workload": f"gpt2-small-kv-cache, {n} vectors, fp16; median of {steps} launches",
             "peak_mfma_f16_tflops": MFMA_F16_PEAK_TFLOPS, "codes": out}

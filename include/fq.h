@@ -61,7 +61,7 @@ typedef struct {
   int32_t idx_bits;     /* bits per index, log2 N */
   int32_t record_words; /* uint32 words per record, ceil(nb * idx_bits / 32) */
   int32_t last_block;   /* real coordinates in the last block */
-  int32_t reserved;
+  int32_t packed_bits;  /* bits per packed record (fq_pack_records): nb * idx_bits + 16 */
   double rate_nominal;  /* log2(N) / k bits per coordinate [FQ 2.3] */
   double rate_actual;   /* nb * idx_bits / d */
   double distortion;    /* test distortion per unit vector recorded in the artifact */
@@ -157,6 +157,39 @@ fq_status fq_encode(const fq_codebook* cb, const void* x, fq_dtype x_dtype, int6
 fq_status fq_decode(const fq_codebook* cb, const uint32_t* codes, const uint16_t* norms,
                     const int64_t* rows, int64_t n_records, int64_t n, void* y,
                     fq_dtype y_dtype, int64_t y_ld, void* stream);
+
+/*
+ * Packed records: the fixed-rate indices and the binary16 norm of a vector in
+ * one bit stream, without rounding records up to whole words, so that the
+ * stored size is the code's own rate plus the norm [FQ 1: fixed-rate records
+ * at fixed addresses; the norm is stored with the code, 2.3].  Record r
+ * occupies bits [r R, (r + 1) R) of `packed` (uint32 words, bits counted from
+ * the least significant bit of little-endian words), R = packed_bits =
+ * nb * idx_bits + 16: field j at record bits [j idx_bits, (j+1) idx_bits),
+ * then the norm's 16 bits.  n records take ceil(n R / 32) words; bits past
+ * the last record are 0.  Any record still decodes by address arithmetic
+ * alone (bit offset r R).  For k = 64, N = 4096, R = 28 bits: 1024 / 28 =
+ * 36.6 times smaller than the binary16 vector (the word-aligned layout plus
+ * the separate norm stores 48 bits, 21.3 times).
+ *
+ * fq_pack_records converts n word-aligned records and their norms (the
+ * layout of fq_encode) into the packed stream.  codes 4-byte, norms 2-byte,
+ * packed 4-byte aligned; n == 0 is a no-op.
+ */
+fq_status fq_pack_records(const fq_codebook* cb, const uint32_t* codes, const uint16_t* norms,
+                          int64_t n, uint32_t* packed, void* stream);
+
+/*
+ * fq_decode reading packed records (see fq_pack_records): row i decodes
+ * record i (rows NULL; n records in `packed`) or record rows[i] of the
+ * n_records in `packed` (an address outside [0, n_records) decodes to a zero
+ * row; with rows, the stream may span at most 2^31 - 1 bytes, else
+ * FQ_ERR_UNSUPPORTED).  packed 4-byte aligned; y, rows, y_dtype and y_ld as
+ * fq_decode.
+ */
+fq_status fq_decode_packed(const fq_codebook* cb, const uint32_t* packed, const int64_t* rows,
+                           int64_t n_records, int64_t n, void* y, fq_dtype y_dtype, int64_t y_ld,
+                           void* stream);
 
 /*
  * Bytes of device workspace fq_attend_decode needs for this shape.

@@ -54,7 +54,7 @@ void fill_info(const fq::ArtifactHeader& h, fq_info* o) {
   o->idx_bits = h.bits;
   o->record_words = h.W;
   o->last_block = h.last;
-  o->reserved = 0;
+  o->packed_bits = (int32_t)(h.nb * h.bits + 16);
   o->rate_nominal = (double)h.bits / h.k;
   o->rate_actual = (double)h.nb * h.bits / h.d;
   o->distortion = h.d_test;
@@ -371,7 +371,7 @@ fq_status fq_codebook_info(const fq_codebook* cb, fq_info* out) {
   out->idx_bits = cb->bits;
   out->record_words = cb->W;
   out->last_block = cb->last;
-  out->reserved = 0;
+  out->packed_bits = fq::packed_record_bits(cb);
   out->rate_nominal = cb->rate_nominal;
   out->rate_actual = cb->rate_actual;
   out->distortion = cb->distortion;
@@ -485,6 +485,45 @@ fq_status fq_decode(const fq_codebook* cb, const uint32_t* codes, const uint16_t
   (void)hipGetLastError();
   hipError_t e = fq::launch_decode(cb, codes, norms, rows, rows ? n_records : n, n, y, y_dtype,
                                    y_ld, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FQ_OK : FQ_ERR_DEVICE;
+}
+
+fq_status fq_pack_records(const fq_codebook* cb, const uint32_t* codes, const uint16_t* norms,
+                          int64_t n, uint32_t* packed, void* stream) {
+  if (!cb || n < 0) return FQ_ERR_INVALID_ARG;
+  if (n == 0) return FQ_OK;
+  if (!codes || !norms || !packed || !aligned(codes, 4) || !aligned(norms, 2) ||
+      !aligned(packed, 4))
+    return FQ_ERR_INVALID_ARG;
+  if (n > (int64_t(1) << 40)) return FQ_ERR_INVALID_ARG;
+  DeviceGuard g(cb->device);
+  if (g.err != hipSuccess) return FQ_ERR_DEVICE;
+  (void)hipGetLastError();
+  hipError_t e = fq::launch_pack(cb, codes, norms, n, packed, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FQ_OK : FQ_ERR_DEVICE;
+}
+
+fq_status fq_decode_packed(const fq_codebook* cb, const uint32_t* packed, const int64_t* rows,
+                           int64_t n_records, int64_t n, void* y, fq_dtype y_dtype, int64_t y_ld,
+                           void* stream) {
+  if (!cb || n < 0) return FQ_ERR_INVALID_ARG;
+  if (y_dtype != FQ_F16 && y_dtype != FQ_F32) return FQ_ERR_INVALID_ARG;
+  if (n == 0) return FQ_OK;
+  const int esz = y_dtype == FQ_F16 ? 2 : 4;
+  if (!packed || !y || y_ld < fq::D || (y_ld * esz) % 16 != 0 || !aligned(y, 16) ||
+      !aligned(packed, 4))
+    return FQ_ERR_INVALID_ARG;
+  if (rows && (!aligned(rows, 8) || n_records < 0)) return FQ_ERR_INVALID_ARG;
+  if (y_ld > (int64_t(1) << 22)) return FQ_ERR_UNSUPPORTED;
+  // gathered records are addressed with 32-bit buffer offsets over the whole stream
+  if (rows && (n_records * fq::packed_record_bits(cb) + 31) / 32 * 4 > (int64_t(1) << 31) - 1)
+    return FQ_ERR_UNSUPPORTED;
+  if (n > (int64_t(1) << 40)) return FQ_ERR_INVALID_ARG;
+  DeviceGuard g(cb->device);
+  if (g.err != hipSuccess) return FQ_ERR_DEVICE;
+  (void)hipGetLastError();
+  hipError_t e = fq::launch_decode(cb, packed, nullptr, rows, rows ? n_records : n, n, y, y_dtype,
+                                   y_ld, static_cast<hipStream_t>(stream), true);
   return e == hipSuccess ? FQ_OK : FQ_ERR_DEVICE;
 }
 

@@ -81,6 +81,85 @@ __device__ inline void load_chunk_gather(ChunkRegs<W>& t, int64_t chunk, int lan
   t.nu_bits = __builtin_amdgcn_raw_buffer_load_b16(rn, offn, 0, 0);
 }
 
+// Packed records (fq_pack_records): record r at bits [r R, r R + R) of one
+// word stream, R = F + 16 with F = NB BITS field bits, then the binary16 norm.
+template <int K, int BITS>
+struct PackedShape {
+  static constexpr int F = Shape<K, BITS>::NB * BITS;   // field bits
+  static constexpr int R = F + 16;                      // record bits
+  static constexpr int NWR = (R + 31 + 31) / 32;        // stream words one record can touch
+};
+
+// Re-align a record from the stream words wd (the first holding its bit sh)
+// into the word-aligned layout: fields in t.w (bits past F zero), norm in t.nu_bits.
+template <int K, int BITS, int W>
+__device__ inline void realign(const uint32_t (&wd)[PackedShape<K, BITS>::NWR + 1], uint32_t sh,
+                               ChunkRegs<W>& t) {
+  using P = PackedShape<K, BITS>;
+  constexpr int NS = (P::F + 15) / 32 + 1;   // record-string words holding fields and norm
+  uint32_t rs[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) rs[i] = __builtin_amdgcn_alignbit(wd[i + 1], wd[i], sh);
+#pragma unroll
+  for (int i = 0; i < W; ++i) t.w[i] = rs[i];
+  constexpr int TOP = P::F - 32 * (W - 1);   // field bits in the last word
+  if constexpr (TOP < 32) t.w[W - 1] &= (1u << TOP) - 1u;
+  constexpr int NW0 = P::F >> 5, NSH = P::F & 31;
+  if constexpr (NSH <= 16)
+    t.nu_bits = (rs[NW0] >> NSH) & 0xFFFFu;
+  else
+    t.nu_bits = __builtin_amdgcn_alignbit(rs[NW0 + 1], rs[NW0], NSH) & 0xFFFFu;
+}
+
+// Record `chunk * CHUNK + lane` of a packed stream of n records.
+template <int K, int BITS, int W>
+__device__ inline void load_chunk_packed(ChunkRegs<W>& t, int64_t chunk, int lane,
+                                         const uint32_t* packed, int64_t n) {
+  using P = PackedShape<K, BITS>;
+  const int64_t base = chunk * CHUNK;
+  const int64_t left = n - base;
+  const int cnt = left <= 0 ? 0 : (left < CHUNK ? (int)left : CHUNK);
+  const int64_t bit0 = base * P::R;
+  const int64_t word0 = bit0 >> 5;
+  const int64_t words_total = (n * P::R + 31) >> 5;
+  // the chunk's words: those of its cnt records (none past the stream's end)
+  const int64_t span = cnt == 0 ? 0 : (((bit0 & 31) + (int64_t)cnt * P::R + 31) >> 5);
+  const int64_t have = words_total - word0 < span ? words_total - word0 : span;
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(packed + word0), (short)0, (int)(have > 0 ? have * 4 : 0), BUF_DWORD3);
+  const uint32_t bit = (uint32_t)(bit0 & 31) + (uint32_t)lane * P::R;
+  uint32_t wd[P::NWR + 1];
+#pragma unroll
+  for (int i = 0; i < P::NWR; ++i)
+    wd[i] = __builtin_amdgcn_raw_buffer_load_b32(rc, ((bit >> 5) + i) * 4, 0, 0);
+  wd[P::NWR] = 0u;
+  realign<K, BITS, W>(wd, bit & 31, t);
+}
+
+// Packed record rows[r] (at most 2^31 - 1 bytes of stream, checked on the
+// host); an invalid address reads 0 and decodes to 0.
+template <int K, int BITS, int W>
+__device__ inline void load_chunk_packed_gather(ChunkRegs<W>& t, int64_t chunk, int lane,
+                                                const uint32_t* packed, const int64_t* rows,
+                                                int64_t n_records, int64_t n) {
+  using P = PackedShape<K, BITS>;
+  const int64_t r = chunk * CHUNK + lane;
+  const int64_t rr = r < n ? r : n - 1;
+  const int64_t rec = rows[rr];
+  const bool ok = r < n && rec >= 0 && rec < n_records;
+  const int64_t words_total = (n_records * P::R + 31) >> 5;
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(packed), (short)0, (int)(words_total * 4), BUF_DWORD3);
+  const int64_t bit = ok ? rec * P::R : 0;
+  const uint32_t w0 = ok ? (uint32_t)(bit >> 5) : 0x20000000u;   // past the range: reads 0
+  uint32_t wd[P::NWR + 1];
+#pragma unroll
+  for (int i = 0; i < P::NWR; ++i)
+    wd[i] = __builtin_amdgcn_raw_buffer_load_b32(rc, (w0 + i) * 4, 0, 0);
+  wd[P::NWR] = 0u;
+  realign<K, BITS, W>(wd, (uint32_t)(bit & 31), t);
+}
+
 // Coordinates [c0, c0 + 8) of z_hat (binary16) for one staged vector.
 template <int K>
 __device__ inline half8 gather8(const uint16_t* idx, const _Float16* cbh, int c0) {
@@ -115,7 +194,7 @@ __device__ inline half8 gather8(const uint16_t* idx, const _Float16* cbh, int c0
   }
 }
 
-template <int K, int BITS, typename TY, bool GATHER>
+template <int K, int BITS, typename TY, bool GATHER, bool PACKED>
 __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
     const uint32_t* __restrict__ codes, const uint16_t* __restrict__ norms,
     const int64_t* __restrict__ rows, int64_t n_records, int64_t n, TY* __restrict__ y,
@@ -164,7 +243,11 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
   // a chunk index past the end gives an empty descriptor: its loads read 0
   auto load = [&](ChunkRegs<W>& t, int64_t c) {
     c = c < n_chunks ? c : n_chunks;
-    if constexpr (GATHER)
+    if constexpr (PACKED && GATHER)
+      load_chunk_packed_gather<K, BITS, W>(t, c, lane, codes, rows, n_records, n);
+    else if constexpr (PACKED)
+      load_chunk_packed<K, BITS, W>(t, c, lane, codes, n);
+    else if constexpr (GATHER)
       load_chunk_gather<W>(t, c, lane, codes, norms, rows, n_records, n);
     else
       load_chunk<W>(t, c, lane, codes, norms, n);
@@ -260,13 +343,13 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
   }
 }
 
-template <int K, int BITS, typename TY, bool GATHER>
+template <int K, int BITS, typename TY, bool GATHER, bool PACKED>
 hipError_t launch_k(const fq_codebook* cb, const uint32_t* codes, const uint16_t* norms,
                     const int64_t* rows, int64_t n_records, int64_t n, TY* y, int64_t ld,
                     hipStream_t s) {
   const size_t cb_bytes = large_block(K) ? 0 : ((size_t)cb->N * K * sizeof(_Float16) + 15) / 16 * 16;
   const size_t shm = cb_bytes + DEC_WAVES * wave_lds<K, BITS, TY>();
-  auto kern = decode_kernel<K, BITS, TY, GATHER>;
+  auto kern = decode_kernel<K, BITS, TY, GATHER, PACKED>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
@@ -283,13 +366,13 @@ hipError_t launch_k(const fq_codebook* cb, const uint32_t* codes, const uint16_t
   return hipGetLastError();
 }
 
-template <typename TY, bool GATHER>
+template <typename TY, bool GATHER, bool PACKED>
 hipError_t dispatch(const fq_codebook* cb, const uint32_t* codes, const uint16_t* norms,
                     const int64_t* rows, int64_t n_records, int64_t n, TY* y, int64_t ld,
                     hipStream_t s) {
 #define FQ_DEC(KK, BB)                                                                     \
   if (cb->k == KK && cb->bits == BB)                                                       \
-    return launch_k<KK, BB, TY, GATHER>(cb, codes, norms, rows, n_records, n, y, ld, s);
+    return launch_k<KK, BB, TY, GATHER, PACKED>(cb, codes, norms, rows, n_records, n, y, ld, s);
   FQ_VARIANTS(FQ_DEC)
   FQ_VARIANTS_LARGE(FQ_DEC)
 #undef FQ_DEC
@@ -300,15 +383,90 @@ hipError_t dispatch(const fq_codebook* cb, const uint32_t* codes, const uint16_t
 
 hipError_t launch_decode(const fq_codebook* cb, const uint32_t* codes, const uint16_t* norms,
                          const int64_t* rows, int64_t n_records, int64_t n, void* y, fq_dtype yt,
-                         int64_t ld, hipStream_t s) {
+                         int64_t ld, hipStream_t s, bool packed) {
   if (yt == FQ_F16) {
     _Float16* yy = static_cast<_Float16*>(y);
-    return rows ? dispatch<_Float16, true>(cb, codes, norms, rows, n_records, n, yy, ld, s)
-                : dispatch<_Float16, false>(cb, codes, norms, rows, n_records, n, yy, ld, s);
+    if (packed)
+      return rows ? dispatch<_Float16, true, true>(cb, codes, norms, rows, n_records, n, yy, ld, s)
+                  : dispatch<_Float16, false, true>(cb, codes, norms, rows, n_records, n, yy, ld, s);
+    return rows ? dispatch<_Float16, true, false>(cb, codes, norms, rows, n_records, n, yy, ld, s)
+                : dispatch<_Float16, false, false>(cb, codes, norms, rows, n_records, n, yy, ld, s);
   }
   float* yy = static_cast<float*>(y);
-  return rows ? dispatch<float, true>(cb, codes, norms, rows, n_records, n, yy, ld, s)
-              : dispatch<float, false>(cb, codes, norms, rows, n_records, n, yy, ld, s);
+  if (packed)
+    return rows ? dispatch<float, true, true>(cb, codes, norms, rows, n_records, n, yy, ld, s)
+                : dispatch<float, false, true>(cb, codes, norms, rows, n_records, n, yy, ld, s);
+  return rows ? dispatch<float, true, false>(cb, codes, norms, rows, n_records, n, yy, ld, s)
+              : dispatch<float, false, false>(cb, codes, norms, rows, n_records, n, yy, ld, s);
+}
+
+// ---------------------------------------------------------------- packing
+namespace {
+
+// Bits [lo, lo + 32) of record r's bit string: its F field bits (from the
+// word-aligned record, bits past F ignored), then the 16 norm bits, then zeros.
+template <int K, int BITS>
+__device__ inline uint32_t record_string_bits(const uint32_t* rec, uint32_t norm, int lo) {
+  using P = PackedShape<K, BITS>;
+  constexpr int W = Shape<K, BITS>::W;
+  auto sword = [&](int j) -> uint32_t {
+    uint32_t v = 0;
+    if (j < W) {
+      const int top = P::F - 32 * j;   // field bits in word j
+      v = top >= 32 ? rec[j] : (top > 0 ? rec[j] & ((1u << top) - 1u) : 0u);
+    }
+    constexpr int NW0 = P::F >> 5, NSH = P::F & 31;
+    if (j == NW0) v |= norm << NSH;
+    if (NSH > 16 && j == NW0 + 1) v |= norm >> (32 - NSH);
+    return v;
+  };
+  const int i = lo >> 5;
+  return __builtin_amdgcn_alignbit(sword(i + 1), sword(i), (uint32_t)(lo & 31));
+}
+
+// One thread per word of the stream: the bits of the (at most two) records
+// that fall in it.
+template <int K, int BITS>
+__global__ __launch_bounds__(256) void pack_kernel(const uint32_t* __restrict__ codes,
+                                                   const uint16_t* __restrict__ norms, int64_t n,
+                                                   uint32_t* __restrict__ packed, int64_t words) {
+  using P = PackedShape<K, BITS>;
+  constexpr int W = Shape<K, BITS>::W;
+  const int64_t w = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (w >= words) return;
+  const int64_t b0 = 32 * w, b1 = b0 + 32;
+  const int64_t r_last = (b1 - 1) / P::R < n - 1 ? (b1 - 1) / P::R : n - 1;
+  uint32_t out = 0;
+  for (int64_t r = b0 / P::R; r <= r_last; ++r) {
+    const int64_t rs = r * P::R;
+    const int64_t lo = (b0 > rs ? b0 : rs) - rs;                         // record bits [lo, hi)
+    const int64_t hi = (b1 < rs + P::R ? b1 : rs + P::R) - rs;
+    const int len = (int)(hi - lo);
+    const uint32_t v = record_string_bits<K, BITS>(codes + r * W, norms[r], (int)lo);
+    const uint32_t m = len >= 32 ? ~0u : ((1u << len) - 1u);
+    out |= (v & m) << (int)((b0 > rs ? b0 : rs) - b0);
+  }
+  packed[w] = out;
+}
+
+}  // namespace
+
+int packed_record_bits(const fq_codebook* cb) { return cb->nb * cb->bits + 16; }
+
+hipError_t launch_pack(const fq_codebook* cb, const uint32_t* codes, const uint16_t* norms,
+                       int64_t n, uint32_t* packed, hipStream_t s) {
+  const int64_t words = (n * packed_record_bits(cb) + 31) / 32;
+  const int64_t blocks = (words + 255) / 256;
+#define FQ_PACK(KK, BB)                                                                      \
+  if (cb->k == KK && cb->bits == BB) {                                                       \
+    hipLaunchKernelGGL((pack_kernel<KK, BB>), dim3((unsigned)blocks), dim3(256), 0, s, codes, \
+                       norms, n, packed, words);                                             \
+    return hipGetLastError();                                                                \
+  }
+  FQ_VARIANTS(FQ_PACK)
+  FQ_VARIANTS_LARGE(FQ_PACK)
+#undef FQ_PACK
+  return hipErrorInvalidValue;
 }
 
 }  // namespace fq

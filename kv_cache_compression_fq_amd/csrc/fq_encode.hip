@@ -51,9 +51,12 @@ using namespace encx;
 // table (staged once per workgroup) are shared by more waves and two
 // workgroups fit a compute unit: 16 waves per CU, 4 per SIMD (with 4 waves
 // per workgroup the LDS allowed 3 workgroups, 3 waves per SIMD, and the
-// encodes ran about 11 % slower)
+// encodes ran about 11 % slower).  The 4096-entry table (64 KB) leaves room
+// for one workgroup per compute unit only, so that one gets 12 waves (3 per
+// SIMD; 23 % faster than 8 on the 2^24-vector stress set; 16 waves with the
+// table split into binary16 codewords and float32 norms gained under 2 %).
 template <int BITS>
-constexpr int enc_waves() { return 8; }
+constexpr int enc_waves() { return BITS == 12 ? 12 : 8; }
 constexpr float SLACK = 1e-5f;  // covers |D~ - D| inside the square roots of the bound
 
 template <int K, int BITS>

@@ -93,9 +93,14 @@ hipError_t launch_encode_large(const fq_codebook* cb, const void* x, fq_dtype xt
 bool encode_k8_applies(const fq_codebook* cb);
 hipError_t launch_encode_k8(const fq_codebook* cb, const void* x, fq_dtype xt, int64_t n,
                             int64_t ld, uint32_t* codes, uint16_t* norms, hipStream_t s);
+// `packed`: codes is a packed record stream (norms unused), see fq_pack_records
 hipError_t launch_decode(const fq_codebook* cb, const uint32_t* codes, const uint16_t* norms,
                          const int64_t* rows, int64_t n_records, int64_t n, void* y,
-                         fq_dtype yt, int64_t ld, hipStream_t s);
+                         fq_dtype yt, int64_t ld, hipStream_t s, bool packed = false);
+// word-aligned records + norms -> packed stream
+hipError_t launch_pack(const fq_codebook* cb, const uint32_t* codes, const uint16_t* norms,
+                       int64_t n, uint32_t* packed, hipStream_t s);
+int packed_record_bits(const fq_codebook* cb);
 bool attend_supported(const fq_codebook* cb);  // the codebooks fit the kernel's LDS
 size_t attend_workspace_bytes(const fq_codebook* cb_k, int B, int Hq, int Hkv, int64_t T);
 // Tokens a decode step appends (the last M of the T attended tokens), to be

@@ -19,7 +19,8 @@ FQ_OK, FQ_ERR_INVALID_ARG, FQ_ERR_BAD_ARTIFACT, FQ_ERR_UNSUPPORTED, FQ_ERR_NO_ME
 FQ_STATIC_SCRATCH_BYTES = 4 << 20
 
 EXPORTS = ["fq_status_string", "fq_artifact_check", "fq_codebook_load", "fq_codebook_info",
-           "fq_search_cost", "fq_codebook_free", "fq_encode", "fq_decode", "fq_attend_workspace_size",
+           "fq_search_cost", "fq_codebook_free", "fq_encode", "fq_decode", "fq_pack_records",
+           "fq_decode_packed", "fq_attend_workspace_size",
            "fq_attend_decode", "fq_attend_decode_static", "fq_attend_queries",
            "fq_decode_step"]
 
@@ -34,12 +35,12 @@ class fq_info(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("k", ctypes.c_int32), ("N", ctypes.c_int32),
                 ("nb", ctypes.c_int32), ("idx_bits", ctypes.c_int32),
                 ("record_words", ctypes.c_int32), ("last_block", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("rate_nominal", ctypes.c_double),
+                ("packed_bits", ctypes.c_int32), ("rate_nominal", ctypes.c_double),
                 ("rate_actual", ctypes.c_double), ("distortion", ctypes.c_double),
                 ("artifact_hash", ctypes.c_uint64)]
 
     def as_dict(self):
-        return {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
+        return {f: getattr(self, f) for f, _ in self._fields_}
 
 
 _lib = None
@@ -67,6 +68,8 @@ def library(path=LIB_PATH):
     lib.fq_codebook_free.restype = None
     lib.fq_encode.argtypes = [_P, _P, ctypes.c_int, _I64, _I64, _P, _P, _P]
     lib.fq_decode.argtypes = [_P, _P, _P, _P, _I64, _I64, _P, ctypes.c_int, _I64, _P]
+    lib.fq_pack_records.argtypes = [_P, _P, _P, _I64, _P, _P]
+    lib.fq_decode_packed.argtypes = [_P, _P, _P, _I64, _I64, _P, ctypes.c_int, _I64, _P]
     lib.fq_attend_workspace_size.argtypes = [_P, ctypes.c_int, ctypes.c_int, ctypes.c_int, _I64,
                                              ctypes.POINTER(ctypes.c_size_t)]
     lib.fq_attend_decode.argtypes = [_P, _P, _P, _P, _P, _P, _P, ctypes.c_int, ctypes.c_int,
@@ -163,6 +166,13 @@ class Codebook:
     def nb(self):
         return self.info["nb"]
 
+    @property
+    def packed_bits(self):
+        return self.info["packed_bits"]
+
+    def packed_words(self, n):
+        return -(-(n * self.packed_bits) // 32)
+
 
 def fq_codebook_load(blob, device=0):
     h = ctypes.c_void_p()
@@ -238,6 +248,41 @@ def fq_decode(cb, codes, norms, rows=None, y=None, y_dtype=None, stream=None):
     _check(library().fq_decode(cb.handle, _ptr(codes), _ptr(norms), _ptr(rows), n_records, n,
                                _ptr(y), _dtype_code(y.dtype), y.stride(0),
                                _stream(stream, codes.device)), "fq_decode")
+    return y
+
+
+def fq_pack_records(cb, codes, norms, packed=None, stream=None):
+    """Word-aligned records [n, W] + norms [n] -> packed stream [ceil(n R / 32)] int32."""
+    import torch
+    if codes.dim() != 2 or codes.shape[1] != cb.W or not codes.is_contiguous():
+        raise ValueError("codes must be [n, W] contiguous")
+    n = codes.shape[0]
+    if norms.shape != (n,) or not norms.is_contiguous():
+        raise ValueError("norms must be [n] contiguous")
+    if packed is None:
+        packed = torch.empty((cb.packed_words(n),), dtype=torch.int32, device=codes.device)
+    if packed.numel() < cb.packed_words(n) or not packed.is_contiguous():
+        raise ValueError("packed must hold ceil(n R / 32) words")
+    _check(library().fq_pack_records(cb.handle, _ptr(codes), _ptr(norms), n, _ptr(packed),
+                                     _stream(stream, codes.device)), "fq_pack_records")
+    return packed
+
+
+def fq_decode_packed(cb, packed, n_records, rows=None, y=None, y_dtype=None, stream=None):
+    """Decode n_records packed records (rows=None) or records rows[i]; returns y [n, 64]."""
+    import torch
+    if packed.dim() != 1 or not packed.is_contiguous() or packed.numel() < cb.packed_words(n_records):
+        raise ValueError("packed must be a contiguous stream of ceil(n_records R / 32) words")
+    n = n_records if rows is None else rows.shape[0]
+    if rows is not None and (rows.dtype != torch.int64 or not rows.is_contiguous()):
+        raise ValueError("rows must be contiguous int64")
+    if y is None:
+        y = torch.empty((n, 64), dtype=y_dtype or torch.float16, device=packed.device)
+    if y.dim() != 2 or y.shape[0] != n or y.stride(1) != 1:
+        raise ValueError("y must be [n, >=64] with unit column stride")
+    _check(library().fq_decode_packed(cb.handle, _ptr(packed), _ptr(rows), n_records, n, _ptr(y),
+                                      _dtype_code(y.dtype), y.stride(0),
+                                      _stream(stream, packed.device)), "fq_decode_packed")
     return y
 
 

@@ -23,6 +23,12 @@ Readings:
   record, counted from the least significant bit of little-endian 32-bit
   words; a record is W = ceil(nb b / 32) words; unused high bits are 0.
   Norms live in their own array, one binary16 per record.
+* Packed records (a second storage form): record r of R = nb b + 16 bits at
+  bits [r R, (r+1) R) of one word stream, counted from the least significant
+  bit of little-endian 32-bit words -- field j at record bits [j b, (j+1) b),
+  then the 16 bits of the binary16 norm; bits past the last record are 0.
+  No record is rounded up to whole words, so a k = 64, N = 4096 vector takes
+  28 bits (12 + 16), the rate of the code plus its norm.
 """
 from fractions import Fraction
 
@@ -209,3 +215,41 @@ def decode_records(words, norm_bits, Pi, C):
     nb = -(-d // k)
     bits = int(N).bit_length() - 1
     return decode(unpack(words, nb, bits), norm_bits, Pi, C)
+
+
+# -------------------------------------------------------------- packed records
+def packed_record_bits(nb, bits):
+    """R: the fields of one record and its 16-bit norm."""
+    return nb * bits + 16
+
+
+def pack_stream(idx, norm_bits, bits):
+    """Indices [n, nb] and binary16 norm bits [n] -> packed stream (uint32 words)."""
+    idx = np.asarray(idx, dtype=np.uint64)
+    n, nb = idx.shape
+    R = packed_record_bits(nb, bits)
+    nu = np.asarray(norm_bits, dtype=np.uint64)
+    rec = np.zeros((n, R), dtype=np.uint8)            # one bit per entry, LSB first
+    for j in range(nb):
+        for t in range(bits):
+            rec[:, j * bits + t] = (idx[:, j] >> np.uint64(t)) & np.uint64(1)
+    for t in range(16):
+        rec[:, nb * bits + t] = (nu >> np.uint64(t)) & np.uint64(1)
+    words = -(-(n * R) // 32)
+    flat = np.zeros(words * 32, dtype=np.uint8)
+    flat[:n * R] = rec.reshape(-1)
+    return np.packbits(flat, bitorder="little").view("<u4").astype(np.uint32)
+
+
+def unpack_stream(words, n, nb, bits):
+    """Inverse of ``pack_stream``: (indices [n, nb] int64, norm bits [n] uint16)."""
+    R = packed_record_bits(nb, bits)
+    w = np.ascontiguousarray(words, dtype="<u4")
+    flat = np.unpackbits(w.view(np.uint8), bitorder="little")[:n * R].reshape(n, R)
+    weights = (np.uint64(1) << np.arange(bits, dtype=np.uint64))
+    idx = np.zeros((n, nb), dtype=np.int64)
+    for j in range(nb):
+        idx[:, j] = (flat[:, j * bits:(j + 1) * bits].astype(np.uint64) @ weights).astype(np.int64)
+    w16 = (np.uint64(1) << np.arange(16, dtype=np.uint64))
+    nu = (flat[:, nb * bits:].astype(np.uint64) @ w16).astype(np.uint16)
+    return idx, nu

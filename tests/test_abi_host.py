@@ -44,6 +44,7 @@ def test_committed_artifacts_pass_library_check(k, N):
         (k, N, a["nb"], a["bits"], a["W"])
     assert info["artifact_hash"] == a["hash"]
     assert info["rate_nominal"] == a["bits"] / k
+    assert info["packed_bits"] == a["nb"] * a["bits"] + 16
 
 
 def make_book(k, N, C=None, Pi=None, d=64):
@@ -109,6 +110,10 @@ def test_null_arguments_rejected_without_device():
                                 ctypes.c_float(1.0), None, 0, None, None) == INV
     assert lib.fq_attend_decode_static(None, None, None, None, None, None, None, 1, 1, 1, 1,
                                        ctypes.c_float(1.0), None, None) == INV
+    assert lib.fq_pack_records(None, None, None, 10, None, None) == INV
+    assert lib.fq_decode_packed(None, None, None, 0, 10, None, 1, 64, None) == INV
+    e, f = ctypes.c_double(), ctypes.c_double()
+    assert lib.fq_search_cost(None, None, 1, 10, 64, ctypes.byref(e), ctypes.byref(f)) == INV
 
 
 def test_load_without_device_reports_device_error():

@@ -224,6 +224,56 @@ def test_random_access_decode(dev, kb):
     assert np.all(got[~ok] == 0)
 
 
+# ----------------------------------------------------------- packed records
+@pytest.mark.parametrize("k,N", [(64, 4096), (32, 4096), (8, 16), (2, 16), (3, 512), (3, 4096)])
+def test_pack_records_bit_exact(dev, k, N):
+    """fq_pack_records of uniform random records and norms equals the oracle's
+    packed stream bit for bit (ragged counts), and writes nothing past it."""
+    art, cb = book(k, N)
+    bits = art["nb"] * art["bits"]
+    assert cb.packed_bits == bits + 16
+    for n in (1, 13, 1000, 4099):
+        w = synth.random_records((n,), cb.W, bits, 41 + n)
+        nu = synth.random_norms((n,), 42 + n)
+        words = cb.packed_words(n)
+        pv, pw = canary_buffer(words, 0, torch.int32, dev)
+        fq.fq_pack_records(cb, to_dev(w, dev, np.int32), to_dev(nu, dev, np.int16), packed=pv)
+        torch.cuda.synchronize()
+        assert canary_intact(pw, words)
+        want = codec.pack_stream(codec.unpack(w, art["nb"], art["bits"]), nu, art["bits"])
+        assert np.array_equal(host(pv, np.uint32), want), (k, N, n)
+
+
+@pytest.mark.parametrize("k,N", [(64, 4096), (32, 4096), (8, 16), (3, 4096), (2, 64)])
+def test_decode_packed_contiguous_and_random_access(dev, k, N):
+    """Encode, pack, decode from the packed stream: every row equals the
+    word-aligned decode of the same codes bit for bit, and the oracle's decode
+    within 1e-3 nu16; random access (with out-of-range addresses -> zero rows)."""
+    art, cb = book(k, N)
+    x = np.concatenate([synth.kv_slab(2, 4, 1, 1, 3, 700).reshape(-1, 64), synth.special_vectors()])
+    n = len(x)
+    codes, norms = fq.fq_encode(cb, to_dev(x, dev))
+    packed = fq.fq_pack_records(cb, codes, norms)
+    yv, yw = canary_buffer(n, 64, torch.int16, dev)
+    fq.fq_decode_packed(cb, packed, n, y=yv.view(torch.float16))
+    y_ref = fq.fq_decode(cb, codes, norms)
+    rows = synth.random_rows(n, 3000, seed=43)
+    rows[:4] = [-1, n, n - 1, 0]
+    rv, rw = canary_buffer(len(rows), 64, torch.int16, dev)
+    fq.fq_decode_packed(cb, packed, n, rows=to_dev(rows, dev), y=rv.view(torch.float16))
+    torch.cuda.synchronize()
+    assert canary_intact(yw, n) and canary_intact(rw, len(rows))
+    assert torch.equal(yv, y_ref.view(torch.int16))
+    c_np, n_np = host(codes, np.uint32), host(norms, np.uint16)
+    i2, n2 = codec.unpack_stream(host(packed, np.uint32), n, art["nb"], art["bits"])
+    assert np.array_equal(i2, codec.unpack(c_np, art["nb"], art["bits"])) and np.array_equal(n2, n_np)
+    check_decode_full(art, c_np, n_np, host(yv, np.float16), f"packed k{k}N{N}")
+    got = host(rv, np.float16).astype(np.float64)
+    ok = (rows >= 0) & (rows < n)
+    assert np.all(got[~ok] == 0)
+    assert np.array_equal(got[ok], host(yv, np.float16).astype(np.float64)[rows[ok]])
+
+
 # ---------------------------------------------------------------- attention
 ATT_CASES = [
     # (B, Hq, Hkv, T, codebook shared by K and V); k = 4, 8 with T a multiple
@@ -690,6 +740,31 @@ def test_large_blocks_gpt2_cache_full_size(dev, k):
     rows = sample_rows(n, 1 << 17, seed=k * 1000 + 4096)
     check_rows_full(art, x[rows], c_np[rows], n_np[rows], f"gpt2 k{k}N4096 (2^17 rows)")
     check_decode_full(art, c_np, n_np, host(yv, np.float16), f"gpt2 k{k}N4096")
+
+
+@pytest.mark.parametrize("k", [32, 64])
+def test_packed_records_gpt2_cache_full_size(dev, k):
+    """The 36.6x (k = 64) and 25.6x (k = 32) packed form of the whole GPT-2-shaped
+    cache: packed stream equal to the oracle's packing of the GPU's codes, every
+    vector decoded from it equal to the word-aligned decode bit for bit."""
+    print(f"gpt2 cache k{k}N4096 packed", flush=True)
+    art, cb = book(k, 4096)
+    x = gpt2_cache()
+    n = len(x)
+    codes, norms = fq.fq_encode(cb, to_dev(x, dev))
+    words = cb.packed_words(n)
+    pv, pw = canary_buffer(words, 0, torch.int32, dev)
+    fq.fq_pack_records(cb, codes, norms, packed=pv)
+    y1 = fq.fq_decode(cb, codes, norms)
+    y2 = fq.fq_decode_packed(cb, pv, n)
+    torch.cuda.synchronize()
+    assert canary_intact(pw, words)
+    want = codec.pack_stream(codec.unpack(host(codes, np.uint32), art["nb"], art["bits"]),
+                             host(norms, np.uint16), art["bits"])
+    assert np.array_equal(host(pv, np.uint32), want)
+    assert torch.equal(y1, y2)
+    print(f"PARITY gpt2 k{k}N4096 packed rows={n} bits_per_vector={cb.packed_bits} "
+          f"compression={1024 / cb.packed_bits:.1f}x", flush=True)
 
 
 @pytest.mark.parametrize("k,N", [(4, 256), (8, 256)])

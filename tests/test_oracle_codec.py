@@ -68,6 +68,37 @@ def test_pack_roundtrip_and_padding(nb, bits):
         assert np.all(words[:, -1] >> np.uint32(used) == 0)
 
 
+def test_pack_stream_hand_examples():
+    ex = json.load(open(os.path.join(GOLDEN_DIR, "packed_stream_examples.json")))["examples"]
+    for e in ex:
+        idx = np.array(e["fields"], dtype=np.int64)
+        nbits = np.array([int(v, 16) for v in e["norms"]], dtype=np.uint16)
+        words = codec.pack_stream(idx, nbits, e["bits"])
+        assert [f"0x{w:08X}" for w in words] == e["words"], e["why"]
+        i2, n2 = codec.unpack_stream(words, len(idx), e["nb"], e["bits"])
+        assert np.array_equal(i2, idx) and np.array_equal(n2, nbits)
+
+
+@pytest.mark.parametrize("nb,bits", [(1, 12), (2, 12), (8, 4), (16, 2), (22, 9), (32, 4)])
+def test_pack_stream_roundtrip_and_record_bits(nb, bits):
+    """Round trip on ragged counts, and record r's first nb*bits bits are the
+    word-aligned record's (same field layout), its next 16 its norm."""
+    rng = np.random.default_rng([19, nb, bits])
+    for n in (1, 7, 33, 200):
+        idx = rng.integers(0, 1 << bits, size=(n, nb))
+        nbits = rng.integers(0, 1 << 16, size=n).astype(np.uint16)
+        words = codec.pack_stream(idx, nbits, bits)
+        R = codec.packed_record_bits(nb, bits)
+        assert len(words) == -(-(n * R) // 32)
+        i2, n2 = codec.unpack_stream(words, n, nb, bits)
+        assert np.array_equal(i2, idx) and np.array_equal(n2, nbits)
+        allbits = np.unpackbits(words.view(np.uint8), bitorder="little")
+        assert not np.any(allbits[n * R:])                     # padding bits are zero
+        aligned = np.unpackbits(codec.pack(idx, bits).view(np.uint8), bitorder="little")
+        aligned = aligned.reshape(n, -1)[:, :nb * bits]
+        assert np.array_equal(allbits[:n * R].reshape(n, R)[:, :nb * bits], aligned)
+
+
 # ------------------------------------------------------------------ encode
 def naive_encode_one(x, Pi, C):
     """Pure-Python loops: norm, rotation, per-block brute-force argmin."""
