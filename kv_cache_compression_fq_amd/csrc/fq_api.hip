@@ -226,14 +226,18 @@ fq_status fq_codebook_load(const void* artifact, size_t nbytes, int device, fq_c
         }
   }
   // Encode rotation error bound per coordinate of a unit vector.  Each output
-  // is a float32 sum of four 16-product groups (each accumulated from zero,
-  // at most 15 roundings) for the hi part and four for the lo part (scaled by
-  // 2^-11), then one fused multiply-add and one product: at most 20 roundings
-  // of 2^-23 relative to sum_j |Pi_ij x_j| <= |x|, plus the binary16 split of
-  // Pi (|x|_1 <= 8 |x|) and the float32 reciprocal of the norm; for float32
-  // input the split of x adds 2^-23.
+  // is a float32 sum of four 16-product groups of the hi part (each
+  // accumulated from zero, at most 15 roundings), then one fused multiply-add
+  // with the lo part and one product: at most 20 roundings of 2^-23 relative
+  // to sum_j |Pi_ij x_j| <= |x|.  The lo part (Pi_lo x, and Pi_hi x_lo for
+  // float32 input, with |Pi_lo| < 1 and |x_lo|_1 <= 8 |x|) is one chained
+  // accumulation of at most 128 terms of size sum <= 16 |x| in all, each
+  // rounding at most 2^-24 of the running sum, weighted 2^-11: below
+  // 128 * 16 * 2^-35 |x| = 2^-24 |x|.  Plus the binary16 split of Pi
+  // (|x|_1 <= 8 |x|) and the float32 reciprocal of the norm; for float32 input
+  // the split of x adds 2^-23.
   {
-    const double acc = 20.0 * 0x1p-23 * (1.0 + 0x1p-10) * (1.0 + 0x1p-11);
+    const double acc = 20.0 * 0x1p-23 * (1.0 + 0x1p-10) * (1.0 + 0x1p-11) + 0x1p-24;
     // scaling: norm within 3.3e-7 relative, reciprocal 1 ulp, final fma and product
     const double scal = 3.3e-7 + 3.0 * 0x1p-24;
     cb->enc_ez16 = (float)((acc + 8.0 * rho_pi + scal) * 1.01);

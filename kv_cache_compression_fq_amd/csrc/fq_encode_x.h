@@ -112,9 +112,12 @@ __device__ inline void finish_x<float>(const XRaw<float>& r, XFrag<float>& f) {
 
 // z~ of the chunk into sZ: row j (= lane % 16) gets coordinates
 // 16 ot + 4 (lane / 16) + r.  Pi = Pi_hi + 2^-11 Pi_lo as A fragments of
-// v_mfma_f32_16x16x16_f16 in sRot ([part][ot][kq][lane][4]); every
-// 16-product group is accumulated from zero and the groups are summed in
-// float32, which keeps the rounding bound small; inv is 1 / |x|.
+// v_mfma_f32_16x16x16_f16 in sRot ([part][ot][kq][lane][4]).  Every
+// 16-product group of the hi part is accumulated from zero and the groups are
+// summed in float32, which keeps the rounding bound small; the lo products
+// (Pi_lo x, and Pi_hi x_lo for float32 input) carry a weight of 2^-11, so
+// their roundings hardly count and they are chained in one accumulator.  inv
+// is 1 / |x|.
 template <typename TX>
 __device__ inline void rotate_to_lds(const XFrag<TX>& xf, const _Float16* sRot, float inv, float* sZ,
                                      int lane) {
@@ -122,25 +125,21 @@ __device__ inline void rotate_to_lds(const XFrag<TX>& xf, const _Float16* sRot, 
 #pragma unroll
   for (int ot = 0; ot < 4; ++ot) {
     const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
-    constexpr int NP = sizeof(TX) == 4 ? 3 : 2;
-    floatx4 pp[4][NP];
+    floatx4 ph4[4];
+    floatx4 lo = zero;
 #pragma unroll
     for (int kq = 0; kq < 4; ++kq) {
       const half4 ph = *reinterpret_cast<const half4*>(sRot + (((0 * 4 + ot) * 4 + kq) * 64 + lane) * 4);
       const half4 pl = *reinterpret_cast<const half4*>(sRot + (((1 * 4 + ot) * 4 + kq) * 64 + lane) * 4);
-      pp[kq][0] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, xf.hi[kq], zero, 0, 0, 0);
-      pp[kq][1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, xf.hi[kq], zero, 0, 0, 0);
-      if constexpr (NP == 3)
-        pp[kq][2] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, xf.lo[kq], zero, 0, 0, 0);
+      ph4[kq] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, xf.hi[kq], zero, 0, 0, 0);
+      lo = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, xf.hi[kq], lo, 0, 0, 0);
+      if constexpr (sizeof(TX) == 4) lo = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, xf.lo[kq], lo, 0, 0, 0);
     }
     floatx4 zv;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float zh = (pp[0][0][r] + pp[1][0][r]) + (pp[2][0][r] + pp[3][0][r]);
-      float zl = (pp[0][1][r] + pp[1][1][r]) + (pp[2][1][r] + pp[3][1][r]);
-      if constexpr (NP == 3)
-        zl += (pp[0][2][r] + pp[1][2][r]) + (pp[2][2][r] + pp[3][2][r]);
-      zv[r] = fmaf(zl, 0x1p-11f, zh) * inv;
+      const float zh = (ph4[0][r] + ph4[1][r]) + (ph4[2][r] + ph4[3][r]);
+      zv[r] = fmaf(lo[r], 0x1p-11f, zh) * inv;
     }
     *reinterpret_cast<floatx4*>(sZ + j * ZP + 16 * ot + 4 * g) = zv;
   }
