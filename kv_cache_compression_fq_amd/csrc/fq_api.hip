@@ -423,9 +423,10 @@ fq_status fq_search_cost(const fq_codebook* cb, const void* x, fq_dtype x_dtype,
         bool inside = true;
         int cell = 0, mul = 1;
         for (int t = 0; t < dims; ++t) {
-          const float zf = (float)z[j * k + t];
-          inside = inside && fq::grid_inside(zf);
-          cell += fq::grid_axis(zf, G, part ? sc1 : sc) * mul;
+          const float u = fq::grid_pos((float)z[j * k + t], part ? sc1 : sc);
+          const bool in = fq::grid_pos_inside(u, G);
+          inside = inside && in;
+          if (in) cell += (int)u * mul;
           mul *= G;
         }
         const uint16_t c0 = (part ? cb->grid1_host : cb->grid_host)[(size_t)cell * re];

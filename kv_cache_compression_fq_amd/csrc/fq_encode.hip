@@ -59,13 +59,32 @@ template <int BITS>
 constexpr int enc_waves() { return BITS == 12 ? 12 : 8; }
 constexpr float SLACK = 1e-5f;  // covers |D~ - D| inside the square roots of the bound
 
+// 1 / sqrt(a) in float64 for a > 0 (infinity for 0, NaN for NaN): the hardware
+// estimate refined by two Newton steps y <- y + y (1 - a y^2) / 2, each of
+// which squares the relative error, so the result is within a few units in
+// the last place.
+__device__ inline double rsqrt_f64(double a) {
+  double y = __builtin_amdgcn_rsq(a);
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const double e = fma(-a * y, y, 1.0);
+    y = fma(0.5 * y, e, y);
+  }
+  return y;
+}
+
+// Fields of BITS bits that can overlap one 32-bit word of a record.
+template <int BITS>
+constexpr int pack_fields() { return 31 / BITS + 2; }
+
 template <int K, int BITS>
 struct EncShape {
   static constexpr int NB = (D + K - 1) / K;
   static constexpr int LAST = D - (NB - 1) * K;
   static constexpr int S = ((K + 1) + 3) / 4 * 4;   // search-table stride (floats)
   static constexpr int W = (NB * BITS + 31) / 32;
-  static constexpr int IP = (NB + 2) / 2 * 2;       // u16 per staged index row
+  // u16 per staged index row: the NB indices, then zeros for the packer
+  static constexpr int IP = (NB + pack_fields<BITS>()) / 2 * 2;
   static constexpr int NCOL = EV * NB;              // columns per chunk
   static constexpr int CPL = (NCOL + 63) / 64;      // columns per lane
   static constexpr bool EXACT_LAST = LAST < K;      // one-coordinate last block
@@ -87,8 +106,9 @@ struct EncArgs {
   int N;
   float ez;   // bound on |z~ - z| per coordinate of a unit vector
   float gv;   // relative rounding bound of the float32 search value
-  const uint16_t* grid;    // candidate records of the block grid (k = 2, 3)
+  const uint16_t* grid;    // candidate records of the block grid (k = 2, 3, 4)
   const uint16_t* grid1;   // candidate records of the one-coordinate last block
+  uint32_t grid_bytes, grid1_bytes;
   int G, G1;               // cells per dimension
   float gscale, g1scale;   // cells per unit length
   OutRows rows;            // record of each encoded row
@@ -105,8 +125,9 @@ __host__ __device__ inline size_t enc_table_bytes(int N, int S) {   // N rows + 
 }
 
 // Word w of a record from the staged indices of one vector (4-byte aligned
-// row of uint16): byte permutes for 8-bit fields, nibble merges for 4-bit
-// fields, a shift loop otherwise.
+// row of uint16, zero past the NB indices for pack_fields - 1 entries): byte
+// permutes for 8-bit fields, nibble merges for 4-bit fields, otherwise the
+// overlapping fields gathered into 64 bits and shifted into place.
 template <int BITS, int NB>
 __device__ inline uint32_t pack_word(const uint16_t* idx, int w) {
   const uint32_t* p = reinterpret_cast<const uint32_t*>(idx);
@@ -122,16 +143,13 @@ __device__ inline uint32_t pack_word(const uint16_t* idx, int w) {
     }
     return v;
   } else {
+    constexpr int F = pack_fields<BITS>();
     const int j0 = (32 * w) / BITS;
-    int j1 = (32 * w + 31) / BITS;
-    if (j1 > NB - 1) j1 = NB - 1;
-    uint32_t v = 0;
-    for (int jj = j0; jj <= j1; ++jj) {
-      const int sh = jj * BITS - 32 * w;
-      const uint32_t f = idx[jj];
-      v |= sh >= 0 ? (f << sh) : (f >> (-sh));
-    }
-    return v;
+    const int sh = 32 * w - j0 * BITS;   // 0 <= sh < BITS
+    uint64_t acc = 0;
+#pragma unroll
+    for (int u = 0; u < F; ++u) acc |= (uint64_t)idx[j0 + u] << (u * BITS);
+    return (uint32_t)(acc >> sh);
   }
 }
 
@@ -145,30 +163,32 @@ struct ColPrep {
   uint32_t rec[RW];
 };
 
-template <int K, int RW, bool GRID, bool LASTB>
+// Candidate records are read through a buffer resource (32-bit offsets; the
+// grid of a codebook is at most a few MB).
+template <int K, int RW, bool GRID>
 __device__ inline void prepare_column(ColPrep<K, RW>& cp, const float* zrow, bool live,
-                                      const uint16_t* grid, int G, float gscale) {
-  constexpr int KR = LASTB ? 1 : K;   // real coordinates
+                                      __amdgpu_buffer_rsrc_t grid, int G, float gscale) {
   float zz = 0.f;
 #pragma unroll
   for (int t = 0; t < K; ++t) {
-    cp.z[t] = (live && t < KR) ? zrow[t] : 0.f;
+    cp.z[t] = live ? zrow[t] : 0.f;
     zz = fmaf(cp.z[t], cp.z[t], zz);
   }
   cp.zz = zz;
   cp.inside = live;
   if constexpr (GRID) {
-    int cell = 0, mul = 1;
+    uint32_t cell = 0, mul = 1;
 #pragma unroll
-    for (int t = 0; t < KR; ++t) {
-      cp.inside = cp.inside && grid_inside(cp.z[t]);
-      cell += grid_axis(cp.z[t], G, gscale) * mul;
-      mul *= G;
+    for (int t = 0; t < K; ++t) {
+      const float u = grid_pos(cp.z[t], gscale);
+      cp.inside = cp.inside && grid_pos_inside(u, G);
+      cell += (uint32_t)(int)u * mul;   // used only when every coordinate is inside
+      mul *= (uint32_t)G;
     }
-    const uint32_t* rp = reinterpret_cast<const uint32_t*>(grid + (size_t)cell * (2 * RW));
+    const uint32_t off = (cp.inside ? cell : 0u) * (4u * RW);
 #pragma unroll
     for (int h = 0; h < RW / 4; ++h) {
-      const u32x4 r0 = *reinterpret_cast<const u32x4*>(rp + 4 * h);
+      const u32x4 r0 = __builtin_amdgcn_raw_buffer_load_b128(grid, off + 16 * h, 0, 0);
       cp.rec[4 * h] = r0.x;
       cp.rec[4 * h + 1] = r0.y;
       cp.rec[4 * h + 2] = r0.z;
@@ -178,9 +198,8 @@ __device__ inline void prepare_column(ColPrep<K, RW>& cp, const float* zrow, boo
 }
 
 // Best and second-best t(n) = |c_n|^2 - 2 <z, c_n> over the cell's list (grid)
-// or the whole codebook (scan), and the gap test.  For the last block only the
-// first coordinate counts: t(n) = c_n0^2 - 2 z_0 c_n0.
-template <int K, int S, int RW, bool GRID, bool LASTB>
+// or the whole codebook (scan), and the gap test.
+template <int K, int S, int RW, bool GRID>
 __device__ inline void search_column(const ColPrep<K, RW>& cp, const float* sEnc, int N, float gv,
                                      float ez, int& i1out, bool& certain) {
   float m1 = INFINITY, m2 = INFINITY;
@@ -188,39 +207,56 @@ __device__ inline void search_column(const ColPrep<K, RW>& cp, const float* sEnc
   bool listed = true;   // the search covered every possible nearest codeword
   // list slots past the count hold the sentinel row N (zero codeword with an
   // infinite norm), so a full block needs no per-slot test
-  auto visit = [&](const float* er, int i, bool use) {
-    float t;
-    if constexpr (LASTB) {
-      t = fmaf(er[0], cp.z[0], 0.25f * er[0] * er[0]);
-      t = use ? t : INFINITY;
-    } else {
-      t = er[K];
+  auto visit = [&](const float (&er)[K + 1], int i) {
+    float t = er[K];
 #pragma unroll
-      for (int tt = 0; tt < K; ++tt) t = fmaf(er[tt], cp.z[tt], t);
-    }
+    for (int tt = 0; tt < K; ++tt) t = fmaf(er[tt], cp.z[tt], t);
     const bool p = t < m1;
     m2 = __builtin_amdgcn_fmed3f(m1, m2, t);
     m1 = p ? t : m1;
     i1 = p ? i : i1;
   };
+  auto row = [&](uint32_t i, float (&er)[K + 1]) {
+#pragma unroll
+    for (int tt = 0; tt <= K; ++tt) er[tt] = sEnc[i * S + tt];
+  };
   if constexpr (GRID) {
-    // the cell's exact candidate list (count first, then increasing indices)
+    // the cell's exact candidate list (count first, then increasing indices),
+    // two entries per step so that two table reads are in flight together
     const uint32_t c0 = cp.rec[0] & 0xFFFFu;
     const int cnt = (cp.inside && c0 != GRID_OVERFLOW) ? (int)c0 : 0;
     listed = cnt > 0;
+    auto idx_of = [&](int e) -> uint32_t {
+      const uint32_t w = cp.rec[e >> 1];
+      // low half by a byte permute, which keeps the row address one shift-add
+      return (e & 1) ? (w >> 16) : __builtin_amdgcn_perm(0u, w, 0x0c0c0100u);
+    };
 #pragma unroll
-    for (int e = 1; e < 2 * RW; ++e) {
-      if (__builtin_amdgcn_ballot_w64(e <= cnt) == 0) break;
-      const uint32_t i = (e & 1) ? (cp.rec[e >> 1] >> 16) : (cp.rec[e >> 1] & 0xFFFFu);
-      visit(sEnc + i * S, (int)i, e <= cnt);
+    for (int e0 = 1; e0 < 2 * RW; e0 += 2) {
+      if (__builtin_amdgcn_ballot_w64(e0 <= cnt) == 0) break;
+      const uint32_t ia = idx_of(e0);
+      float ea[K + 1], eb[K + 1];
+      row(ia, ea);
+      if (e0 + 1 < 2 * RW) {
+        const uint32_t ib = idx_of(e0 + 1);
+        row(ib, eb);
+        visit(ea, (int)ia);
+        visit(eb, (int)ib);
+      } else {
+        visit(ea, (int)ia);
+      }
     }
   } else {
 #pragma unroll 4
-    for (int i = 0; i < N; ++i) visit(sEnc + i * S, i, true);
+    for (int i = 0; i < N; ++i) {
+      float er[K + 1];
+      row((uint32_t)i, er);
+      visit(er, i);
+    }
   }
   // gap test of the header, with the runner-up's terms doubled for both
   // (m1 <= m2) and (r + 3|z|)^2 <= 2 r^2 + 18 |z|^2
-  constexpr float KSQ = LASTB ? 1.f : (K == 2 ? 1.41421356f : (K == 3 ? 1.73205081f : (K == 4 ? 2.f : 2.82842712f)));
+  constexpr float KSQ = K == 2 ? 1.41421356f : (K == 3 ? 1.73205081f : (K == 4 ? 2.f : 2.82842712f));
   const float d2 = fmaxf(m2 + cp.zz, 0.f) + SLACK;
   // hardware square root (within 1 ulp), nudged up to stay an upper bound
   const float rt = __builtin_amdgcn_sqrtf(d2);
@@ -252,6 +288,8 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
   uint16_t* sIdx = reinterpret_cast<uint16_t*>(wb + EV * ZP * 4 + (Sh::EXACT_LAST ? EV * 8 : 0));
   uint16_t* sFb = sIdx + EV * IP;
 
+  // the staged index rows' zero tails (never written afterwards)
+  for (int i = lane; i < EV * (IP - NB); i += 64) sIdx[(i / (IP - NB)) * IP + NB + i % (IP - NB)] = 0;
   for (int i = threadIdx.x; i < ROT_BYTES / 16; i += blockDim.x)
     reinterpret_cast<u32x4*>(sRot)[i] = reinterpret_cast<const u32x4*>(a.rotfrag)[i];
   for (int i = threadIdx.x; i < (N + 1) * S / 4; i += blockDim.x)
@@ -261,6 +299,10 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
   __syncthreads();
 
   const TX* __restrict__ x = static_cast<const TX*>(a.x);
+  const __amdgpu_buffer_rsrc_t grid_rc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.grid), (short)0, (int)a.grid_bytes, BUF_DWORD3);
+  const __amdgpu_buffer_rsrc_t grid1_rc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.grid1), (short)0, (int)a.grid1_bytes, BUF_DWORD3);
   const int64_t nchunks = (a.n + EV - 1) / EV;
   constexpr int WAVES = enc_waves<BITS>();
   const int64_t tw = (int64_t)gridDim.x * WAVES;
@@ -313,7 +355,7 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
       ss += shfl_xor_f64(ss, 32);
       dt += shfl_xor_f64(dt, 16);
       dt += shfl_xor_f64(dt, 32);
-      if (g == 0) sZL[j] = dt / sqrt(ss);   // a zero vector gives NaN
+      if (g == 0) sZL[j] = dt * rsqrt_f64(ss);   // a zero vector gives NaN
     }
     if (ch + tw < nchunks) load_raw<TX>(row_of(ch + tw), g, xraw);
     // norm within 3.3e-7 relative (pairwise sum, hardware square root): its
@@ -354,8 +396,7 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
         const int c = lane + 64 * (qb + q);
         const int v = c / NBF, b = c - v * NBF;
         const bool live = c < NCF && v < nv;
-        prepare_column<K, RW, GRID, false>(cp[q], sZ + v * ZP + K * b, live, a.grid, a.G,
-                                           a.gscale);
+        prepare_column<K, RW, GRID>(cp[q], sZ + v * ZP + K * b, live, grid_rc, a.G, a.gscale);
       }
 #pragma unroll
       for (int q = 0; q < QB; ++q) {
@@ -364,7 +405,7 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
         const bool live = c < NCF && v < nv;
         int i1;
         bool certain;
-        search_column<K, S, RW, GRID, false>(cp[q], sEnc, N, a.gv, a.ez, i1, certain);
+        search_column<K, S, RW, GRID>(cp[q], sEnc, N, a.gv, a.ez, i1, certain);
         record(c, live, v, b, i1, certain);
       }
     }
@@ -375,14 +416,13 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
       const bool live = lane < nv;
       const int v = lane < EV ? lane : 0;
       const double z0 = sZL[v];
-      const float zf = (float)z0;
-      const bool inside = live && grid_inside(zf);
-      const int u = grid_axis(zf, a.G1, a.g1scale);
-      const uint32_t* rp = reinterpret_cast<const uint32_t*>(a.grid1 + (size_t)u * (2 * RW));
+      const float u = grid_pos((float)z0, a.g1scale);
+      const bool inside = live && grid_pos_inside(u, a.G1);
+      const uint32_t off = (inside ? (uint32_t)(int)u : 0u) * (4u * RW);
       uint32_t rec[RW];
 #pragma unroll
       for (int h = 0; h < RW / 4; ++h) {
-        const u32x4 r0 = *reinterpret_cast<const u32x4*>(rp + 4 * h);
+        const u32x4 r0 = __builtin_amdgcn_raw_buffer_load_b128(grid1_rc, off + 16 * h, 0, 0);
         rec[4 * h] = r0.x;
         rec[4 * h + 1] = r0.y;
         rec[4 * h + 2] = r0.z;
@@ -392,15 +432,26 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
       const int cnt = (inside && c0 != GRID_OVERFLOW) ? (int)c0 : 0;
       double best = INFINITY;
       int bi = 0;
-#pragma unroll
-      for (int e = 1; e < 2 * RW; ++e) {
-        if (__builtin_amdgcn_ballot_w64(e <= cnt) == 0) break;
-        const uint32_t i = (e & 1) ? (rec[e >> 1] >> 16) : (rec[e >> 1] & 0xFFFFu);
-        const double df = z0 + 0.5 * (double)sEnc[i * S];   // c_0 = -e_0 / 2, exact
+      auto consider = [&](int e, uint32_t i, float c) {
+        const double df = z0 + 0.5 * (double)c;   // c_0 = -e_0 / 2, exact
         const double dd = df * df;
         if (e <= cnt && dd < best) {
           best = dd;
           bi = (int)i;
+        }
+      };
+#pragma unroll
+      for (int e0 = 1; e0 < 2 * RW; e0 += 2) {   // two table reads in flight per step
+        if (__builtin_amdgcn_ballot_w64(e0 <= cnt) == 0) break;
+        const uint32_t ia = rec[e0 >> 1] >> 16;   // odd entries: high halves
+        const float ca = sEnc[ia * S];
+        if (e0 + 1 < 2 * RW) {
+          const uint32_t ib = rec[(e0 + 1) >> 1] & 0xFFFFu;
+          const float cb = sEnc[ib * S];
+          consider(e0, ia, ca);
+          consider(e0 + 1, ib, cb);
+        } else {
+          consider(e0, ia, ca);
         }
       }
       record(NCF + v, live, v, NB - 1, bi, cnt > 0);
@@ -472,9 +523,10 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
 #pragma unroll
         for (int t = 0; t < K; ++t)
           if (t < dims) {
-            const float zf = (float)zd[t];
-            inside = inside && grid_inside(zf);
-            cell += grid_axis(zf, G, sc) * mul;
+            const float u = grid_pos((float)zd[t], sc);
+            const bool in = grid_pos_inside(u, G);
+            inside = inside && in;
+            cell += (in ? (int)u : 0) * mul;   // stays inside the table
             mul *= G;
           }
         rec = (last ? a.grid1 : a.grid) + (size_t)cell * (2 * RW);
@@ -502,9 +554,11 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
     // ---- 6. pack + store (contiguous records, or appended to caches)
     if (a.rows.inner == 0) {
       uint32_t* __restrict__ out = a.codes + base * Sh::W;
-      for (int t = lane; t < nv * Sh::W; t += 64) {
+#pragma unroll
+      for (int it = 0; it < (EV * Sh::W + 63) / 64; ++it) {   // the same words of every chunk
+        const int t = lane + 64 * it;
         const int v = t / Sh::W, w = t - v * Sh::W;
-        out[t] = pack_word<BITS, NB>(sIdx + v * IP, w);
+        if (t < nv * Sh::W) out[t] = pack_word<BITS, NB>(sIdx + v * IP, w);
       }
       if (g == 0 && j < nv) a.norms[base + j] = nbits;
     } else {
@@ -558,6 +612,8 @@ hipError_t launch_k(const fq_codebook* cb, const TX* x, int64_t n, int64_t ld, u
   a.gv = (float)((K + 2) * 0x1p-24 * 1.01);
   a.grid = cb->t.grid;
   a.grid1 = cb->t.grid1 ? cb->t.grid1 : cb->t.grid;
+  a.grid_bytes = (uint32_t)(cb->grid_host.size() * sizeof(uint16_t));
+  a.grid1_bytes = (uint32_t)((cb->t.grid1 ? cb->grid1_host : cb->grid_host).size() * sizeof(uint16_t));
   a.G = cb->grid_G;
   a.G1 = cb->grid1_G > 0 ? cb->grid1_G : 1;
   a.gscale = grid_scale(cb->grid_G);

@@ -1,9 +1,15 @@
 // Host-side declarations of the library that need no HIP headers: variant
 // table, artifact parsing, and the candidate-list grids of the block search.
-// The grid cell arithmetic is written as constexpr functions, which the HIP
-// compiler also makes available to device code, so the encoder and the host
-// build of the grid checks evaluate the very same float32 expressions.
+// The grid cell arithmetic is written once, as functions the HIP compiler
+// builds for both host and device, so the encoder and the host build of the
+// grid checks evaluate the very same float32 expressions.
 #pragma once
+
+#if defined(__HIP__)
+#define FQ_HD __host__ __device__
+#else
+#define FQ_HD
+#endif
 
 #include <stddef.h>
 #include <stdint.h>
@@ -92,16 +98,17 @@ bool grid_plan(int k, int N, int last, int* G, int* G1);
 // Cells per unit length of a grid with G cells per dimension, in float32.
 inline float grid_scale(int G) { return (float)(G / (2.0 * GRID_R)); }
 
-// Whether a float32 coordinate lies inside the grid, and its cell along one
-// axis: (v + R) * scale truncated and clamped to [0, G - 1] (NaN maps to 0;
-// such a coordinate is never inside).  The encoder's cell of a block is
-// sum_t axis(z_t) G^t, taken only when every coordinate is inside.
-constexpr bool grid_inside(float v) { return v >= -(float)GRID_R && v < (float)GRID_R; }
-constexpr int grid_axis(float v, int G, float scale) {
-  float f = (v + (float)GRID_R) * scale;
-  f = f > 0.f ? f : 0.f;
-  f = f < (float)(G - 1) ? f : (float)(G - 1);
-  return (int)f;
+// Position of a float32 coordinate along one axis of a grid with G cells per
+// dimension (scale = grid_scale(G)), in cells from the grid's lower edge:
+// v * scale + R * scale with one rounding (a fused multiply-add).  The
+// coordinate lies inside the grid when the position is in [0, G) (false for
+// NaN), and then its cell is the position truncated to an integer.  The
+// encoder's cell of a block is sum_t cell(z_t) G^t, taken only when every
+// coordinate is inside.  Host and device evaluate the same correctly rounded
+// operations.
+FQ_HD inline float grid_pos(float v, float scale) {
+  return __builtin_fmaf(v, scale, (float)GRID_R * scale);
 }
+FQ_HD inline bool grid_pos_inside(float u, int G) { return u >= 0.f && u < (float)G; }
 
 }  // namespace fq

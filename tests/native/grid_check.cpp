@@ -18,7 +18,7 @@
 // each looked up twice, from its float32 rounding and from a float32 value
 // moved by up to 1e-5 per coordinate (ten times the encoder's bound on its
 // rotation error), with the encoder's own float32 cell arithmetic
-// (grid_inside / grid_axis from fq_host.h).  A cell without a list is fine
+// (grid_pos / grid_pos_inside from fq_host.h).  A cell without a list is fine
 // (the encoder then scans the whole codebook); a listed cell that misses the
 // nearest codeword is a failure.  It also checks the record layout and, when
 // asked, feeds corrupted artifacts to the parser (the sanitizer build).
@@ -157,8 +157,10 @@ Stats check_grid(const fq::GridTable& g, const std::vector<float>& C, int N, int
       bool inside = true;
       int cell = 0, mul = 1;
       for (int t = 0; t < dims; ++t) {
-        inside = inside && fq::grid_inside(zf[t]);
-        cell += fq::grid_axis(zf[t], G, scale) * mul;
+        const float u = fq::grid_pos(zf[t], scale);
+        const bool in = fq::grid_pos_inside(u, G);
+        inside = inside && in;
+        if (in) cell += (int)u * mul;
         mul *= G;
       }
       ++lookups;
