@@ -198,8 +198,9 @@ __device__ inline void prepare_column(ColPrep<K, RW>& cp, const float* zrow, boo
 }
 
 // Best and second-best t(n) = |c_n|^2 - 2 <z, c_n> over the cell's list (grid)
-// or the whole codebook (scan), and the gap test.
-template <int K, int S, int RW, bool GRID>
+// or the whole codebook (scan; NC > 0: unrolled for codebooks of NC entries),
+// and the gap test.
+template <int K, int S, int RW, bool GRID, int NC>
 __device__ inline void search_column(const ColPrep<K, RW>& cp, const float* sEnc, int N, float gv,
                                      float ez, int& i1out, bool& certain) {
   float m1 = INFINITY, m2 = INFINITY;
@@ -245,6 +246,15 @@ __device__ inline void search_column(const ColPrep<K, RW>& cp, const float* sEnc
       } else {
         visit(ea, (int)ia);
       }
+    }
+  } else if (NC > 0 && N == NC) {
+    // the whole codebook, with the trip count known at compile time (every
+    // lane reads the same rows: broadcast loads, constant indices)
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      float er[K + 1];
+      row((uint32_t)i, er);
+      visit(er, i);
     }
   } else {
 #pragma unroll 4
@@ -405,7 +415,7 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
         const bool live = c < NCF && v < nv;
         int i1;
         bool certain;
-        search_column<K, S, RW, GRID>(cp[q], sEnc, N, a.gv, a.ez, i1, certain);
+        search_column<K, S, RW, GRID, (BITS <= 4 ? (1 << BITS) : 0)>(cp[q], sEnc, N, a.gv, a.ez, i1, certain);
         record(c, live, v, b, i1, certain);
       }
     }
