@@ -59,6 +59,29 @@ template <int BITS>
 constexpr int enc_waves() { return BITS == 12 ? 12 : 8; }
 constexpr float SLACK = 1e-5f;  // covers |D~ - D| inside the square roots of the bound
 
+// Values of other lanes of the same 16-lane row through DPP: row_ror:8
+// (0x128), row_ror:4 (0x124), quad_perm [2,3,0,1] (0x4E) and [1,0,3,2]
+// (0xB1).  Each step combines a lane with a partner, so after the four steps
+// every lane of the row holds the reduction over all 16.
+template <int CTRL>
+__device__ inline int row_dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ inline double row_dpp(double v) {
+  int2 p = __builtin_bit_cast(int2, v);
+  p.x = row_dpp_i<CTRL>(p.x);
+  p.y = row_dpp_i<CTRL>(p.y);
+  return __builtin_bit_cast(double, p);
+}
+__device__ inline double row16_sum(double v) {
+  v += row_dpp<0x128>(v);
+  v += row_dpp<0x124>(v);
+  v += row_dpp<0x4E>(v);
+  v += row_dpp<0xB1>(v);
+  return v;
+}
+
 // 1 / sqrt(a) in float64 for a > 0 (infinity for 0, NaN for NaN): the hardware
 // estimate refined by two Newton steps y <- y + y (1 - a y^2) / 2, each of
 // which squares the relative error, so the result is within a few units in
@@ -469,7 +492,18 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
     wave_lds_sync();
 
     // ---- 5. exact float64 redo of uncertified columns: four at a time, one
-    //      per 16-lane group (lane i of a group holds coordinates 4i .. 4i + 3)
+    //      per 16-lane group (lane i of a group holds coordinates 4i .. 4i + 3).
+    //      Binary16 input is staged in LDS (the z rows are free now), so the
+    //      only global reads are the rows of Pi and the cell's record.
+    _Float16* sXh = reinterpret_cast<_Float16*>(sZ);   // [EV][64]
+    if constexpr (sizeof(TX) == 2) {
+      if (nfb > 0) {
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq)
+          *reinterpret_cast<half4*>(sXh + j * D + 16 * kq + 4 * g) = xf.hi[kq];
+        wave_lds_sync();
+      }
+    }
     for (int e0 = 0; e0 < nfb; e0 += 4) {
       const int l16 = lane & 15;
       const bool ok = e0 + g < nfb;
@@ -477,31 +511,33 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
       const bool last = c >= NCF;
       const int v = last ? c - NCF : c / NBF, b = last ? NB - 1 : c - (c / NBF) * NBF;
       const int rj = last ? Sh::LAST : K;
-      const TX* xr = xrow(base + v) + 4 * l16;
-      double xq[4];
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) xq[qq] = (double)xr[qq];
-      double ssd = 0.0;
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) ssd = fma(xq[qq], xq[qq], ssd);
-#pragma unroll
-      for (int m = 8; m >= 1; m >>= 1) ssd += shfl_xor_f64(ssd, m);
-      const double nuv = sqrt(ssd);
       double pr[K][4];
 #pragma unroll
       for (int t = 0; t < K; ++t)
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq)
           pr[t][qq] = t < rj ? a.pi64[(K * b + t < D ? K * b + t : D - 1) * D + 4 * l16 + qq] : 0.0;
+      double xq[4];
+      if constexpr (sizeof(TX) == 2) {
+        const half4 h = *reinterpret_cast<const half4*>(sXh + v * D + 4 * l16);
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) xq[qq] = (double)(float)h[qq];
+      } else {
+        const TX* xr = xrow(base + v) + 4 * l16;
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) xq[qq] = (double)xr[qq];
+      }
+      double ssd = 0.0;
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) ssd = fma(xq[qq], xq[qq], ssd);
+      const double inv = rsqrt_f64(row16_sum(ssd));   // 1 / |x|
       double zd[K];
 #pragma unroll
       for (int t = 0; t < K; ++t) {
         double sum = 0.0;
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) sum = fma(pr[t][qq], xq[qq], sum);
-#pragma unroll
-        for (int m = 8; m >= 1; m >>= 1) sum += shfl_xor_f64(sum, m);
-        zd[t] = sum / nuv;
+        zd[t] = row16_sum(sum) * inv;
       }
       double best = INFINITY;
       int bi = 0;
@@ -523,7 +559,7 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
       // codeword that can be nearest there: each lane takes every 16th one;
       // outside the grid (or for an over-full cell) scan the whole codebook
       int cnt = 0;
-      const uint16_t* rec = nullptr;
+      uint32_t mine = 0, mine2 = 0;   // this lane's list entries (read with the count)
       if constexpr (GRID) {
         const int dims = last ? 1 : K;
         bool inside = true;
@@ -539,19 +575,25 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
             cell += (in ? (int)u : 0) * mul;   // stays inside the table
             mul *= G;
           }
-        rec = (last ? a.grid1 : a.grid) + (size_t)cell * (2 * RW);
+        const uint16_t* rec = (last ? a.grid1 : a.grid) + (size_t)cell * (2 * RW);
         const uint32_t c0 = rec[0];
+        mine = rec[1 + (l16 < 2 * RW - 1 ? l16 : 2 * RW - 2)];
+        if constexpr (2 * RW - 1 > 16) mine2 = rec[1 + (l16 + 16 < 2 * RW - 1 ? l16 + 16 : 2 * RW - 2)];
         cnt = (inside && c0 != GRID_OVERFLOW) ? (int)c0 : 0;
       }
-      if (cnt > 0) {
-        for (int e = l16; e < cnt; e += 16) consider((int)rec[e + 1]);
+      if (cnt > 0) {   // a list holds at most 2 RW - 1 <= 31 entries
+        if (l16 < cnt) consider((int)mine);
+        if constexpr (2 * RW - 1 > 16)
+          if (l16 + 16 < cnt) consider((int)mine2);
       } else {
         for (int i = l16; i < N; i += 16) consider(i);
       }
 #pragma unroll
-      for (int m = 8; m >= 1; m >>= 1) {
-        const double ob = shfl_xor_f64(best, m);
-        const int oi = __shfl_xor(bi, m, 64);
+      for (int m = 0; m < 4; ++m) {   // the lowest index among the smallest distances
+        const double ob = m == 0 ? row_dpp<0x128>(best) : m == 1 ? row_dpp<0x124>(best)
+                        : m == 2 ? row_dpp<0x4E>(best) : row_dpp<0xB1>(best);
+        const int oi = m == 0 ? row_dpp_i<0x128>(bi) : m == 1 ? row_dpp_i<0x124>(bi)
+                     : m == 2 ? row_dpp_i<0x4E>(bi) : row_dpp_i<0xB1>(bi);
         if (ob < best || (ob == best && oi < bi)) {
           best = ob;
           bi = oi;

@@ -110,6 +110,27 @@ def test_nearest_matches_naive_loop(k, N):
     assert np.allclose(d2, np.sum((X - C[idx]) ** 2, axis=1), rtol=1e-12, atol=1e-15)
 
 
+def test_unit_distortion_partial_block_hand_worked():
+    # d = 4, k = 3: one full block and a one-coordinate last block [FQ 2.3:
+    # blocks of k coordinates, the last one shorter].  Codewords (0,0,0) and
+    # (1,0,0); blocks (0.4,5,5) and (0.6,5,5).  Full blocks: both at squared
+    # distance 50.16 (0.16 + 25 + 25 from the nearer codeword).  Last block
+    # (first coordinate only): 0.4 -> 0 and 0.6 -> 1, both 0.16.  So
+    # D = (nb - 1) e_full + e_part = 50.16 + 0.16.
+    C = np.array([[0.0, 0.0, 0.0], [1.0, 0.0, 0.0]])
+    X = np.array([[0.4, 5.0, 5.0], [0.6, 5.0, 5.0]])
+    D, e_full, e_part = codebook.unit_distortion(C, 4, X)
+    assert math.isclose(e_full, 50.16, rel_tol=1e-14)
+    assert math.isclose(e_part, 0.16, rel_tol=1e-12)
+    assert math.isclose(D, 50.32, rel_tol=1e-14)
+    # d = 7, k = 3: two full blocks, the last one of one coordinate
+    D7, _, _ = codebook.unit_distortion(C, 7, X)
+    assert math.isclose(D7, 2 * 50.16 + 0.16, rel_tol=1e-14)
+    # k divides d: no partial term
+    D6, e6, p6 = codebook.unit_distortion(C, 6, X)
+    assert p6 is None and math.isclose(D6, 2 * 50.16, rel_tol=1e-14)
+
+
 def test_lloyd_monotone_and_centroid_condition():
     X = source.sample_blocks(64, 2, 1 << 14, [14])
     C, hist = codebook.lloyd(codebook.initial_codebook(64, 2, 16), X, max_iter=400, tol=1e-13)
