@@ -14,7 +14,9 @@
 //     way), z~ = y / nu in float32, staged in LDS.
 //  3. block search: every (vector, block) column looks for
 //     argmin_n t(n) = |c_n|^2 - 2 <z~, c_n> (the distance without |z|^2) over
-//     the codebook, in float32, keeping the best and second-best value.
+//     the exact candidate list of its grid cell (k = 2, 3, and 4 with N >= 64;
+//     see fq_grid.cpp) or over the whole codebook, in float32, keeping the
+//     best and second-best value.
 //  4. certification: with D = t + |z|^2, the computed t of every codeword is
 //     within gv (sqrt D + 3|z|)^2 of its exact value at z~ (a chain of k
 //     float32 fused multiply-adds, each rounded once), and z~ is within ez of
@@ -25,8 +27,9 @@
 //     z and the result is final.
 //  5. otherwise (near ties, non-finite data, blocks outside the candidate
 //     grid) the block is redone exactly by 16 lanes: z's block in float64 from
-//     x and the float64 Pi, then all N codewords with sum_t (z_t - c_t)^2 in
-//     float64, ties to the lowest index.
+//     x and the float64 Pi, then sum_t (z_t - c_t)^2 in float64 over the
+//     candidates of that block's cell (all N codewords where the cell has no
+//     list), ties to the lowest index.
 //  For k = 3 the one-coordinate last block is searched on its coordinate
 //  computed exactly in float64 (the codewords' first coordinates are packed
 //  too closely for the float32 certificate to settle most of those blocks).
