@@ -224,8 +224,8 @@ __device__ inline void prepare_column(ColPrep<K, RW>& cp, const float* zrow, boo
 }
 
 // Best and second-best t(n) = |c_n|^2 - 2 <z, c_n> over the cell's list (grid)
-// or the whole codebook (scan; NC > 0: unrolled for codebooks of NC entries),
-// and the gap test.
+// or the whole codebook (scan; NC > 0: unrolled over the NC = N entries, as
+// every artifact holds N = 2^bits codewords), and the gap test.
 template <int K, int S, int RW, bool GRID, int NC>
 __device__ inline void search_column(const ColPrep<K, RW>& cp, const float* sEnc, int N, float gv,
                                      float ez, int& i1out, bool& certain) {
@@ -273,7 +273,7 @@ __device__ inline void search_column(const ColPrep<K, RW>& cp, const float* sEnc
         visit(ea, (int)ia);
       }
     }
-  } else if (NC > 0 && N == NC) {
+  } else if constexpr (NC > 0) {
     // the whole codebook, with the trip count known at compile time (every
     // lane reads the same rows: broadcast loads, constant indices)
 #pragma unroll
