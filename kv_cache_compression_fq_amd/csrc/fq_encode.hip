@@ -224,8 +224,8 @@ __device__ inline void prepare_column(ColPrep<K, RW>& cp, const float* zrow, boo
 }
 
 // Best and second-best t(n) = |c_n|^2 - 2 <z, c_n> over the cell's list (grid)
-// or the whole codebook (scan; NC > 0: unrolled over the NC = N entries, as
-// every artifact holds N = 2^bits codewords), and the gap test.
+// or the whole codebook (scan; NC > 0: a compile-time trip count of NC = N
+// entries, as every artifact holds N = 2^bits codewords), and the gap test.
 template <int K, int S, int RW, bool GRID, int NC>
 __device__ inline void search_column(const ColPrep<K, RW>& cp, const float* sEnc, int N, float gv,
                                      float ez, int& i1out, bool& certain) {
@@ -273,10 +273,20 @@ __device__ inline void search_column(const ColPrep<K, RW>& cp, const float* sEnc
         visit(ea, (int)ia);
       }
     }
-  } else if constexpr (NC > 0) {
-    // the whole codebook, with the trip count known at compile time (every
-    // lane reads the same rows: broadcast loads, constant indices)
+  } else if constexpr (NC > 0 && NC * (K + 1) <= 32) {
+    // a table of at most 32 floats: fully unrolled, so its rows (the same for
+    // every lane) stay in registers across the chunk's columns
 #pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      float er[K + 1];
+      row((uint32_t)i, er);
+      visit(er, i);
+    }
+  } else if constexpr (NC > 0) {
+    // the whole codebook with the trip count known at compile time, unrolled
+    // by four (fully unrolled, the compiler would keep every row live across
+    // the columns and spill)
+#pragma unroll 4
     for (int i = 0; i < NC; ++i) {
       float er[K + 1];
       row((uint32_t)i, er);
