@@ -112,7 +112,6 @@ struct EncShape {
   // u16 per staged index row: the NB indices, then zeros for the packer
   static constexpr int IP = (NB + pack_fields<BITS>()) / 2 * 2;
   static constexpr int NCOL = EV * NB;              // columns per chunk
-  static constexpr int CPL = (NCOL + 63) / 64;      // columns per lane
   static constexpr bool EXACT_LAST = LAST < K;      // one-coordinate last block
   static constexpr size_t WAVE_BYTES =
       ((size_t)EV * ZP * 4 + (EXACT_LAST ? EV * 8 : 0) + (size_t)EV * IP * 2 + (size_t)NCOL * 2 +
