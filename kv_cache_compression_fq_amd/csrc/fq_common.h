@@ -13,7 +13,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BUF_DWORD3 = 0x00020000;   // raw buffer descriptor word 3 (gfx9 family)
-constexpr int CPOL_NT = 2;               // buffer cache policy: non-temporal (streaming)
+constexpr int CPOL_NT_SC1 = 2 | 16;      // buffer cache policy: non-temporal (nt) at system scope (sc1)
 
 // Compile-time record shape of a (k, index bits) variant for d = 64.
 template <int K, int BITS>
