@@ -118,11 +118,14 @@ def measured_counters(op):
         f = line.split()
         if len(f) >= 6 and f[0] == "op" and f[1] == op:
             try:
-                vals = [None if v == "-" else float(v) for v in f[2:6]]
+                vals = [None if v in ("-", "nan") else float(v) for v in f[2:7]]
             except ValueError:
                 return None
-            return {"traffic_bytes": vals[0], "valu_busy_pct": vals[1],
-                    "valu_lanes_pct": vals[2], "mfma_busy_pct": vals[3]}
+            out = {"traffic_bytes": vals[0], "valu_busy_pct": vals[1],
+                   "valu_lanes_pct": vals[2], "mfma_busy_pct": vals[3]}
+            if len(vals) > 4 and vals[4] is not None:
+                out["executed_lane_ops_per_vector"] = vals[4]
+            return out
     return None
 
 
@@ -285,6 +288,11 @@ def main():
         e["full_scan_block_share"] = scan
         e["roofline"] = encode_roofline(k, N, e["vectors_per_s"], entries)
         e["counters"] = measured_counters(f"encode_k{k}N{N}")
+        if e["counters"] and "executed_lane_ops_per_vector" in e["counters"]:
+            # executed VALU work (counters) over the search's own work model
+            e["counters"]["executed_over_search_lane_ops"] = (
+                e["counters"]["executed_lane_ops_per_vector"] /
+                e["roofline"]["search_lane_ops_per_vector"])
         d = ops[f"decode_k{k}N{N}"]
         d["vectors_per_s"] = n / (d["ms_avg"] * 1e-3)
         d["bytes_per_vector"] = codec_bytes(k, N)
