@@ -38,7 +38,7 @@ MFMA_F16_PEAK_TFLOPS = 2500.0                      # dense binary16 matrix cores
 STEP_VARIANTS = [(8, 16), (4, 4), (3, 4096)]
 STRESS_STREAMS, STRESS_T = 256, 65536
 GPT2_VARIANTS = [(2, 16), (2, 64), (2, 256), (3, 512)]
-LARGE_VARIANTS = [(32, 4096), (64, 4096)]
+LARGE_VARIANTS = [(32, 4096), (64, 4096), (64, 16384)]
 L2, B2, H2, T2 = 12, 4, 12, 1024
 N_RAND = 1 << 20
 COPY_BYTES = 1 << 28
@@ -597,11 +597,13 @@ def fidelity(torch, fq, synth, dev, B=2, Hq=32, Hkv=4, T=4096, layers=(0, 11, 21
 
 
 def bench_large(torch, fq, synth, dev, steps, warmup):
-    """Encode and decode of the GPT-2-shaped cache with the k = 32 and k = 64, N = 4096 codes.
+    """Encode and decode of the GPT-2-shaped cache with the large-block codes:
+    k = 32 and k = 64 with N = 4096, and k = 64 with N = 16384 (30-bit packed
+    records, the 34.1x point).
 
-    The block search is a dense contraction here (4096 codewords of k
-    coordinates per block, 64 * 4096 multiply-adds per vector at either k), run
-    on the matrix cores: its roofline is the binary16 MFMA peak.  The kernel
+    The block search is a dense contraction here (N codewords of k coordinates
+    per block, 64 * N multiply-adds per vector at either k), run on the matrix
+    cores: its roofline is the binary16 MFMA peak.  The kernel
     forms every product twice (z split into binary16 hi and lo parts), so
     the algorithmic fraction reported here is at most one half.
     """

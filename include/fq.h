@@ -77,15 +77,16 @@ const char* fq_status_string(fq_status s);
  * The artifact holds the shared rotation Pi (float64, d x d, row-major,
  * z = Pi u) and the shared codebook C (float32, N x k): one offline codebook
  * for every layer and head [FQ 2.1] and one shared Haar rotation [FQ 1, 2.3].
- * Checks: magic, version, header size, d = 64, 1 <= k <= 64, N a power of two
- * with 2 <= N <= 4096, nb / idx_bits / record_words / last_block consistent,
- * total size, FNV-1a hash, finite values, max |Pi^T Pi - I| <= 1e-9.
- * Returns FQ_ERR_BAD_ARTIFACT for a malformed or corrupt blob,
- * FQ_ERR_UNSUPPORTED for a valid blob the kernels are not built for.  Built
- * (k, N): k = 2 with N in {16, 32, 64, 128, 256}; k = 3 with N in {512, 4096};
- * k = 4 with N in {4, 256}; k = 8 with N in {16, 256}; k = 32 and k = 64 with
- * N = 4096 (whose tables must hold binary16 values; fq_codebook_load returns
- * FQ_ERR_UNSUPPORTED otherwise).  `out` may be NULL.
+ * Checks: magic, version, header size, 1 <= d <= 4096, 1 <= k <= d, N a power
+ * of two with 2 <= N <= 2^20, nb / idx_bits / record_words / last_block
+ * consistent, total size, FNV-1a hash, finite values, max |Pi^T Pi - I| <=
+ * 1e-9.  Returns FQ_ERR_BAD_ARTIFACT for a malformed or corrupt blob,
+ * FQ_ERR_UNSUPPORTED for a valid blob the kernels are not built for (d != 64
+ * or a (k, N) outside this list).  Built (k, N): k = 2 with N in {16, 32, 64,
+ * 128, 256}; k = 3 with N in {512, 4096}; k = 4 with N in {4, 256}; k = 8
+ * with N in {16, 256}; k = 32 with N = 4096; k = 64 with N in {4096, 16384}
+ * (the k = 32 and 64 tables must hold binary16 values; fq_codebook_load
+ * returns FQ_ERR_UNSUPPORTED otherwise).  `out` may be NULL.
  */
 fq_status fq_artifact_check(const void* artifact, size_t nbytes, fq_info* out);
 
@@ -168,9 +169,10 @@ fq_status fq_decode(const fq_codebook* cb, const uint32_t* codes, const uint16_t
  * nb * idx_bits + 16: field j at record bits [j idx_bits, (j+1) idx_bits),
  * then the norm's 16 bits.  n records take ceil(n R / 32) words; bits past
  * the last record are 0.  Any record still decodes by address arithmetic
- * alone (bit offset r R).  For k = 64, N = 4096, R = 28 bits: 1024 / 28 =
- * 36.6 times smaller than the binary16 vector (the word-aligned layout plus
- * the separate norm stores 48 bits, 21.3 times).
+ * alone (bit offset r R).  For k = 64, R = 28 bits at N = 4096 (1024 / 28 =
+ * 36.6 times smaller than the binary16 vector) and 30 bits at N = 16384
+ * (34.1 times [FQ 4.2]); the word-aligned layout plus the separate norm
+ * stores 48 bits (21.3 times).
  *
  * fq_pack_records converts n word-aligned records and their norms (the
  * layout of fq_encode) into the packed stream.  codes 4-byte, norms 2-byte,

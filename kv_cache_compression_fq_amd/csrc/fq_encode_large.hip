@@ -1,35 +1,39 @@
 // FibQuant encode on the matrix cores (FibQuant technical summary, sections
 // 2.2 and 2.3): large blocks, k = 32 and k = 64 (one or two blocks per vector)
-// with N = 4096 codewords (the extreme rates below one bit per coordinate of
-// section 4), and k = 8 with N = 256 (one bit per coordinate; at the end of
+// with N = 4096 codewords, and k = 64 with N = 16384 (a 14-bit index: with the
+// 16-bit norm a 30-bit record, the most compressed point of the rate sweep of
+// section 4.2), and k = 8 with N = 256 (one bit per coordinate; at the end of
 // the file).
 //
 // The nearest-codeword search is a dense contraction here: every block is
-// compared with all 4096 codewords of k coordinates, 4096 k multiply-adds per
-// block, and the table (N k binary16 values, 256 or 512 KB) is larger than
+// compared with all N codewords of k coordinates, N k multiply-adds per
+// block, and the table (N k binary16 values, 256 KB to 2 MB) is larger than
 // LDS.  So the search runs on the matrix cores:
 //
 //  * One workgroup of 8 waves streams the codebook through LDS in stages of
-//    256 codewords (double-buffered, each stage loaded once per workgroup and
-//    shared by its 8 waves).  A wave holds 64 block columns (64 vectors at
-//    k = 64, 32 vectors at k = 32) as binary16 B operands, split
-//    z~ = z_hi + z_lo (both binary16, the lo part unscaled so it accumulates
-//    into the same sum), and for every tile of 16 codewords forms
+//    256 codewords with their -|c|^2 / 2 (double-buffered, each stage loaded
+//    once per workgroup and shared by its 8 waves).  A wave holds 64 block
+//    columns (64 vectors at k = 64, 32 vectors at k = 32) as binary16 B
+//    operands, split z~ = z_hi + z_lo (both binary16, the lo part unscaled
+//    so it accumulates into the same sum), and for every tile of 16 codewords
+//    forms
 //    s(n) = <c_n, z~> - |c_n|^2 / 2 with v_mfma_f32_16x16x32_f16, the
 //    accumulator starting at -|c_n|^2 / 2 (float32 from the host).  The
 //    nearest codeword maximises s.
 //  * Each lane keeps, for its 4 accumulator rows ("slots": the codewords
 //    16 t + 4 (lane / 16) + r of every tile t), the best and second-best key,
-//    where a key is the float32 score with its low 8 mantissa bits replaced by
-//    the tile number t, compared as a signed integer (the scores' order for
-//    scores >= 0).  The 16 slots of a column are merged at the end.
+//    where a key is the float32 score with its low TB mantissa bits replaced
+//    by the tile number t (TB = log2(N / 16): 8 bits for 4096 codewords, 10
+//    for 16384), compared as a signed integer (the scores' order for scores
+//    >= 0).  The 16 slots of a column are merged at the end.
 //  * Certification.  The computed score of every codeword is within
 //    E = EA |z~| + EB of its exact value at z~ (binary16 split of z~: 2^-22
 //    relative plus 2^-25 absolute per coordinate; float32 accumulation of
 //    2k + 2 terms, taken as one rounding of 2^-23 per term relative to the
 //    sum of their magnitudes; the rounded |c|^2 / 2), z~ is within ez of the
 //    exact z per coordinate, which moves a score difference by at most
-//    2 ez sqrt(k) max|c|, and a key is within 2^-15 of its score relative.
+//    2 ez sqrt(k) max|c|, and a key is within 2^(TB-23) of its score
+//    relative (so two keys' order is their scores' within 2^(TB-22)).
 //    A codeword whose key is more than M below the best key cannot be the
 //    exact nearest.  When the best key exceeds M, only the best slot is
 //    within M and no slot's second key is, the float32 winner is final.
@@ -42,8 +46,8 @@
 //    more than 8 candidates); ties go to the lowest index; the exact index
 //    replaces the field.  A list that could overflow during a pass is
 //    settled at the start of the pass instead.
-//  * Records (one 32-bit word: one or two 12-bit fields) and norms are
-//    written with coalesced stores.
+//  * Records (one 32-bit word: one or two 12-bit fields, or one 14-bit field)
+//    and norms are written with coalesced stores.
 #include "fq_common.h"
 #include "fq_encode_x.h"
 #include "fq_internal.h"
@@ -56,9 +60,6 @@ using namespace encx;
 constexpr int LW = 8;        // waves per workgroup
 constexpr int CG = 4;        // column groups of 16 per wave pass
 constexpr int TCW = 256;     // codewords per LDS stage
-constexpr int LBITS = 12;    // log2 N
-constexpr int LN = 1 << LBITS;
-constexpr int NSTAGE = LN / TCW;
 // Uncertain blocks listed per wave: row (2 words), block | count << 8 |
 // all-codewords flag << 16, hidden-slot mask, up to 8 candidate indices
 // (u16; more set the all-codewords flag).  A pass adds at most 64 entries,
@@ -67,8 +68,12 @@ constexpr int FL_MAX = 84;
 constexpr int FL_WORDS = 8;
 constexpr int FL_CAND = 8;
 
-template <int K>
+// LB = log2 N: 12 (k = 32, 64) or 14 (k = 64)
+template <int K, int LB>
 struct LShape {
+  static constexpr int LN = 1 << LB;               // codewords
+  static constexpr int NSTAGE = LN / TCW;          // LDS stages per sweep
+  static constexpr int TB = LB - 4;                // bits of a tile number (16 codewords a tile)
   static constexpr int NB = D / K;                 // blocks per vector (k divides d)
   static constexpr int KC = K / 32;                // 32-coordinate steps per block
   static constexpr int VPW = 16 * CG / NB;         // vectors per wave pass
@@ -76,7 +81,8 @@ struct LShape {
   static constexpr int STAGE_BYTES = TCW * K * 2;  // one stage of codebook fragments
   static constexpr int LOADS = STAGE_BYTES / (16 * LW * 64);   // 16-byte loads per thread
   static constexpr size_t WAVE_BYTES = (size_t)EV * ZP * 4 + 2 * 64 * 8 + FL_MAX * FL_WORDS * 4;
-  static constexpr size_t LDS = 2 * (size_t)STAGE_BYTES + LN * 4 + ROT_BYTES + LW * WAVE_BYTES + LW * 4;
+  static constexpr size_t HN_BYTES = 2 * TCW * 4;    // -|c|^2 / 2 of the two stages
+  static constexpr size_t LDS = 2 * (size_t)STAGE_BYTES + HN_BYTES + ROT_BYTES + LW * WAVE_BYTES + LW * 4;
 };
 
 struct LArgs {
@@ -102,15 +108,27 @@ __device__ inline double wave_sum_f64(double v) {
 
 // Keys compare as signed integers: the order of the float scores for scores
 // >= 0 (the only ones a certified or listed winner can have, see the margin
-// test), below every non-negative score otherwise.
-__device__ inline uint32_t key_tile(int key) { return (uint32_t)key & 0xFFu; }
+// test), below every non-negative score otherwise.  The low TB bits hold the
+// tile number.  Either form is one VALU instruction: a byte permute for
+// TB = 8; otherwise v_and_or_b32 with the mask held in a vector register (the
+// tile number is a scalar, and the instruction takes one scalar operand and
+// no literal).
+template <int TB>
+__device__ inline int make_key(float score, uint32_t tile, uint32_t vmask) {
+  if constexpr (TB == 8)
+    return (int)__builtin_amdgcn_perm(__float_as_uint(score), tile, 0x07060500u);
+  else
+    return (int)((__float_as_uint(score) & vmask) | tile);
+}
+template <int TB>
+__device__ inline uint32_t key_tile(int key) { return (uint32_t)key & ((1u << TB) - 1u); }
 __device__ inline float key_value(int key) { return __int_as_float(key); }
 
 // The exact nearest codeword of one listed block (the whole wave): z's block
 // in float64 from x and Pi (lane t < k holds z_t), then float64 distances to
 // the listed candidates, to every codeword 16 t + s of each hidden slot s,
 // or to all N codewords (binary16 table `cbt`, exact); ties to the lowest index.
-template <int K, typename TX, int NCW = LN>
+template <int K, typename TX, int NCW>
 __device__ int settle_block(const LArgs& a, const TX* x, const _Float16* cbt, const uint32_t* ent,
                             double* sX, double* sZd, int lane) {
   const int64_t row = (int64_t)((uint64_t)ent[0] | ((uint64_t)ent[1] << 32));
@@ -211,30 +229,31 @@ __device__ int settle_block(const LArgs& a, const TX* x, const _Float16* cbt, co
   return bi;
 }
 
-template <int K, typename TX>
+template <int K, int LB, typename TX>
 __global__ __launch_bounds__(LW * 64) void encode_large_kernel(LArgs a) {
-  using Sh = LShape<K>;
-  constexpr int NB = Sh::NB, KC = Sh::KC;
+  using Sh = LShape<K, LB>;
+  constexpr int NB = Sh::NB, KC = Sh::KC, LN = Sh::LN, NSTAGE = Sh::NSTAGE, TB = Sh::TB;
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* sStage = smem;                                           // 2 stages
-  float* sHn = reinterpret_cast<float*>(smem + 2 * Sh::STAGE_BYTES);      // [N]
-  _Float16* sRot = reinterpret_cast<_Float16*>(smem + 2 * Sh::STAGE_BYTES + LN * 4);
+  float* sHn = reinterpret_cast<float*>(smem + 2 * Sh::STAGE_BYTES);      // [2][TCW]
+  _Float16* sRot = reinterpret_cast<_Float16*>(smem + 2 * Sh::STAGE_BYTES + Sh::HN_BYTES);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  unsigned char* wb = smem + 2 * Sh::STAGE_BYTES + LN * 4 + ROT_BYTES + wave * Sh::WAVE_BYTES;
+  unsigned char* wb = smem + 2 * Sh::STAGE_BYTES + Sh::HN_BYTES + ROT_BYTES + wave * Sh::WAVE_BYTES;
   float* sZ = reinterpret_cast<float*>(wb);                               // [EV][ZP]
   double* sX = reinterpret_cast<double*>(wb + EV * ZP * 4);              // exact path: x
   double* sZd = sX + 64;                                                  // exact path: z block
   uint32_t* sList = reinterpret_cast<uint32_t*>(sZd + 64);                // uncertain blocks
-  int* sCount = reinterpret_cast<int*>(smem + 2 * Sh::STAGE_BYTES + LN * 4 + ROT_BYTES +
+  int* sCount = reinterpret_cast<int*>(smem + 2 * Sh::STAGE_BYTES + Sh::HN_BYTES + ROT_BYTES +
                                        LW * Sh::WAVE_BYTES);              // list lengths
   int nfl = 0;
   const int j = lane & 15, grp = lane >> 4;
 
   for (int i = threadIdx.x; i < ROT_BYTES / 16; i += blockDim.x)
     reinterpret_cast<u32x4*>(sRot)[i] = reinterpret_cast<const u32x4*>(a.rotfrag)[i];
-  for (int i = threadIdx.x; i < LN / 4; i += blockDim.x)
+  for (int i = threadIdx.x; i < TCW / 4; i += blockDim.x)
     reinterpret_cast<floatx4*>(sHn)[i] = reinterpret_cast<const floatx4*>(a.hn)[i];
   const u32x4* gfrag = reinterpret_cast<const u32x4*>(a.lfrag);
+  const u32x4* ghn = reinterpret_cast<const u32x4*>(a.hn);
   constexpr int STAGE_Q = Sh::STAGE_BYTES / 16;   // 16-byte pieces per stage
 #pragma unroll
   for (int u = 0; u < Sh::LOADS; ++u)
@@ -260,10 +279,10 @@ __global__ __launch_bounds__(LW * 64) void encode_large_kernel(LArgs a) {
 
   // settle one listed block and replace its field of the record
   auto settle_fix = [&](const uint32_t* ent) {
-    const int bi = settle_block<K, TX>(a, x, a.cbh, ent, sX, sZd, lane);
+    const int bi = settle_block<K, TX, LN>(a, x, a.cbh, ent, sX, sZd, lane);
     if (lane == 0) {
       const int64_t row = (int64_t)((uint64_t)ent[0] | ((uint64_t)ent[1] << 32));
-      const int sh = LBITS * (int)(ent[2] & 0xFFu);
+      const int sh = LB * (int)(ent[2] & 0xFFu);
       uint32_t* rp = a.codes + row;
       atomicAnd(rp, ~(((uint32_t)LN - 1u) << sh));
       atomicOr(rp, (uint32_t)bi << sh);
@@ -321,6 +340,8 @@ __global__ __launch_bounds__(LW * 64) void encode_large_kernel(LArgs a) {
 
     // ---- the codebook sweep
     int m1[CG][4], m2[CG][4];
+    uint32_t vmask = ~((1u << TB) - 1u);   // in a vector register: see make_key
+    asm volatile("" : "+v"(vmask));
 #pragma unroll
     for (int c = 0; c < CG; ++c)
 #pragma unroll
@@ -339,14 +360,20 @@ __global__ __launch_bounds__(LW * 64) void encode_large_kernel(LArgs a) {
             (__attribute__((address_space(3))) void*)(sStage + (sbuf ^ 1) * Sh::STAGE_BYTES + 16 * piece),
             16, 0, 0);
       }
+      if (wave == 0)   // the stage's -|c|^2 / 2: 64 lanes x 16 bytes
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(ghn + sn * (TCW / 4) + lane),
+            (__attribute__((address_space(3))) void*)(sHn + (sbuf ^ 1) * TCW), 16, 0, 0);
+      static_assert(TCW / 4 == 64, "one 16-byte piece per lane");
       const unsigned char* st = sStage + sbuf * Sh::STAGE_BYTES;
+      const float* hs = sHn + sbuf * TCW;
       // scores of codeword tile i (16 codewords) for the wave's 64 columns
       auto scores = [&](int i, floatx4 (&acc)[CG]) {
         half8 av[KC];
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc)
           av[kc] = *reinterpret_cast<const half8*>(st + ((i * KC + kc) * 64 + lane) * 16);
-        const floatx4 c0 = *reinterpret_cast<const floatx4*>(sHn + 16 * (16 * s + i) + 4 * grp);
+        const floatx4 c0 = *reinterpret_cast<const floatx4*>(hs + 16 * i + 4 * grp);
 #pragma unroll
         for (int c = 0; c < CG; ++c) acc[c] = c0;
 #pragma unroll
@@ -365,8 +392,7 @@ __global__ __launch_bounds__(LW * 64) void encode_large_kernel(LArgs a) {
         for (int c = 0; c < CG; ++c)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            // bytes 3..1 of the score, byte 0 = the tile number
-            const int key = (int)__builtin_amdgcn_perm(__float_as_uint(acc[c][r]), t, 0x07060500u);
+            const int key = make_key<TB>(acc[c][r], t, vmask);
             // median of the three (the canonical form of v_med3_i32)
             m2[c][r] = max(min(m1[c][r], m2[c][r]), min(max(m1[c][r], m2[c][r]), key));
             m1[c][r] = max(m1[c][r], key);
@@ -414,7 +440,7 @@ __global__ __launch_bounds__(LW * 64) void encode_large_kernel(LArgs a) {
         b1 = tk ? o1 : b1;
         r1 = tk ? r : r1;
       }
-      int n1 = 16 * (int)key_tile(b1) + 4 * grp + r1;
+      int n1 = 16 * (int)key_tile<TB>(b1) + 4 * grp + r1;
 #pragma unroll
       for (int m = 16; m <= 32; m <<= 1) {
         const int o1 = __shfl_xor(b1, m, 64), o2 = __shfl_xor(b2, m, 64);
@@ -427,7 +453,8 @@ __global__ __launch_bounds__(LW * 64) void encode_large_kernel(LArgs a) {
       const float bv = key_value(b1);
       const float zn = __builtin_amdgcn_sqrtf(zz[c]);
       const float E = fmaf(a.EA, zn, a.EB);
-      const float M = fmaf(2.f, E, fmaf(0x1p-14f, fabsf(bv), a.ZT)) * 1.0001f + 1e-12f;
+      constexpr float KEYREL = (float)(1u << TB) * 0x1p-22f;   // two keys' rounding, relative
+      const float M = fmaf(2.f, E, fmaf(KEYREL, fabsf(bv), a.ZT)) * 1.0001f + 1e-12f;
       const float lim = bv - M;
       int ncand = 0;
       bool hidden = false;
@@ -474,7 +501,7 @@ __global__ __launch_bounds__(LW * 64) void encode_large_kernel(LArgs a) {
               const int key = __builtin_amdgcn_readlane(m1[c][r], 16 * lg + jj);
               const int key2 = __builtin_amdgcn_readlane(m2[c][r], 16 * lg + jj);
               if (key_value(key) >= col_lim) {
-                if (lane == 0 && nc < FL_CAND) ce[nc] = (uint16_t)(16 * (int)key_tile(key) + 4 * lg + r);
+                if (lane == 0 && nc < FL_CAND) ce[nc] = (uint16_t)(16 * (int)key_tile<TB>(key) + 4 * lg + r);
                 ++nc;
               }
               if (key_value(key2) >= col_lim) hm |= 1u << (4 * lg + r);
@@ -503,7 +530,7 @@ __global__ __launch_bounds__(LW * 64) void encode_large_kernel(LArgs a) {
       const int h = grp & 1;
       const uint32_t f0 = (uint32_t)(h == 0 ? res[0] : res[2]);
       const uint32_t f1 = (uint32_t)(h == 0 ? res[1] : res[3]);
-      if (lane < 32 && vbase + lane < n) a.codes[vbase + lane] = f0 | (f1 << LBITS);
+      if (lane < 32 && vbase + lane < n) a.codes[vbase + lane] = f0 | (f1 << LB);
     }
   }
 
@@ -527,12 +554,12 @@ __global__ __launch_bounds__(LW * 64) void encode_large_kernel(LArgs a) {
 
 void set_bounds(LArgs& a, const fq_codebook* cb, int k, size_t xsize);
 
-template <int K, typename TX>
+template <int K, int LB, typename TX>
 hipError_t launch_large_k(const fq_codebook* cb, const TX* x, int64_t n, int64_t ld,
                           uint32_t* codes, uint16_t* norms, hipStream_t s) {
-  using Sh = LShape<K>;
-  if (cb->N != LN || cb->t.lfrag == nullptr || cb->t.hnorm == nullptr) return hipErrorInvalidValue;
-  auto kern = encode_large_kernel<K, TX>;
+  using Sh = LShape<K, LB>;
+  if (cb->N != Sh::LN || cb->t.lfrag == nullptr || cb->t.hnorm == nullptr) return hipErrorInvalidValue;
+  auto kern = encode_large_kernel<K, LB, TX>;
   const size_t shm = Sh::LDS;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
@@ -738,7 +765,7 @@ __global__ __launch_bounds__(EW * 64, 3) void encode_k8_kernel(LArgs a) {
           b1 = tk ? o1 : b1;
           r1 = tk ? r : r1;
         }
-        int n1 = 16 * (int)key_tile(b1) + 4 * grp + r1;
+        int n1 = 16 * (int)key_tile<8>(b1) + 4 * grp + r1;
         // a swap hands each lane its partner's triple beside its own (in
         // either order); the merge is symmetric, so both lanes agree
         auto merge = [&](auto q1, auto q2, auto qn) {
@@ -801,7 +828,7 @@ __global__ __launch_bounds__(EW * 64, 3) void encode_k8_kernel(LArgs a) {
                 const int key = __builtin_amdgcn_readlane(m1[c][r], 16 * lg + jj);
                 const int key2 = __builtin_amdgcn_readlane(m2[c][r], 16 * lg + jj);
                 if (key_value(key) >= col_lim) {
-                  if (lane == 0 && nc < FL_CAND) ce[nc] = (uint16_t)(16 * (int)key_tile(key) + 4 * lg + r);
+                  if (lane == 0 && nc < FL_CAND) ce[nc] = (uint16_t)(16 * (int)key_tile<8>(key) + 4 * lg + r);
                   ++nc;
                 }
                 if (key_value(key2) >= col_lim) hm |= 1u << (4 * lg + r);
@@ -892,12 +919,14 @@ hipError_t launch_encode_large(const fq_codebook* cb, const void* x, fq_dtype xt
                                int64_t ld, uint32_t* codes, uint16_t* norms, hipStream_t s) {
   if (xt == FQ_F16) {
     const _Float16* xx = static_cast<const _Float16*>(x);
-    if (cb->k == 32) return launch_large_k<32, _Float16>(cb, xx, n, ld, codes, norms, s);
-    if (cb->k == 64) return launch_large_k<64, _Float16>(cb, xx, n, ld, codes, norms, s);
+    if (cb->k == 32 && cb->bits == 12) return launch_large_k<32, 12, _Float16>(cb, xx, n, ld, codes, norms, s);
+    if (cb->k == 64 && cb->bits == 12) return launch_large_k<64, 12, _Float16>(cb, xx, n, ld, codes, norms, s);
+    if (cb->k == 64 && cb->bits == 14) return launch_large_k<64, 14, _Float16>(cb, xx, n, ld, codes, norms, s);
   } else {
     const float* xx = static_cast<const float*>(x);
-    if (cb->k == 32) return launch_large_k<32, float>(cb, xx, n, ld, codes, norms, s);
-    if (cb->k == 64) return launch_large_k<64, float>(cb, xx, n, ld, codes, norms, s);
+    if (cb->k == 32 && cb->bits == 12) return launch_large_k<32, 12, float>(cb, xx, n, ld, codes, norms, s);
+    if (cb->k == 64 && cb->bits == 12) return launch_large_k<64, 12, float>(cb, xx, n, ld, codes, norms, s);
+    if (cb->k == 64 && cb->bits == 14) return launch_large_k<64, 14, float>(cb, xx, n, ld, codes, norms, s);
   }
   return hipErrorInvalidValue;
 }

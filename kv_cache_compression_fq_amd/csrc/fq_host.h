@@ -21,7 +21,7 @@
 namespace fq {
 
 constexpr int D = 64;             // vector length handled by the kernels
-constexpr int MAX_N = 4096;       // largest codebook
+constexpr int MAX_N = 16384;      // largest codebook (k = 64)
 constexpr int MAX_WORDS = 12;     // record words for k >= 2, N <= 4096: ceil(32*12/32)
 constexpr int MAX_QUERIES = 8;    // queries per head in one attention call
 
@@ -31,10 +31,11 @@ constexpr int MAX_QUERIES = 8;    // queries per head in one attention call
 #define FQ_VARIANTS(X) \
   X(2, 4) X(2, 5) X(2, 6) X(2, 7) X(2, 8) X(3, 9) X(3, 12) X(4, 2) X(4, 8) X(8, 4) X(8, 8)
 
-// Large blocks (k = d/2 and k = d, N = 4096): the table exceeds LDS, so they
-// have their own encode kernel (fq_encode_large.hip) and a decode that gathers
-// codewords from the L2-resident table.
-#define FQ_VARIANTS_LARGE(X) X(32, 12) X(64, 12)
+// Large blocks (k = d/2 and k = d with N = 4096, and k = d with N = 16384):
+// the table exceeds LDS, so they have their own encode kernel
+// (fq_encode_large.hip) and a decode that gathers codewords from the
+// L2-resident table.
+#define FQ_VARIANTS_LARGE(X) X(32, 12) X(64, 12) X(64, 14)
 
 inline bool variant_supported(int k, int bits) {
 #define FQ_IS(KK, BB) if (k == KK && bits == BB) return true;

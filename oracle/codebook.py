@@ -142,7 +142,7 @@ def nearest(C, X):
     idx = np.empty(X.shape[0], dtype=np.int64)
     d2 = np.empty(X.shape[0], dtype=np.float64)
     cc = np.sum(C * C, axis=1)
-    chunk = 1 << 15
+    chunk = max(1 << 10, min(1 << 15, (1 << 27) // C.shape[0]))   # <= 1 GB per product
     for s in range(0, X.shape[0], chunk):
         xs = X[s:s + chunk]
         part = cc[None, :] - 2.0 * (xs @ C.T)

@@ -10,7 +10,7 @@ if ROOT not in sys.path:
 CODEBOOK_DIR = os.path.join(ROOT, "kv_cache_compression_fq_amd", "codebooks")
 GOLDEN_DIR = os.path.join(ROOT, "tests", "golden")
 VARIANTS = [(2, 16), (2, 64), (2, 256), (3, 512), (4, 256), (8, 256), (8, 16), (4, 4), (3, 4096),
-            (2, 32), (2, 128), (32, 4096), (64, 4096)]
+            (2, 32), (2, 128), (32, 4096), (64, 4096), (64, 16384)]
 
 
 def pytest_configure(config):

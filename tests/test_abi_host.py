@@ -91,6 +91,10 @@ def test_unsupported_but_valid_artifacts():
     assert st == UNS and info["nb"] == 13
     st, info = fq.fq_artifact_check(make_book(2, 8192))
     assert st == UNS
+    # 14-bit indices are built for k = 64 only; 15 bits for none
+    assert fq.fq_artifact_check(make_book(32, 16384))[0] == UNS
+    st, info = fq.fq_artifact_check(make_book(64, 32768))
+    assert st == UNS and info["idx_bits"] == 15
 
 
 def test_null_arguments_rejected_without_device():

@@ -103,9 +103,10 @@ def test_encode_variants_fp16(dev, k, N):
     print(f"k{k}N{N}: {ex} exact, {win} in window")
 
 
-@pytest.mark.parametrize("k,N", [(8, 256), (32, 4096), (64, 4096)])
+@pytest.mark.parametrize("k,N", [(8, 256), (32, 4096), (64, 4096), (64, 16384)])
 def test_encode_large_blocks_fp32_and_tiny(dev, k, N):
-    """The matrix-core searches (k = 8 with N = 256; k = 32 / 64 with N = 4096):
+    """The matrix-core searches (k = 8 with N = 256; k = 32 / 64 with N = 4096;
+    k = 64 with N = 16384):
     float32 input with the special vectors, then inputs shorter than one wave's
     share (5 rows) and one row past a workgroup's share (513 rows)."""
     art, cb = book(k, N)
@@ -119,7 +120,7 @@ def test_encode_large_blocks_fp32_and_tiny(dev, k, N):
     print(f"k{k}N{N} fp32: {ex} exact, {win} in window")
 
 
-@pytest.mark.parametrize("k,N", [(8, 256), (32, 4096), (64, 4096)])
+@pytest.mark.parametrize("k,N", [(8, 256), (32, 4096), (64, 4096), (64, 16384)])
 def test_encode_large_blocks_many_uncertain(dev, k, N):
     """Runs of zero vectors (every block uncertain: all codewords scanned,
     index 0) between ordinary rows, more than one pass's worth per wave, so
@@ -200,7 +201,7 @@ def test_decode_variants(dev, k, N, ydt):
     print(f"k{k}N{N} {ydt}: max err/nu {np.max(err / np.maximum(nu16, 1e-30)):.2e}")
 
 
-@pytest.mark.parametrize("kb", [(4, 256), (64, 4096), (3, 512)])
+@pytest.mark.parametrize("kb", [(4, 256), (64, 4096), (3, 512), (64, 16384)])
 def test_random_access_decode(dev, kb):
     art, cb = book(*kb)
     x = synth.kv_slab(3, 0, 0, 4, 1, 500).reshape(-1, 64)
@@ -225,7 +226,8 @@ def test_random_access_decode(dev, kb):
 
 
 # ----------------------------------------------------------- packed records
-@pytest.mark.parametrize("k,N", [(64, 4096), (32, 4096), (8, 16), (2, 16), (3, 512), (3, 4096)])
+@pytest.mark.parametrize("k,N", [(64, 4096), (32, 4096), (8, 16), (2, 16), (3, 512), (3, 4096),
+                                 (64, 16384)])
 def test_pack_records_bit_exact(dev, k, N):
     """fq_pack_records of uniform random records and norms equals the oracle's
     packed stream bit for bit (ragged counts), and writes nothing past it."""
@@ -244,7 +246,7 @@ def test_pack_records_bit_exact(dev, k, N):
         assert np.array_equal(host(pv, np.uint32), want), (k, N, n)
 
 
-@pytest.mark.parametrize("k,N", [(64, 4096), (32, 4096), (8, 16), (3, 4096), (2, 64)])
+@pytest.mark.parametrize("k,N", [(64, 4096), (32, 4096), (8, 16), (3, 4096), (2, 64), (64, 16384)])
 def test_decode_packed_contiguous_and_random_access(dev, k, N):
     """Encode, pack, decode from the packed stream: every row equals the
     word-aligned decode of the same codes bit for bit, and the oracle's decode
@@ -462,6 +464,49 @@ def test_decode_step_off_grid_codebook(dev):
                                 0.125, pos + M)
     rel = np.linalg.norm(got - ref, axis=-1) / np.linalg.norm(ref, axis=-1)
     assert np.max(rel) <= 2e-3
+
+
+OFF_GRID = [(2, 64), (3, 512), (4, 256), (8, 256), (8, 16), (4, 4), (3, 4096)]
+
+
+@pytest.mark.parametrize("k,N", OFF_GRID)
+def test_off_grid_codebooks(dev, k, N):
+    """Tables that are not on the binary16 grid (the shipped ones are, reading
+    of the table precision): each shipped table scaled by 1 + 1e-4 sin(i) per
+    entry.  Encode (candidate lists rebuilt for the new table; for k = 8 with
+    N = 256 the vector-unit scan instead of the matrix-core search, which
+    needs a binary16 table) against the oracle on the same float32 table,
+    decode (binary16 copy of the table: within the 1e-3 nu bar) and, where
+    the attention kernels take the variant, attention over random records
+    (hi / lo table path) against the oracle's decompress-then-attend."""
+    art = artifact.read_artifact(open(artifact_path(k, N), "rb").read())
+    C = art["C"].astype(np.float64)
+    C = (C * (1.0 + 1e-4 * np.sin(np.arange(C.size)).reshape(C.shape))).astype(np.float32)
+    assert not np.array_equal(C.astype(np.float16).astype(np.float32), C)
+    art2 = dict(art)
+    art2["C"] = C
+    blob = artifact.write_artifact(art["Pi"], art2)
+    ref = artifact.read_artifact(blob)
+    cb = fq.fq_codebook_load(blob, 0)
+    x = np.concatenate([synth.kv_slab(3, 5, 0, 2, 3, 400).reshape(-1, 64), synth.special_vectors()])
+    codes, norms = gpu_encode(cb, x, dev)
+    ex, win = check_encode(ref, x, codes, norms)
+    y = fq.fq_decode(cb, to_dev(codes, dev, np.int32), to_dev(norms, dev, np.int16))
+    torch.cuda.synchronize()
+    check_decode_full(ref, codes, norms, y.cpu().numpy(), f"off-grid k{k}N{N}")
+    if (k, N) != (3, 4096):      # the 4096-entry table exceeds the attention kernels' LDS
+        B, Hq, Hkv, T = 2, 8, 2, 520
+        bits = cb.nb * cb.info["idx_bits"]
+        kw = synth.random_records((B, Hkv, T), cb.W, bits, 71)
+        vw = synth.random_records((B, Hkv, T), cb.W, bits, 72)
+        kn = synth.random_norms((B, Hkv, T), 73)
+        vn = synth.random_norms((B, Hkv, T), 74)
+        q = synth.query(B, Hq, seed=75)
+        got = run_attention(dev, q, kw, kn, vw, vn, cb, cb)
+        want = attend.attend(q, kw, kn, vw, vn, ref["Pi"], ref["C"], ref["C"], 0.125)
+        rel = np.linalg.norm(got - want, axis=-1) / np.linalg.norm(want, axis=-1)
+        assert np.max(rel) <= 2e-3, float(np.max(rel))
+    print(f"off-grid k{k}N{N}: {ex} exact, {win} in window", flush=True)
 
 
 def test_decode_step_large_append(dev):
@@ -710,13 +755,13 @@ def test_gpt2_cache_full_size(dev, k, N):
     check_decode_full(art, c_np, n_np, host(yv, np.float16), f"gpt2 k{k}N{N}")
 
 
-@pytest.mark.parametrize("k", [32, 64])
-def test_large_blocks_gpt2_cache_full_size(dev, k):
-    """k = 32 / 64, N = 4096 on the whole GPT-2-small-shaped cache: every row
-    against the oracle (each costs 4096 * 64 float64 multiply-adds there),
-    every norm and pad bit, every decoded vector."""
-    print(f"gpt2 cache k{k}N4096", flush=True)
-    art, cb = book(k, 4096)
+@pytest.mark.parametrize("k,N", [(32, 4096), (64, 4096), (64, 16384)])
+def test_large_blocks_gpt2_cache_full_size(dev, k, N):
+    """k = 32 / 64 with N = 4096 and k = 64 with N = 16384 on the whole
+    GPT-2-small-shaped cache: every row against the oracle (each costs N * 64
+    float64 multiply-adds there), every norm and pad bit, every decoded vector."""
+    print(f"gpt2 cache k{k}N{N}", flush=True)
+    art, cb = book(k, N)
     x = gpt2_cache()
     n = len(x)
     codes, norms, (cw, nw) = canary_codec_outputs(cb, n, dev)
@@ -726,17 +771,18 @@ def test_large_blocks_gpt2_cache_full_size(dev, k):
     torch.cuda.synchronize()
     assert canary_intact(cw, n) and canary_intact(nw, n) and canary_intact(yw, n)
     c_np, n_np = host(codes, np.uint32), host(norms, np.uint16)
-    check_rows_full(art, x, c_np, n_np, f"gpt2 k{k}N4096 (all rows)")
-    check_decode_full(art, c_np, n_np, host(yv, np.float16), f"gpt2 k{k}N4096")
+    check_rows_full(art, x, c_np, n_np, f"gpt2 k{k}N{N} (all rows)")
+    check_decode_full(art, c_np, n_np, host(yv, np.float16), f"gpt2 k{k}N{N}")
 
 
-@pytest.mark.parametrize("k", [32, 64])
-def test_packed_records_gpt2_cache_full_size(dev, k):
-    """The 36.6x (k = 64) and 25.6x (k = 32) packed form of the whole GPT-2-shaped
-    cache: packed stream equal to the oracle's packing of the GPU's codes, every
-    vector decoded from it equal to the word-aligned decode bit for bit."""
-    print(f"gpt2 cache k{k}N4096 packed", flush=True)
-    art, cb = book(k, 4096)
+@pytest.mark.parametrize("k,N", [(32, 4096), (64, 4096), (64, 16384)])
+def test_packed_records_gpt2_cache_full_size(dev, k, N):
+    """The 25.6x (k = 32), 36.6x (k = 64, N = 4096) and 34.1x (k = 64,
+    N = 16384) packed forms of the whole GPT-2-shaped cache: packed stream equal
+    to the oracle's packing of the GPU's codes, every vector decoded from it
+    equal to the word-aligned decode bit for bit."""
+    print(f"gpt2 cache k{k}N{N} packed", flush=True)
+    art, cb = book(k, N)
     x = gpt2_cache()
     n = len(x)
     codes, norms = fq.fq_encode(cb, to_dev(x, dev))
@@ -751,7 +797,7 @@ def test_packed_records_gpt2_cache_full_size(dev, k):
                              host(norms, np.uint16), art["bits"])
     assert np.array_equal(host(pv, np.uint32), want)
     assert torch.equal(y1, y2)
-    print(f"PARITY gpt2 k{k}N4096 packed rows={n} bits_per_vector={cb.packed_bits} "
+    print(f"PARITY gpt2 k{k}N{N} packed rows={n} bits_per_vector={cb.packed_bits} "
           f"compression={1024 / cb.packed_bits:.1f}x", flush=True)
 
 

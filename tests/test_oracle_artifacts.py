@@ -102,7 +102,7 @@ def test_sub_one_bit_band(k, N):
     assert 0.5 <= a["D_test"] < 1.0
 
 
-@pytest.mark.parametrize("k,N", [(2, 16), (2, 256), (3, 512), (32, 4096), (64, 4096)])
+@pytest.mark.parametrize("k,N", [(2, 16), (2, 256), (3, 512), (32, 4096), (64, 4096), (64, 16384)])
 def test_recorded_distortion_reproduces(k, N):
     a = load(k, N)
     C = a["C"].astype(np.float64)
@@ -123,6 +123,10 @@ def test_large_block_codes():
     D32, D64 = load(32, 4096)["D_test"], load(64, 4096)["D_test"]
     assert D32 < D64 < 1.0
     assert D32 > load(8, 256)["D_test"]
+    # the 14-bit whole-vector code sits between them in rate (0.1875 < 14/64 <
+    # 0.375 bits per coordinate) and so in distortion
+    D64b = load(64, 16384)["D_test"]
+    assert D32 < D64b < D64
     # the nearest-codeword search of the large tables (matrix-product form)
     # against plain squared distances on a tiny input
     C = load(64, 4096)["C"].astype(np.float64)
