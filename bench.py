@@ -175,6 +175,10 @@ def encode_roofline(k, N, vps, entries):
             "valu_limit_vectors_per_s": lim_valu, "hbm_limit_vectors_per_s": lim_hbm}
 
 
+# the configurations timed outside the step, in the order they run
+EXTRAS = ["copy_ceiling", "gpt2_step", "large_k", "attend_tinyllama", "configs"]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -188,6 +192,9 @@ def main():
                     help="skip the attention-fidelity sweep over the rates")
     ap.add_argument("--no-extras", action="store_true",
                     help="time the step only (no other configurations, no copy ceiling)")
+    ap.add_argument("--extras", default=",".join(EXTRAS),
+                    help="comma-separated subset of the other configurations to time: "
+                         + ", ".join(EXTRAS))
     ap.add_argument("--attend-layers", type=int, default=22)
     ap.add_argument("--attend-steps", type=int, default=10)
     ap.add_argument("--cost-sample", type=int, default=1 << 15,
@@ -339,13 +346,20 @@ def main():
     torch.cuda.empty_cache()
 
     extras = {}
-    if not a.no_extras:
+    chosen = set() if a.no_extras else {e.strip() for e in a.extras.split(",") if e.strip()}
+    unknown = chosen - set(EXTRAS)
+    if unknown:
+        raise SystemExit(f"unknown --extras {sorted(unknown)}; choose from {EXTRAS}")
+    if "copy_ceiling" in chosen:
         extras["copy_ceiling"] = copy_ceiling(torch, dev)
+    if "gpt2_step" in chosen:
         extras["gpt2_step"] = bench_gpt2(torch, fq, synth, dev, a.steps, a.warmup)
+    if "large_k" in chosen:
         extras["large_k"] = bench_large(torch, fq, synth, dev, a.steps, a.warmup)
-        if a.attend_layers > 0:
-            extras["attend_tinyllama"] = bench_attend(torch, fq, synth, dev, a.attend_layers,
-                                                      a.attend_steps, a.warmup)
+    if "attend_tinyllama" in chosen and a.attend_layers > 0:
+        extras["attend_tinyllama"] = bench_attend(torch, fq, synth, dev, a.attend_layers,
+                                                  a.attend_steps, a.warmup)
+    if "configs" in chosen:
         extras["configs"] = bench_configs(torch, fq, synth, dev)
     if not a.no_fidelity:
         extras["fidelity"] = fidelity(torch, fq, synth, dev)
