@@ -58,11 +58,19 @@ struct XRaw<float> {
   floatx4 q[4];
 };
 
-template <typename TX>
+// Each input row is read exactly once.  NT = true marks the loads
+// non-temporal, so the input stream does not evict other data from L2.
+template <typename TX, bool NT = false>
 __device__ inline void load_raw(const TX* xr, int g, XRaw<TX>& r) {
+  using Q = std::remove_reference_t<decltype(r.q[0])>;
 #pragma unroll
-  for (int kq = 0; kq < 4; ++kq)
-    r.q[kq] = *reinterpret_cast<const std::remove_reference_t<decltype(r.q[0])>*>(xr + 16 * kq + 4 * g);
+  for (int kq = 0; kq < 4; ++kq) {
+    const Q* p = reinterpret_cast<const Q*>(xr + 16 * kq + 4 * g);
+    if constexpr (NT)
+      r.q[kq] = __builtin_nontemporal_load(p);
+    else
+      r.q[kq] = *p;
+  }
 }
 
 template <typename TX>
