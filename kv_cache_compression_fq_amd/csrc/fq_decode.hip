@@ -34,9 +34,59 @@ constexpr int TILE = 16;           // vectors per MFMA tile
 constexpr int CHUNK = 64;          // vectors per wave iteration (one lane per record)
 constexpr int OUT_PITCH = D + 8;   // LDS row (elements) of the transpose buffer
 
+// k = 3: a record is expanded once, when staged, into its 64 binary16
+// coordinates (row pitch ZR_PITCH elements), so the product reads one 16-byte
+// piece per operand instead of gathering eight coordinates one by one; the
+// LDS table then holds each codeword padded to four entries (8 bytes).
+constexpr int ZR_PITCH = D + 8;
+template <int K>
+constexpr bool expand_rows() { return K == 3; }
+template <int K>
+constexpr int table_k() { return expand_rows<K>() ? 4 : K; }
+
+template <int K, int BITS>
+constexpr size_t stage_bytes() {
+  return expand_rows<K>() ? (size_t)CHUNK * ZR_PITCH * 2 : (size_t)CHUNK * Shape<K, BITS>::IDX_PITCH * 2;
+}
+
 template <int K, int BITS, typename TY>
 constexpr size_t wave_lds() {
-  return CHUNK * Shape<K, BITS>::IDX_PITCH * 2 + CHUNK * 4 + TILE * OUT_PITCH * sizeof(TY);
+  return stage_bytes<K, BITS>() + CHUNK * 4 + TILE * OUT_PITCH * sizeof(TY);
+}
+
+// Record fields -> the vector's 64 binary16 coordinates in LDS row `row`
+// (k = 3: 21 blocks of three and a last block of one).  Codeword i sits at
+// tab[4 i .. 4 i + 2]; output word w holds coordinates 2 w and 2 w + 1, each
+// taken with one byte permute from the codeword registers that hold them.
+template <int K, int BITS, int W>
+__device__ inline void expand_record(const uint32_t (&w)[W], const _Float16* tab, _Float16* row) {
+  constexpr int NB = Shape<K, BITS>::NB;
+  constexpr uint32_t MASK = (1u << BITS) - 1u;
+  uint32_t c[NB][2];   // c[j][0] = coordinates 0, 1 of block j; c[j][1] = coordinate 2
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int pos = j * BITS, wi = pos >> 5, o = pos & 31;
+    uint32_t v = w[wi] >> o;
+    if (o + BITS > 32) v |= w[wi + 1] << (32 - o);
+    const uint2 cw = *reinterpret_cast<const uint2*>(tab + (v & MASK) * 4);
+    c[j][0] = cw.x;
+    c[j][1] = cw.y;
+  }
+  u32x4* out = reinterpret_cast<u32x4*>(row);
+#pragma unroll
+  for (int q = 0; q < D / 8; ++q) {
+    uint32_t wd[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int c0 = 8 * q + 2 * h, c1 = c0 + 1;   // coordinates of this word
+      const int j0 = c0 / K, t0 = c0 % K, j1 = c1 / K, t1 = c1 % K;
+      const uint32_t a = c[j0][t0 >> 1], b = c[j1][t1 >> 1];
+      const uint32_t alo = (t0 & 1) ? 2u : 0u, blo = (t1 & 1) ? 2u : 0u;
+      // bytes 0-3 select from a, 4-7 from b
+      wd[h] = __builtin_amdgcn_perm(b, a, alo | (alo + 1) << 8 | (4 + blo) << 16 | (5 + blo) << 24);
+    }
+    out[q] = u32x4{wd[0], wd[1], wd[2], wd[3]};
+  }
 }
 
 template <int W>
@@ -206,17 +256,26 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
   constexpr bool GTAB = large_block(K);
   extern __shared__ __align__(16) unsigned char smem[];
   _Float16* sCbh = reinterpret_cast<_Float16*>(smem);
-  const size_t cb_bytes = GTAB ? 0 : ((size_t)N * K * sizeof(_Float16) + 15) / 16 * 16;
+  constexpr int TK = table_k<K>();
+  const size_t cb_bytes = GTAB ? 0 : ((size_t)N * TK * sizeof(_Float16) + 15) / 16 * 16;
   // the wave index is uniform: keep it (and the buffer descriptors derived from
   // it) in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   unsigned char* wbase = smem + cb_bytes + (size_t)wave * wave_lds<K, BITS, TY>();
-  uint16_t* sIdx = reinterpret_cast<uint16_t*>(wbase);                       // [CHUNK][IDX_PITCH]
-  float* sNu = reinterpret_cast<float*>(wbase + CHUNK * Sh::IDX_PITCH * 2);  // [CHUNK]
-  TY* sOut = reinterpret_cast<TY*>(wbase + CHUNK * Sh::IDX_PITCH * 2 + CHUNK * 4);
+  uint16_t* sIdx = reinterpret_cast<uint16_t*>(wbase);   // [CHUNK][IDX_PITCH] (or k = 3: rows)
+  _Float16* sZr = reinterpret_cast<_Float16*>(wbase);    // k = 3: [CHUNK][ZR_PITCH]
+  float* sNu = reinterpret_cast<float*>(wbase + stage_bytes<K, BITS>());   // [CHUNK]
+  TY* sOut = reinterpret_cast<TY*>(wbase + stage_bytes<K, BITS>() + CHUNK * 4);
 
-  if constexpr (!GTAB)
+  if constexpr (expand_rows<K>()) {
+    for (int i = threadIdx.x; i < N; i += DEC_THREADS) {
+      const _Float16 z = (_Float16)0.f;
+      const half4 h = {cbh_g[i * K], cbh_g[i * K + 1], cbh_g[i * K + 2], z};
+      *reinterpret_cast<half4*>(sCbh + i * 4) = h;
+    }
+  } else if constexpr (!GTAB) {
     for (int e = threadIdx.x; e < N * K; e += DEC_THREADS) sCbh[e] = cbh_g[e];
+  }
   // A operands: Pi^T as 16 x 32 fragments, [mt][s] = Pi[32 s + 8 grp + e][16 mt + col]
   half8 pa[4][2];
   const int col = lane & 15, grp = lane >> 4;
@@ -253,7 +312,10 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
       load_chunk<W>(t, c, lane, codes, norms, n);
   };
   auto stage = [&](const ChunkRegs<W>& t) {
-    unpack_record<K, BITS, W>(t.w, sIdx + lane * Sh::IDX_PITCH);
+    if constexpr (expand_rows<K>())
+      expand_record<K, BITS, W>(t.w, sCbh, sZr + lane * ZR_PITCH);
+    else
+      unpack_record<K, BITS, W>(t.w, sIdx + lane * Sh::IDX_PITCH);
     sNu[lane] = f16_bits_to_f32((uint16_t)t.nu_bits);
   };
   auto decode_chunk = [&](int64_t base) {
@@ -274,7 +336,13 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(
       for (int mt = 0; mt < 4; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const half8 zh = GTAB ? zg[m][s] : gather8<K>(vidx, sCbh, 32 * s + 8 * grp);
+        half8 zh;
+        if constexpr (GTAB)
+          zh = zg[m][s];
+        else if constexpr (expand_rows<K>())
+          zh = *reinterpret_cast<const half8*>(sZr + (TILE * m + col) * ZR_PITCH + 32 * s + 8 * grp);
+        else
+          zh = gather8<K>(vidx, sCbh, 32 * s + 8 * grp);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
           acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[mt][s], zh, acc[mt], 0, 0, 0);
@@ -348,7 +416,7 @@ template <int K, int BITS, typename TY, bool GATHER, bool PACKED>
 hipError_t launch_k(const fq_codebook* cb, const uint32_t* codes, const uint16_t* norms,
                     const int64_t* rows, int64_t n_records, int64_t n, TY* y, int64_t ld,
                     hipStream_t s) {
-  const size_t cb_bytes = large_block(K) ? 0 : ((size_t)cb->N * K * sizeof(_Float16) + 15) / 16 * 16;
+  const size_t cb_bytes = large_block(K) ? 0 : ((size_t)cb->N * table_k<K>() * sizeof(_Float16) + 15) / 16 * 16;
   const size_t shm = cb_bytes + DEC_WAVES * wave_lds<K, BITS, TY>();
   auto kern = decode_kernel<K, BITS, TY, GATHER, PACKED>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
