@@ -229,18 +229,10 @@ __device__ inline half8 gather8(const uint16_t* idx, const _Float16* cbh, int c0
     const uint32_t* h = reinterpret_cast<const uint32_t*>(cbh);
     const u32x4 hv = {h[i0], h[i1], h[i2], h[i3]};
     return __builtin_bit_cast(half8, hv);
-  } else if constexpr (K % 8 == 0 && K >= 16) {   // 8 coordinates of one codeword
+  } else {   // 8 coordinates of one codeword (k = 3 is expanded at staging instead)
+    static_assert(K % 8 == 0 && K >= 16, "gather8: k = 2, 4, 8 or a multiple of 8");
     const uint32_t i0 = idx[c0 / K];
     return *reinterpret_cast<const half8*>(cbh + i0 * K + c0 % K);
-  } else {  // K = 3: one coordinate at a time; the last block may be partial
-    half8 hi;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int c = c0 + e;
-      const int j = c / K, t = c - j * K;
-      hi[e] = cbh[idx[j] * K + t];
-    }
-    return hi;
   }
 }
 
