@@ -225,9 +225,14 @@ __device__ inline void prepare_column(ColPrep<K, RW>& cp, const float* zrow, boo
 // Best and second-best t(n) = |c_n|^2 - 2 <z, c_n> over the cell's list (grid)
 // or the whole codebook (scan; NC > 0: a compile-time trip count of NC = N
 // entries, as every artifact holds N = 2^bits codewords), and the gap test.
+// The search table read through the constant address space: the table is
+// never written while a kernel runs, so uniform reads become scalar loads
+// whose values feed the vector instructions straight from scalar registers.
+typedef const float __attribute__((address_space(4)))* ConstFloatPtr;
+
 template <int K, int S, int RW, bool GRID, int NC>
-__device__ inline void search_column(const ColPrep<K, RW>& cp, const float* sEnc, int N, float gv,
-                                     float ez, int& i1out, bool& certain) {
+__device__ inline void search_column(const ColPrep<K, RW>& cp, const float* sEnc, ConstFloatPtr gEnc,
+                                     int N, float gv, float ez, int& i1out, bool& certain) {
   float m1 = INFINITY, m2 = INFINITY;
   int i1 = 0;
   bool listed = true;   // the search covered every possible nearest codeword
@@ -284,11 +289,13 @@ __device__ inline void search_column(const ColPrep<K, RW>& cp, const float* sEnc
   } else if constexpr (NC > 0) {
     // the whole codebook with the trip count known at compile time, unrolled
     // by four (fully unrolled, the compiler would keep every row live across
-    // the columns and spill)
+    // the columns and spill); every lane reads the same row, so the rows come
+    // through scalar loads instead of LDS
 #pragma unroll 4
     for (int i = 0; i < NC; ++i) {
       float er[K + 1];
-      row((uint32_t)i, er);
+#pragma unroll
+      for (int tt = 0; tt <= K; ++tt) er[tt] = gEnc[i * S + tt];
       visit(er, i);
     }
   } else {
@@ -455,7 +462,8 @@ __global__ __launch_bounds__(enc_waves<BITS>() * 64) __attribute__((amdgpu_waves
         const bool live = c < NCF && v < nv;
         int i1;
         bool certain;
-        search_column<K, S, RW, GRID, (BITS <= 4 ? (1 << BITS) : 0)>(cp[q], sEnc, N, a.gv, a.ez, i1, certain);
+        search_column<K, S, RW, GRID, (BITS <= 4 ? (1 << BITS) : 0)>(
+            cp[q], sEnc, (ConstFloatPtr)a.enc, N, a.gv, a.ez, i1, certain);
         record(c, live, v, b, i1, certain);
       }
     }
