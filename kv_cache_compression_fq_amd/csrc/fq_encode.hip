@@ -278,12 +278,13 @@ __device__ inline void search_column(const ColPrep<K, RW>& cp, const float* sEnc
       }
     }
   } else if constexpr (NC > 0 && NC * (K + 1) <= 32) {
-    // a table of at most 32 floats: fully unrolled, so its rows (the same for
-    // every lane) stay in registers across the chunk's columns
+    // a table of at most 32 floats: fully unrolled, its rows (the same for
+    // every lane) in scalar registers across the chunk's columns
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       float er[K + 1];
-      row((uint32_t)i, er);
+#pragma unroll
+      for (int tt = 0; tt <= K; ++tt) er[tt] = gEnc[i * S + tt];
       visit(er, i);
     }
   } else if constexpr (NC > 0) {
