@@ -8,10 +8,12 @@
 //    (and its norm) with unconditional buffer loads; the loads of the next two
 //    chunks are in flight while the current one is decoded.
 //  * Staging: each lane unpacks its own record (field widths are compile-time,
-//    so every shift is static) into a table of 16-bit indices in LDS.
+//    so every shift is static) into a table of 16-bit indices in LDS; for
+//    k = 3 it writes the vector's 64 binary16 coordinates there instead.
 //  * Per tile of 16 vectors, v_mfma_f32_16x16x32_f16 forms Y^T = Pi^T Z_hat^T:
 //    A = Pi^T, rounded to binary16, in registers for the whole kernel;
-//    B = Z_hat^T, gathered from the LDS codebook (binary16) by index.  Both
+//    B = Z_hat^T, gathered from the LDS codebook (binary16) by index, or read
+//    from the staged coordinates (k = 3).  Both
 //    operands carry binary16 rounding (relative 2^-12 per entry); over the
 //    64-term sums that is ~3e-5 nu rms and ~2e-4 nu worst case, inside the
 //    1e-3 nu decode tolerance before the output's own rounding.  Accumulation
