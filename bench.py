@@ -200,6 +200,10 @@ def main():
     ap.add_argument("--cost-sample", type=int, default=1 << 15,
                     help="vectors copied to the host for the search-work model")
     a = ap.parse_args()
+    chosen = set() if a.no_extras else {e.strip() for e in a.extras.split(",") if e.strip()}
+    unknown = chosen - set(EXTRAS)
+    if unknown:
+        raise SystemExit(f"unknown --extras {sorted(unknown)}; choose from {EXTRAS}")
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the codec shards by (layer, head) or token range "
               "with no exchange, so no multi-GPU figure is produced; run with --gpus 1",
@@ -346,10 +350,6 @@ def main():
     torch.cuda.empty_cache()
 
     extras = {}
-    chosen = set() if a.no_extras else {e.strip() for e in a.extras.split(",") if e.strip()}
-    unknown = chosen - set(EXTRAS)
-    if unknown:
-        raise SystemExit(f"unknown --extras {sorted(unknown)}; choose from {EXTRAS}")
     if "copy_ceiling" in chosen:
         extras["copy_ceiling"] = copy_ceiling(torch, dev)
     if "gpt2_step" in chosen:
